@@ -1,0 +1,21 @@
+"""CPU oracle for the forward pass of one Mixture-of-Experts layer.
+
+TEST INFRASTRUCTURE ONLY.  Nothing in the product path may import, call or
+link this package: only ``tests/``, ``__graft_entry__.smoke()`` and the CPU
+baseline leg of ``bench.py`` use it.  It shares no code with the HIP library.
+"""
+
+from .moe_oracle import (  # noqa: F401
+    E2M1_VALUES,
+    combine,
+    decode_bf16,
+    decode_e8m0,
+    decode_mxfp4,
+    dense_layer,
+    expert_ffn,
+    layer,
+    permute,
+    route,
+    router_logits,
+    swiglu_expert,
+)

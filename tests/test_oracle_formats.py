@@ -1,0 +1,112 @@
+"""Pins for the oracle's input decoders: bf16, E8M0 and MX-FP4 (E2M1).
+
+bf16 and E8M0 are checked against torch's own dtype conversions; E2M1 against
+the format's bit-field definition (sign, two exponent bits with bias 1, one
+mantissa bit, subnormals at exponent 0) and the OCP quantiser's error bound.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import E2M1_VALUES, decode_bf16, decode_e8m0, decode_mxfp4
+from synth import quantize_mxfp4
+
+
+def test_bf16_decode_matches_torch(rng):
+    v = torch.tensor(rng.normal(size=1000) * 10.0 ** rng.integers(-30, 30, size=1000), dtype=torch.float32)
+    b = v.to(torch.bfloat16)
+    bits = b.view(torch.int16).numpy().view(np.uint16)
+    np.testing.assert_array_equal(decode_bf16(bits), b.to(torch.float64).numpy())
+    specials = torch.tensor([0.0, -0.0, float("inf"), -float("inf")], dtype=torch.bfloat16)
+    got = decode_bf16(specials.view(torch.int16).numpy().view(np.uint16))
+    np.testing.assert_array_equal(got, [0.0, -0.0, np.inf, -np.inf])
+    assert np.signbit(got[1])
+
+
+def test_e8m0_decode_matches_torch():
+    s = np.arange(255, dtype=np.uint8)
+    ref = torch.from_numpy(s).view(torch.float8_e8m0fnu).to(torch.float64).numpy()
+    np.testing.assert_array_equal(decode_e8m0(s), ref)
+    assert np.isnan(decode_e8m0(np.array([255], dtype=np.uint8)))[0]
+
+
+def _e2m1_from_bits(code):
+    sign = -1.0 if code & 0x8 else 1.0
+    e = (code >> 1) & 0x3
+    m = code & 0x1
+    mag = 0.5 * m if e == 0 else 2.0 ** (e - 1) * (1.0 + 0.5 * m)
+    return sign * mag
+
+
+def test_e2m1_table_matches_bit_fields():
+    for code in range(16):
+        mag = E2M1_VALUES[code & 7]
+        assert (-mag if code & 8 else mag) == _e2m1_from_bits(code)
+
+
+def test_mxfp4_nibble_order_and_scale():
+    # byte 0x21: low nibble 1 (0.5) is element 0, high nibble 2 (1.0) element 1
+    codes = np.zeros((1, 16), dtype=np.uint8)
+    codes[0, 0] = 0x21
+    codes[0, 1] = 0xF8        # element 2 = -0.0, element 3 = -6.0
+    for s, mult in ((127, 1.0), (130, 8.0), (120, 2.0 ** -7)):
+        vals = decode_mxfp4(codes, np.array([[s]], dtype=np.uint8))
+        assert vals.shape == (1, 32)
+        np.testing.assert_array_equal(vals[0, :4], np.array([0.5, 1.0, -0.0, -6.0]) * mult)
+        assert np.signbit(vals[0, 2])
+        assert np.all(vals[0, 4:] == 0.0)
+
+
+def test_mxfp4_all_codes_block():
+    codes = np.array([[c | ((c + 1) << 4) for c in range(0, 16, 2)] * 2], dtype=np.uint8)
+    vals = decode_mxfp4(codes, np.array([[127]], dtype=np.uint8))
+    expect = [_e2m1_from_bits(c) for c in range(16)] * 2
+    np.testing.assert_array_equal(vals[0], expect)
+
+
+def test_mxfp4_blocks_run_along_last_axis():
+    codes = np.full((2, 32), 0x22, dtype=np.uint8)   # every element 1.0
+    scales = np.array([[127, 128], [126, 131]], dtype=np.uint8)
+    vals = decode_mxfp4(codes, scales)
+    np.testing.assert_array_equal(vals[0, :32], 1.0)
+    np.testing.assert_array_equal(vals[0, 32:], 2.0)
+    np.testing.assert_array_equal(vals[1, :32], 0.5)
+    np.testing.assert_array_equal(vals[1, 32:], 16.0)
+
+
+def test_mxfp4_roundtrip_error_bound(rng):
+    w = torch.tensor(rng.normal(size=(8, 256)) * 0.02, dtype=torch.float32)
+    codes, scales = quantize_mxfp4(w)
+    deq = decode_mxfp4(codes.numpy(), scales.numpy())
+    wb = w.numpy().astype(np.float64).reshape(8, 8, 32)
+    db = deq.reshape(8, 8, 32)
+    sc = decode_e8m0(scales.numpy())
+    amax = np.abs(wb).max(-1)
+    # scale is the largest power of two with amax/scale < 8, i.e. [4, 8)
+    assert np.all(amax / sc >= 4) and np.all(amax / sc < 8)
+    # in-range elements are within half an E2M1 step (step <= 2 below 6)
+    err = np.abs(db - wb) / sc[..., None]
+    inrange = np.abs(wb) / sc[..., None] <= 6.0
+    steps = np.where(np.abs(wb) / sc[..., None] < 2, 0.5, np.where(np.abs(wb) / sc[..., None] < 4, 1.0, 2.0))
+    assert np.all(err[inrange] <= steps[inrange] / 2 + 1e-12)
+    # saturated elements decode to +-6 * scale
+    sat = ~inrange
+    np.testing.assert_array_equal(np.abs(db[sat]), 6.0 * np.broadcast_to(sc[..., None], db.shape)[sat])
+
+
+def test_mxfp4_values_exact_in_bf16(rng):
+    w = torch.tensor(rng.normal(size=(4, 512)) * 0.02, dtype=torch.float32)
+    codes, scales = quantize_mxfp4(w)
+    deq = decode_mxfp4(codes.numpy(), scales.numpy())
+    as_bf16 = torch.tensor(deq).to(torch.bfloat16).to(torch.float64).numpy()
+    np.testing.assert_array_equal(deq, as_bf16)
+
+
+@pytest.mark.parametrize("shape", [(3, 64), (2, 5, 96)])
+def test_mxfp4_shapes(shape, rng):
+    w = torch.tensor(rng.normal(size=shape), dtype=torch.float32)
+    codes, scales = quantize_mxfp4(w)
+    assert codes.shape == (*shape[:-1], shape[-1] // 2)
+    assert scales.shape == (*shape[:-1], shape[-1] // 32)
+    assert decode_mxfp4(codes.numpy(), scales.numpy()).shape == shape
