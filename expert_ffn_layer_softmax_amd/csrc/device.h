@@ -1,0 +1,101 @@
+// Device-side helpers shared by the gfx950 kernels: number formats, wave64
+// reductions and streaming loads.  Written for CDNA4 only (wave64, MFMA).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "internal.h"
+
+namespace moe {
+
+constexpr int kWave = 64;
+
+// 16 bytes as a native clang vector (HIP's uint4 is a struct, which the
+// non-temporal builtins do not accept).
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// ---------------------------------------------------------------------------
+// Storage formats (Fmt values: internal.h)
+// ---------------------------------------------------------------------------
+// bf16 is kept as raw uint16 bits: the upper half of an fp32.
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
+
+// fp32 -> bf16, round to nearest even; NaN stays a (quiet) NaN.
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40u);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+// E8M0 block scale -> fp32 power of two 2^(s-127).  s = 0 is the subnormal
+// 2^-127; s = 255 is NaN.
+__device__ __forceinline__ float e8m0_to_f32(uint32_t s) {
+  uint32_t bits = (s == 0u) ? 0x00400000u : (s == 255u ? 0x7fc00000u : (s << 23));
+  return __uint_as_float(bits);
+}
+
+// Two E2M1 codes in byte `sel` of `w` -> fp32 pair (low nibble first), by
+// the gfx950 scaled-convert instruction with unit scale.
+template <int SEL>
+__device__ __forceinline__ float2 fp4x2_to_f32(uint32_t w) {
+  auto v = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, SEL);
+  return make_float2(v[0], v[1]);
+}
+
+// ---------------------------------------------------------------------------
+// Wave64 reductions (xor butterfly: every lane ends with the same value)
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, kWave);
+  return v;
+}
+
+__device__ __forceinline__ int lane_id() { return threadIdx.x & (kWave - 1); }
+
+// Block-wide exclusive prefix sum of one int per thread (blockDim.x a
+// multiple of 64, at most 1024).  `tmp` needs 17 ints of LDS.  Also returns
+// the block total.  Contains barriers: every thread of the block must call.
+__device__ __forceinline__ int block_exclusive_scan(int v, int* tmp, int* total) {
+  const int lane = lane_id();
+  const int wave = threadIdx.x >> 6;
+  const int nwaves = blockDim.x >> 6;
+  int incl = v;
+#pragma unroll
+  for (int off = 1; off < kWave; off <<= 1) {
+    int o = __shfl_up(incl, off, kWave);
+    if (lane >= off) incl += o;
+  }
+  if (lane == kWave - 1) tmp[wave] = incl;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    int run = 0;
+    for (int w = 0; w < nwaves; ++w) {
+      int c = tmp[w];
+      tmp[w] = run;
+      run += c;
+    }
+    tmp[16] = run;
+  }
+  __syncthreads();
+  int res = tmp[wave] + incl - v;
+  *total = tmp[16];
+  __syncthreads();
+  return res;
+}
+
+// ---------------------------------------------------------------------------
+// Loads
+// ---------------------------------------------------------------------------
+// Streaming (non-temporal) 16-byte load: weights are read once per call, so
+// they should not evict reusable lines from L2.
+__device__ __forceinline__ u32x4 ld_stream16(const void* p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+}
+__device__ __forceinline__ u32x4 ld16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
+
+}  // namespace moe

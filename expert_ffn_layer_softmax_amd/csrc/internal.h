@@ -1,0 +1,78 @@
+// Host-side internals shared by the launchers and the C ABI: workspace plan,
+// launch parameters and the per-kernel event timer.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace moe {
+
+// Storage formats, numbered as moe_dtype_t.
+enum Fmt : int { kF32 = 0, kBF16 = 1, kMXFP4 = 2 };
+
+// Rows per m-tile of the grouped MFMA GEMMs; the tile list in the workspace
+// is sized for this value.
+constexpr int kGemmBM = 128;
+
+// Largest T handled by the fused decode path (down projection + combine in
+// one kernel; per-token accumulators live in registers).
+constexpr int kDecodeMaxT = 16;
+
+struct Dims {
+  int T, d, E, k, f, act, wfmt;
+  long long Tk() const { return (long long)T * k; }
+};
+
+struct Weights {
+  const void *wg, *wu, *wd;
+  const uint8_t *sg, *su, *sd;
+};
+
+// Workspace layout (byte offsets, each 256-aligned).
+struct WsLayout {
+  size_t counts, offsets, sorted_src, dest_row, active, num_active, mtiles, num_mtiles;
+  size_t h, y_sorted, total;
+};
+WsLayout ws_layout(const Dims& dm);
+
+// Routing plan pointers in the workspace (device).
+struct Plan {
+  int* counts;
+  int* offsets;
+  int* sorted_src;
+  int* dest_row;
+  int* active;      // [E] experts with at least one routed pair, ascending
+  int* num_active;  // [1]
+  int* mtiles;      // [2 * max_mtiles] (expert, first row) per m-tile of kGemmBM rows
+  int* num_mtiles;  // [1]
+};
+
+// Per-kernel event timing (abi.cpp).  Bracket every launch with it.
+struct LaunchTimer {
+  LaunchTimer(const char* name, hipStream_t s);
+  ~LaunchTimer();
+  const char* name_;
+  hipStream_t s_;
+  int slot_;
+};
+
+// Launchers: each queues one kernel on `s` and returns hipGetLastError().
+hipError_t launch_router_logits(const void* x, const void* w_r, float* logits, int T, int d,
+                                int E, int act, hipStream_t s);
+hipError_t launch_route_topk(const float* logits, int T, int E, int k, int* topk_idx,
+                             float* topk_w, hipStream_t s);
+hipError_t launch_permute(const int* topk_idx, int T, int E, int k, const Plan& p,
+                          bool with_lists, hipStream_t s);
+hipError_t launch_plan_from_offsets(const int* offsets, int E, const Plan& p, hipStream_t s);
+hipError_t launch_gemv_gate_up(const Dims& dm, const void* x, const Plan& p, const int* sorted_src,
+                               const Weights& w, void* h, hipStream_t s);
+hipError_t launch_gemv_down(const Dims& dm, const void* h, const Plan& p, const Weights& w,
+                            float* y_sorted, hipStream_t s);
+hipError_t launch_gemv_down_combine(const Dims& dm, const void* h, const Plan& p,
+                                    const int* sorted_src, const float* topk_w,
+                                    const Weights& w, void* out, hipStream_t s);
+hipError_t launch_combine(const Dims& dm, const float* y_sorted, const int* dest_row,
+                          const float* topk_w, void* out, hipStream_t s);
+
+}  // namespace moe

@@ -1,0 +1,175 @@
+/*
+ * moe.h -- C ABI of a gfx950 (MI355X) library for the forward pass of one
+ * Mixture-of-Experts decoder layer: router softmax and top-k selection,
+ * grouping of (token, slot) pairs by expert, a grouped SwiGLU expert FFN over
+ * bf16 or MX-FP4 weights with fp32 accumulation, and the weighted combine.
+ *
+ * The layer is the one the Muse Spark pages describe: every decoder layer is
+ * a Mixture-of-Experts layer that sends each token to 8 of its 256 experts
+ * (SGLang-TorchTPU on TPU v7 page, "Introduction"), whose selected expert
+ * outputs are normalised and then combined (TensorSharp Muse Spark report,
+ * "Performance" section).  E, k, d and f are parameters here.
+ *
+ * Conventions shared by every entry point
+ *  - Every buffer pointer is a DEVICE pointer (HIP global memory), row-major,
+ *    contiguous and at least 16-byte aligned; the workspace 256-byte aligned.
+ *  - The caller owns every buffer and keeps it alive until the work queued on
+ *    `stream` has finished.  The library allocates no device memory, keeps no
+ *    pointer after returning and never synchronises the stream.
+ *  - All work is queued asynchronously on `stream` (a hipStream_t; NULL means
+ *    the default stream).  Calls are reentrant.
+ *  - Arguments are validated on the host before any HIP call; a call that
+ *    returns anything but MOE_OK has queued no work.  Errors are returned as
+ *    moe_status_t, never raised or aborted across the ABI.  MOE_ERR_DEVICE
+ *    means a HIP launch failed; moe_last_device_error() then holds the
+ *    hipError_t value for the calling thread.
+ *  - T == 0 is a valid no-op (pointers are then not inspected).
+ *  - Results are deterministic: identical inputs give bit-identical outputs
+ *    (no floating-point atomics anywhere).
+ *
+ * Stored layouts (the reduction dimension is innermost):
+ *    x                 [T][d]          act dtype (fp32 or bf16)
+ *    router w_r        [E][d]          act dtype
+ *    logits            [T][E]          fp32
+ *    w_gate, w_up      [E][f][d]       w dtype
+ *    w_down            [E][d][f]       w dtype
+ *    MX-FP4 weights:   codes uint8 [E][f][d/2] / [E][d][f/2], two E2M1 values
+ *                      per byte, element 2i in the low nibble; E8M0 scales
+ *                      uint8 [E][f][d/32] / [E][d][f/32], one per 32
+ *                      consecutive elements along the reduction dimension.
+ *    topk_idx, topk_w  [T][k]          int32 / fp32
+ *    y_sorted          [T*k][d]        fp32
+ *    out               [T][d]          act dtype
+ *
+ * Supported shapes: 1 <= E <= 1024, 1 <= k <= min(E, 64), d and f positive
+ * multiples of 32, T*k < 2^31.  Supported (act, weight) dtype pairs:
+ * (F32, F32), (BF16, BF16), (BF16, MXFP4); others give MOE_ERR_UNSUPPORTED.
+ */
+#ifndef MOE_MI355X_H_
+#define MOE_MI355X_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MOE_OK = 0,
+  MOE_ERR_INVALID_ARGUMENT = 1,    /* NULL/misaligned pointer, bad size      */
+  MOE_ERR_UNSUPPORTED = 2,         /* valid but unsupported shape or dtypes  */
+  MOE_ERR_WORKSPACE_TOO_SMALL = 3, /* workspace_bytes < moe_workspace_size  */
+  MOE_ERR_DEVICE = 4               /* a HIP call failed                     */
+} moe_status_t;
+
+typedef enum { MOE_DTYPE_F32 = 0, MOE_DTYPE_BF16 = 1, MOE_DTYPE_MXFP4 = 2 } moe_dtype_t;
+
+/* Layer shape.  T tokens of hidden size d, E experts of FFN width f, each
+ * token routed to k experts.  act_dtype / w_dtype hold moe_dtype_t values. */
+typedef struct {
+  int32_t T, d, E, k, f;
+  int32_t act_dtype;
+  int32_t w_dtype;
+} moe_dims_t;
+
+/* Stacked expert weights (device pointers, layouts above).  s_* are the
+ * MX-FP4 scale arrays and must be NULL for other weight dtypes. */
+typedef struct {
+  const void* w_gate;
+  const void* w_up;
+  const void* w_down;
+  const uint8_t* s_gate;
+  const uint8_t* s_up;
+  const uint8_t* s_down;
+} moe_expert_weights_t;
+
+typedef void* moe_stream_t; /* a hipStream_t */
+
+/* Bytes of scratch device memory moe_layer_forward needs for `dims` (also
+ * enough for moe_expert_ffn).  Host-only; no device work. */
+moe_status_t moe_workspace_size(const moe_dims_t* dims, size_t* bytes);
+
+/* Router top-k and weights (the selection of k of E experts per token:
+ * SGLang-TorchTPU page, "Introduction"; the normalised weights the report's
+ * "Performance" section combines by).  For each token t:
+ *   topk_idx[t][0..k) = the k largest logits[t][:], in descending order of
+ *     logit; equal logits ordered by ascending expert index, so a tie at the
+ *     selection boundary goes to the lower index.  -0.0 equals +0.0; -inf is
+ *     a valid logit; NaN is outside the domain (results unspecified).
+ *   topk_w[t][j] = softmax over all E logits, renormalised over the selected
+ *     k, computed in fp32 as exp(l_j - l_0) / sum_j' exp(l_j' - l_0); equal
+ *     logits (also when all are -inf) contribute 1.
+ * Inputs: logits [T][E] fp32.  Outputs: topk_idx [T][k], topk_w [T][k]. */
+moe_status_t moe_route(const float* logits, int32_t T, int32_t E, int32_t k,
+                       int32_t* topk_idx, float* topk_w, moe_stream_t stream);
+
+/* Group the T*k (token, slot) pairs by expert (a stable counting sort of
+ * flat ids q = t*k + j by topk_idx.flat[q]).
+ *   counts[E]        pairs routed to each expert
+ *   offsets[E+1]     exclusive prefix sum of counts, offsets[E] = T*k
+ *   sorted_src[T*k]  flat ids ordered by expert, ascending q within an expert
+ *   dest_row[T*k]    inverse: sorted_src[dest_row[q]] == q
+ * topk_idx values must lie in [0, E); out-of-range ids are clamped (the
+ * outputs are then unspecified but no out-of-bounds access happens). */
+moe_status_t moe_permute(const int32_t* topk_idx, int32_t T, int32_t E, int32_t k,
+                         int32_t* counts, int32_t* offsets, int32_t* sorted_src,
+                         int32_t* dest_row, moe_stream_t stream);
+
+/* Grouped SwiGLU expert FFN.  For every row r of expert e's segment
+ * [offsets[e], offsets[e+1]) with token t = sorted_src[r] / k:
+ *   h = silu(w_gate[e] x[t]) * (w_up[e] x[t]),  silu(z) = z / (1 + exp(-z))
+ *   y_sorted[r] = w_down[e] h
+ * All products accumulate in fp32 (the pages tie accuracy drift to bf16
+ * reduction of per-expert partial results: TensorSharp report, "Answer
+ * quality" section).  h is held in the act dtype in the workspace.
+ * x [T][d] act dtype; y_sorted [T*k][d] fp32 output. */
+moe_status_t moe_expert_ffn(const moe_dims_t* dims, const void* x, const int32_t* offsets,
+                            const int32_t* sorted_src, const moe_expert_weights_t* weights,
+                            float* y_sorted, void* workspace, size_t workspace_bytes,
+                            moe_stream_t stream);
+
+/* Weighted combine (TensorSharp report, "Performance" section: the selected
+ * experts' normalised outputs are combined):
+ *   out[t] = sum_{j<k} topk_w[t][j] * y_sorted[dest_row[t*k + j]]
+ * summed in fp32 in slot order and rounded once to the act dtype (bf16:
+ * round to nearest even). */
+moe_status_t moe_combine(const moe_dims_t* dims, const float* y_sorted, const int32_t* dest_row,
+                         const float* topk_w, void* out, moe_stream_t stream);
+
+/* The whole layer: [router logits] -> route -> permute -> expert FFN ->
+ * combine.  If w_router is non-NULL, logits[T][E] = x . w_router^T (fp32
+ * accumulation) is written to `logits`; otherwise `logits` is read as input.
+ * topk_idx / topk_w receive the routing.  For T <= 16 the down projection is
+ * fused with the combine (the per-token sum runs in ascending expert order
+ * instead of slot order; still deterministic).
+ * workspace must hold moe_workspace_size(dims) bytes. */
+moe_status_t moe_layer_forward(const moe_dims_t* dims, const void* x, const void* w_router,
+                               float* logits, const moe_expert_weights_t* weights,
+                               int32_t* topk_idx, float* topk_w, void* out, void* workspace,
+                               size_t workspace_bytes, moe_stream_t stream);
+
+/* Static, NUL-terminated description of a status code. */
+const char* moe_status_string(moe_status_t status);
+
+/* hipError_t of the last MOE_ERR_DEVICE returned on the calling thread. */
+int32_t moe_last_device_error(void);
+
+/* Per-kernel timing with HIP events, for measurement tools.  While enabled,
+ * every kernel the library launches is bracketed by a pair of events recorded
+ * on the launch stream (at most 8192 launches are recorded; later ones are
+ * not).  moe_timing_start clears earlier records and enables; moe_timing_stop
+ * disables.  moe_timing_query waits for the recorded events and returns, for
+ * the kernel named `kernel` (e.g. "gemv_gate_up"), the number of recorded
+ * launches and their summed duration in milliseconds.  moe_timing_names
+ * writes the distinct recorded kernel names, comma separated, into buf. */
+moe_status_t moe_timing_start(void);
+moe_status_t moe_timing_stop(void);
+moe_status_t moe_timing_query(const char* kernel, int32_t* launches, double* total_ms);
+moe_status_t moe_timing_names(char* buf, size_t buf_bytes);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_MI355X_H_ */

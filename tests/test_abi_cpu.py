@@ -1,0 +1,146 @@
+"""The C-ABI library without a GPU: it loads, exports every entry point that
+include/moe.h declares, and its host-side validation returns the documented
+status codes before any device call (so these run on a CPU-only machine)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moe.h")
+
+OK, INVALID, UNSUPPORTED, WS_SMALL = 0, 1, 2, 3
+
+
+@pytest.fixture(scope="module")
+def m():
+    import expert_ffn_layer_softmax_amd as mod
+    return mod
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(moe_[a-z_]+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol(m):
+    names = _declared()
+    assert "moe_layer_forward" in names and len(names) >= 12
+    for n in names:
+        assert hasattr(m.lib, n), f"{n} declared in moe.h but not exported"
+
+
+def test_python_binding_names_match_abi(m):
+    for n in ("moe_route", "moe_permute", "moe_expert_ffn", "moe_combine", "moe_layer_forward",
+              "moe_workspace_size", "moe_status_string"):
+        assert callable(getattr(m, n))
+
+
+def _dims(m, T=4, d=64, E=8, k=2, f=32, act=1, w=1):
+    return m._lib.MoeDims(T, d, E, k, f, act, w)
+
+
+def _ws(m, dims):
+    out = ctypes.c_size_t(0)
+    st = m.lib.moe_workspace_size(ctypes.byref(dims), ctypes.byref(out))
+    return st, out.value
+
+
+def test_workspace_size_validation(m):
+    assert _ws(m, _dims(m))[0] == OK
+    assert _ws(m, _dims(m))[1] > 0
+    assert _ws(m, _dims(m, k=9))[0] == INVALID          # k > E
+    assert _ws(m, _dims(m, k=0))[0] == INVALID
+    assert _ws(m, _dims(m, T=-1))[0] == INVALID
+    assert _ws(m, _dims(m, d=48))[0] == UNSUPPORTED     # d % 32
+    assert _ws(m, _dims(m, f=40))[0] == UNSUPPORTED
+    assert _ws(m, _dims(m, E=2000, k=2))[0] == UNSUPPORTED
+    assert _ws(m, _dims(m, E=100, k=65))[0] == UNSUPPORTED
+    assert _ws(m, _dims(m, act=0, w=1))[0] == UNSUPPORTED   # f32 act, bf16 weights
+    assert _ws(m, _dims(m, act=1, w=0))[0] == UNSUPPORTED
+    assert _ws(m, _dims(m, act=2, w=2))[0] == UNSUPPORTED   # MX-FP4 activations
+    assert _ws(m, _dims(m, act=5))[0] == INVALID
+    assert m.lib.moe_workspace_size(None, None) == INVALID
+
+
+def test_workspace_grows_with_tokens(m):
+    small = _ws(m, _dims(m, T=1, d=6144, E=256, k=8, f=2816))[1]
+    big = _ws(m, _dims(m, T=4096, d=6144, E=256, k=8, f=2816))[1]
+    # h (bf16) and y_sorted (fp32) for T*k rows dominate
+    assert big >= 4096 * 8 * (2816 * 2 + 6144 * 4)
+    assert small < big
+
+
+FAKE = ctypes.c_void_p(0x10000)        # never dereferenced: every call below is rejected
+MISALIGNED = ctypes.c_void_p(0x10004)
+
+
+def test_route_validation(m):
+    L = m.lib
+    assert L.moe_route(None, 0, 8, 2, None, None, None) == OK          # T == 0
+    assert L.moe_route(None, 4, 8, 2, None, None, None) == INVALID
+    assert L.moe_route(FAKE, 4, 8, 9, FAKE, FAKE, None) == INVALID      # k > E
+    assert L.moe_route(FAKE, 4, 2000, 2, FAKE, FAKE, None) == UNSUPPORTED
+    assert L.moe_route(FAKE, 4, 256, 65, FAKE, FAKE, None) == UNSUPPORTED
+    assert L.moe_route(MISALIGNED, 4, 8, 2, FAKE, FAKE, None) == INVALID
+    assert L.moe_route(FAKE, -1, 8, 2, FAKE, FAKE, None) == INVALID
+
+
+def test_permute_validation(m):
+    L = m.lib
+    assert L.moe_permute(None, 0, 8, 2, None, None, None, None, None) == OK
+    assert L.moe_permute(FAKE, 3, 8, 2, FAKE, None, FAKE, FAKE, None) == INVALID
+    assert L.moe_permute(FAKE, 3, 8, 2, FAKE, FAKE, FAKE, MISALIGNED, None) == INVALID
+    assert L.moe_permute(FAKE, 3, 1025, 2, FAKE, FAKE, FAKE, FAKE, None) == UNSUPPORTED
+
+
+def _w(m, mx=False, bad=None):
+    vals = [FAKE.value] * 3 + ([FAKE.value] * 3 if mx else [None] * 3)
+    if bad is not None:
+        vals[bad[0]] = bad[1]
+    return m._lib.MoeExpertWeights(*vals)
+
+
+def test_layer_forward_validation(m):
+    L = m.lib
+    dims = _dims(m)
+    st, need = _ws(m, dims)
+    args = lambda d, w, ws=FAKE, wsb=need: (ctypes.byref(d), FAKE, None, FAKE, ctypes.byref(w), FAKE,
+                                           FAKE, FAKE, ws, wsb, None)
+    assert L.moe_layer_forward(*args(dims, _w(m), wsb=need - 1)) == WS_SMALL
+    assert L.moe_layer_forward(*args(dims, _w(m, bad=(1, None)))) == INVALID
+    assert L.moe_layer_forward(*args(dims, _w(m, mx=True))) == INVALID      # scales with bf16
+    mxd = _dims(m, w=2)
+    assert L.moe_layer_forward(*args(mxd, _w(m), wsb=_ws(m, mxd)[1])) == INVALID  # no scales
+    assert L.moe_layer_forward(*args(dims, _w(m), ws=ctypes.c_void_p(0x10010))) == INVALID
+    assert L.moe_layer_forward(*args(_dims(m, d=40), _w(m))) == UNSUPPORTED
+    assert L.moe_layer_forward(*args(_dims(m, T=0), _w(m))) == OK
+    assert L.moe_layer_forward(None, None, None, None, None, None, None, None, None, 0, None) == INVALID
+
+
+def test_expert_ffn_and_combine_validation(m):
+    L = m.lib
+    dims = _dims(m)
+    _, need = _ws(m, dims)
+    w = _w(m)
+    assert L.moe_expert_ffn(ctypes.byref(dims), FAKE, FAKE, FAKE, ctypes.byref(w), FAKE, FAKE,
+                            need - 256, None) == WS_SMALL
+    assert L.moe_expert_ffn(ctypes.byref(dims), None, FAKE, FAKE, ctypes.byref(w), FAKE, FAKE,
+                            need, None) == INVALID
+    assert L.moe_combine(ctypes.byref(dims), FAKE, FAKE, FAKE, None, None) == INVALID
+    assert L.moe_combine(ctypes.byref(dims), FAKE, MISALIGNED, FAKE, FAKE, None) == INVALID
+    assert L.moe_combine(ctypes.byref(_dims(m, T=0)), None, None, None, None, None) == OK
+
+
+def test_status_strings(m):
+    for code in range(5):
+        assert m.moe_status_string(code)
+    assert m.moe_status_string(99) == "unknown status"
+
+
+def test_timing_query_validation(m):
+    assert m.lib.moe_timing_query(None, None, None) == INVALID
+    assert m.lib.moe_timing_names(None, 0) == INVALID

@@ -1,0 +1,237 @@
+"""GPU parity: every entry point of the HIP library against the oracle.
+
+Routing (indices, counts, offsets, sorted_src, dest_row) must match bit for
+bit given the device's own fp32 logits; routing weights to 1e-5 relative;
+layer outputs to relative L2 <= 1e-5 (fp32), 5e-3 (bf16) and 2e-2 (MX-FP4
+weights).  Shapes span several tiles with ragged tails; full-size decode and
+verify workloads run in the launch configuration the bench times.
+"""
+
+import zlib
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from gpu_util import (ACT_TOL, MXFP4_TOL, check_routing, expert_getter, log, make_inputs,
+                      rel_l2, require_gpu, run_layer_and_oracle, to_host_act)
+from synth import WORKLOADS, Workload, gen_expert_weights
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    require_gpu()
+    yield
+    torch.cuda.empty_cache()
+
+
+def _tol(wl):
+    return MXFP4_TOL if wl.wfmt == "mxfp4" else ACT_TOL[wl.act]
+
+
+# --------------------------------------------------------------------- route
+@pytest.mark.parametrize("T,E,k,mode", [
+    (1, 256, 8, "normal"), (16, 256, 8, "normal"), (4096, 256, 8, "normal"),
+    (37, 8, 2, "ties"), (64, 100, 7, "ties"), (33, 1000, 64, "normal"), (5, 1024, 1, "ties"),
+    (9, 64, 64, "ties"), (11, 300, 16, "neginf"), (3, 1, 1, "normal"), (130, 129, 9, "neginf"),
+])
+def test_route(T, E, k, mode):
+    from expert_ffn_layer_softmax_amd import moe_route
+    log(f"route T={T} E={E} k={k} {mode}")
+    g = torch.Generator().manual_seed(T * 1000 + E + k)
+    if mode == "ties":
+        l = torch.randint(0, 4, (T, E), generator=g).float()
+    else:
+        l = torch.randn(T, E, generator=g)
+    if mode == "neginf":
+        l[torch.rand(T, E, generator=g) < 0.3] = -float("inf")
+        l[0, :] = -float("inf")
+        l[1, : E // 2] = -float("inf")
+        l[2, 0] = -0.0
+        l[2, 1] = 0.0
+    idx, w = moe_route(l.cuda(), k)
+    torch.cuda.synchronize()
+    ref_idx, ref_w = oracle.route(l.numpy(), k)
+    assert np.array_equal(idx.cpu().numpy(), ref_idx)
+    np.testing.assert_allclose(w.cpu().numpy(), ref_w, rtol=1e-5, atol=1e-7)
+
+
+# ------------------------------------------------------------------- permute
+@pytest.mark.parametrize("T,E,k", [(1, 256, 8), (16, 256, 8), (4096, 256, 8), (333, 1024, 3),
+                                   (1000, 1, 1), (50, 7, 7), (2048, 64, 64), (129, 1000, 8)])
+def test_permute(T, E, k):
+    from expert_ffn_layer_softmax_amd import moe_permute
+    log(f"permute T={T} E={E} k={k}")
+    g = torch.Generator().manual_seed(7 * T + E)
+    # skewed: logits with a per-expert bias, top-k by sort
+    logits = torch.randn(T, E, generator=g) + torch.randn(E, generator=g) * 1.5
+    idx = torch.topk(logits, k, dim=1).indices.to(torch.int32).contiguous()
+    counts, offsets, sorted_src, dest_row = moe_permute(idx.cuda(), E)
+    torch.cuda.synchronize()
+    rc, ro, rs, rd = oracle.permute(idx.numpy(), E)
+    assert np.array_equal(counts.cpu().numpy(), rc)
+    assert np.array_equal(offsets.cpu().numpy(), ro)
+    assert np.array_equal(sorted_src.cpu().numpy(), rs)
+    assert np.array_equal(dest_row.cpu().numpy(), rd)
+
+
+# ------------------------------------------------------------- small layers
+SMALL = [
+    # name, T, d, E, k, f, act, wfmt
+    ("bf16_t1", 1, 256, 16, 4, 96, "bf16", "bf16"),
+    ("bf16_t5", 5, 512, 32, 8, 160, "bf16", "bf16"),
+    ("bf16_t16", 16, 1024, 64, 8, 352, "bf16", "bf16"),
+    ("bf16_t17", 17, 256, 8, 2, 128, "bf16", "bf16"),
+    ("bf16_t200", 200, 192, 12, 3, 224, "bf16", "bf16"),
+    ("bf16_segd", 2, 9216, 4, 2, 64, "bf16", "bf16"),
+    ("bf16_segf", 3, 64, 4, 2, 9216, "bf16", "bf16"),
+    ("mx_t1", 1, 256, 16, 4, 96, "bf16", "mxfp4"),
+    ("mx_t5", 5, 512, 32, 8, 160, "bf16", "mxfp4"),
+    ("mx_t16", 16, 1024, 64, 8, 352, "bf16", "mxfp4"),
+    ("mx_t40", 40, 256, 8, 2, 128, "bf16", "mxfp4"),
+    ("mx_segd", 1, 33792, 2, 1, 32, "bf16", "mxfp4"),
+    ("f32_t3", 3, 96, 5, 5, 32, "f32", "f32"),
+    ("f32_t64", 64, 128, 16, 4, 64, "f32", "f32"),
+    ("f32_segd", 2, 4160, 3, 2, 32, "f32", "f32"),
+]
+
+
+@pytest.mark.parametrize("case", SMALL, ids=[c[0] for c in SMALL])
+def test_layer_small(case):
+    name, T, d, E, k, f, act, wfmt = case
+    log(f"layer {name}")
+    wl = Workload(name, T=T, d=d, E=E, k=k, f=f, act=act, wfmt=wfmt, seed=zlib.crc32(name.encode()) % 100000,
+                  x_std=1.0, wg_std=d ** -0.5, wu_std=d ** -0.5, wd_std=f ** -0.5)
+    x, w, w_r, logits = make_inputs(wl)
+    got, ref, _ = run_layer_and_oracle(wl, x, w, w_r, logits)
+    err = rel_l2(got, ref["out"])
+    log(f"  rel_l2={err:.3e}")
+    assert err <= _tol(wl)
+
+
+@pytest.mark.parametrize("name", ["tiny_fp32", "tiny_fp32_stress"])
+def test_layer_tiny_fp32_with_router(name):
+    wl = WORKLOADS[name]
+    log(f"layer {name}")
+    x, w, w_r, logits = make_inputs(wl)
+    got, ref, _ = run_layer_and_oracle(wl, x, w, w_r, logits)
+    err = rel_l2(got, ref["out"])
+    log(f"  rel_l2={err:.3e}")
+    assert err <= 1e-5
+
+
+def test_layer_k_equals_E_uniform_is_dense_mixture():
+    """k=E with equal logits: the device output equals (1/E) sum_e FFN_e."""
+    wl = Workload("dense_mix", T=4, d=128, E=8, k=8, f=64, act="f32", wfmt="f32", seed=99,
+                  x_std=1.0, wg_std=0.1, wu_std=0.1, wd_std=0.1)
+    x, w, _, _ = make_inputs(wl)
+    from expert_ffn_layer_softmax_amd import moe_layer_forward
+    res = moe_layer_forward(x, w, 8, logits=torch.zeros(4, 8, device="cuda"))
+    torch.cuda.synchronize()
+    xh = to_host_act(x)
+    get = expert_getter(w, "f32")
+    dense = sum(oracle.swiglu_expert(xh, *get(e)) for e in range(8)) / 8
+    assert rel_l2(to_host_act(res["out"]), dense) <= 1e-5
+
+
+def test_determinism_and_t0():
+    from expert_ffn_layer_softmax_amd import moe_layer_forward
+    wl = Workload("det", T=16, d=512, E=32, k=8, f=160, act="bf16", wfmt="bf16", seed=5)
+    x, w, _, logits = make_inputs(wl)
+    a = moe_layer_forward(x, w, 8, logits=logits)["out"].clone()
+    b = moe_layer_forward(x, w, 8, logits=logits)["out"].clone()
+    torch.cuda.synchronize()
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+    wl2 = Workload("det2", T=300, d=256, E=16, k=4, f=96, act="bf16", wfmt="mxfp4", seed=6)
+    x, w, _, logits = make_inputs(wl2)
+    a = moe_layer_forward(x, w, 4, logits=logits)["out"].clone()
+    b = moe_layer_forward(x, w, 4, logits=logits)["out"].clone()
+    torch.cuda.synchronize()
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+    # T = 0 is a no-op
+    e = torch.empty(0, 256, dtype=torch.bfloat16, device="cuda")
+    r = moe_layer_forward(e, w, 4, logits=torch.empty(0, 16, device="cuda"))
+    assert r["out"].shape == (0, 256)
+
+
+# --------------------------------------------------- individual entry points
+@pytest.mark.parametrize("wfmt,T", [("bf16", 7), ("bf16", 64), ("mxfp4", 23), ("f32", 9)])
+def test_stagewise_entry_points(wfmt, T):
+    from expert_ffn_layer_softmax_amd import moe_combine, moe_expert_ffn, moe_permute, moe_route
+    act = "f32" if wfmt == "f32" else "bf16"
+    wl = Workload("stages", T=T, d=320, E=24, k=6, f=192, act=act, wfmt=wfmt, seed=T,
+                  x_std=1.0, wg_std=320 ** -0.5, wu_std=320 ** -0.5, wd_std=192 ** -0.5)
+    log(f"stages {wfmt} T={T}")
+    x, w, _, logits = make_inputs(wl)
+    idx, tw = moe_route(logits, wl.k)
+    counts, offsets, sorted_src, dest_row = moe_permute(idx, wl.E)
+    y = moe_expert_ffn(x, offsets, sorted_src, wl.k, w)
+    out = moe_combine(y, dest_row, tw, x.dtype)
+    torch.cuda.synchronize()
+    lg = logits.cpu().numpy()
+    ridx, rw = oracle.route(lg, wl.k)
+    assert np.array_equal(idx.cpu().numpy(), ridx)
+    rc, ro, rs, rd = oracle.permute(ridx, wl.E)
+    assert np.array_equal(offsets.cpu().numpy(), ro) and np.array_equal(sorted_src.cpu().numpy(), rs)
+    assert np.array_equal(dest_row.cpu().numpy(), rd) and np.array_equal(counts.cpu().numpy(), rc)
+    xh = to_host_act(x)
+    ry = oracle.expert_ffn(xh, ro, rs, wl.k, expert_getter(w, wfmt))
+    yh = y.cpu().numpy().astype(np.float64)
+    assert rel_l2(yh, ry) <= _tol(wl)
+    # combine alone: fp32 sum of the device's own y_sorted, rounded once
+    rout = oracle.combine(yh, rd, tw.cpu().numpy().astype(np.float64))
+    got = to_host_act(out)
+    if act == "bf16":
+        np.testing.assert_allclose(got, rout, rtol=2 ** -8, atol=1e-30)
+    else:
+        np.testing.assert_allclose(got, rout, rtol=1e-6, atol=1e-9)
+
+
+# ------------------------------------------------------- full-size workloads
+@pytest.fixture(scope="module")
+def full_bf16_weights():
+    wl = WORKLOADS["decode_bf16"]
+    log("generating full bf16 expert weights (26.6 GB)")
+    w = gen_expert_weights(wl, "cuda")
+    torch.cuda.synchronize()
+    yield w
+    del w
+    torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("logit_set", [0, 17, 63])
+def test_decode_bf16_full(full_bf16_weights, logit_set):
+    wl = WORKLOADS["decode_bf16"]
+    log(f"decode_bf16 full, logit set {logit_set}")
+    x, w, w_r, logits = make_inputs(wl, weights=full_bf16_weights, logit_set=logit_set)
+    got, ref, _ = run_layer_and_oracle(wl, x, w, w_r, logits)
+    err = rel_l2(got, ref["out"])
+    log(f"  rel_l2={err:.3e}")
+    assert err <= 5e-3
+
+
+def test_verify_bf16_full(full_bf16_weights):
+    wl = WORKLOADS["verify_bf16"]
+    log("verify_bf16 full (T=16)")
+    x, w, w_r, logits = make_inputs(wl, weights=full_bf16_weights, logit_set=5)
+    got, ref, _ = run_layer_and_oracle(wl, x, w, w_r, logits)
+    err = rel_l2(got, ref["out"])
+    log(f"  rel_l2={err:.3e} unique experts={int((ref['counts'] > 0).sum())}")
+    assert err <= 5e-3
+
+
+def test_decode_mxfp4_full():
+    wl = WORKLOADS["decode_mxfp4"]
+    log("generating full MX-FP4 expert weights (7.06 GB)")
+    w = gen_expert_weights(wl, "cuda")
+    for s in (0, 9):
+        x, w, w_r, logits = make_inputs(wl, weights=w, logit_set=s)
+        got, ref, _ = run_layer_and_oracle(wl, x, w, w_r, logits)
+        err = rel_l2(got, ref["out"])
+        log(f"  set {s}: rel_l2={err:.3e}")
+        assert err <= MXFP4_TOL
+    del w
+    torch.cuda.empty_cache()
