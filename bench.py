@@ -140,8 +140,8 @@ def main():
 
     import torch
 
-    from expert_ffn_layer_softmax_amd import (moe_layer_forward, moe_timing_query, moe_timing_start,
-                                              moe_timing_stop)
+    from expert_ffn_layer_softmax_amd import (moe_layer_forward, moe_timing_names, moe_timing_query,
+                                              moe_timing_start, moe_timing_stop)
     from synth import WORKLOADS, gen_expert_weights, gen_logits, gen_x
 
     wl = WORKLOADS[args.workload]
@@ -217,7 +217,7 @@ def main():
     digest = _source_digest(srcs)
     traffic = _traffic(kname, wl.name, digest)
     breakdown = {}
-    for kn in ("route_topk", "permute", "gemv_gate_up", "gemv_down_combine", "gemv_down", "combine"):
+    for kn in moe_timing_names():
         n, t = moe_timing_query(kn)
         if n:
             breakdown[kn] = round(t * 1e3 / n, 2)

@@ -66,6 +66,7 @@ WsLayout ws_layout(const Dims& dm) {
   L.dest_row = o;    o = align_up(o + Tk * 4);
   L.active = o;      o = align_up(o + E * 4);
   L.num_active = o;  o = align_up(o + 4);
+  L.slot_info = o;   o = align_up(o + E * 16);
   L.mtiles = o;      o = align_up(o + max_mtiles * 8);
   L.num_mtiles = o;  o = align_up(o + 4);
   L.h = o;           o = align_up(o + Tk * (size_t)dm.f * act);
@@ -85,6 +86,7 @@ Plan plan_at(void* ws, const WsLayout& L) {
   p.dest_row = reinterpret_cast<int*>(b + L.dest_row);
   p.active = reinterpret_cast<int*>(b + L.active);
   p.num_active = reinterpret_cast<int*>(b + L.num_active);
+  p.slot_info = reinterpret_cast<int*>(b + L.slot_info);
   p.mtiles = reinterpret_cast<int*>(b + L.mtiles);
   p.num_mtiles = reinterpret_cast<int*>(b + L.num_mtiles);
   return p;
@@ -133,7 +135,7 @@ moe_status_t check_weights(const moe_expert_weights_t* w, const Dims& dm, Weight
 // Expert FFN on a prepared plan (offsets, sorted_src, active list).
 hipError_t run_expert_ffn(const Dims& dm, const void* x, const Plan& p, const Weights& w,
                           void* h, float* y_sorted, hipStream_t s) {
-  hipError_t e = launch_gemv_gate_up(dm, x, p, p.sorted_src, w, h, s);
+  hipError_t e = launch_gemv_gate_up(dm, x, p, w, h, s);
   if (e != hipSuccess) return e;
   return launch_gemv_down(dm, h, p, w, y_sorted, s);
 }
@@ -175,7 +177,7 @@ moe_status_t moe_permute(const int32_t* topk_idx, int32_t T, int32_t E, int32_t 
   if (!aligned16(topk_idx) || !aligned16(counts) || !aligned16(offsets) || !aligned16(sorted_src) ||
       !aligned16(dest_row))
     return MOE_ERR_INVALID_ARGUMENT;
-  Plan p{counts, offsets, sorted_src, dest_row, nullptr, nullptr, nullptr, nullptr};
+  Plan p{counts, offsets, sorted_src, dest_row, nullptr, nullptr, nullptr, nullptr, nullptr};
   return device_status(launch_permute(topk_idx, T, E, k, p, false, (hipStream_t)stream));
 }
 
@@ -242,16 +244,15 @@ moe_status_t moe_layer_forward(const moe_dims_t* dims, const void* x, const void
 
   hipError_t e = hipSuccess;
   if (w_router) e = launch_router_logits(x, w_router, logits, dm.T, dm.d, dm.E, dm.act, s);
-  if (e == hipSuccess) e = launch_route_topk(logits, dm.T, dm.E, dm.k, topk_idx, topk_w, s);
-  if (e == hipSuccess) e = launch_permute(topk_idx, dm.T, dm.E, dm.k, p, true, s);
   if (dm.T <= kDecodeMaxT) {
-    if (e == hipSuccess) e = launch_gemv_gate_up(dm, x, p, p.sorted_src, w, h, s);
     if (e == hipSuccess)
-      e = launch_gemv_down_combine(dm, h, p, p.sorted_src, topk_w, w, out, s);
+      e = launch_route_permute_small(logits, dm.T, dm.E, dm.k, topk_idx, topk_w, p, s);
   } else {
-    if (e == hipSuccess) e = run_expert_ffn(dm, x, p, w, h, y_sorted, s);
-    if (e == hipSuccess) e = launch_combine(dm, y_sorted, p.dest_row, topk_w, out, s);
+    if (e == hipSuccess) e = launch_route_topk(logits, dm.T, dm.E, dm.k, topk_idx, topk_w, s);
+    if (e == hipSuccess) e = launch_permute(topk_idx, dm.T, dm.E, dm.k, p, true, s);
   }
+  if (e == hipSuccess) e = run_expert_ffn(dm, x, p, w, h, y_sorted, s);
+  if (e == hipSuccess) e = launch_combine(dm, y_sorted, p.dest_row, topk_w, out, s);
   return device_status(e);
 }
 

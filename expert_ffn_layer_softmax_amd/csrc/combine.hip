@@ -13,7 +13,7 @@ namespace {
 
 constexpr int kMaxK = 64;
 
-// One block per token; threads stride over the row in float4 units.
+// Grid (T, row chunks of 1024 values); each thread one float4 of the row.
 template <int ACT>
 __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ y_sorted,
                                                       const int* __restrict__ dest_row,
@@ -21,14 +21,14 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
                                                       void* __restrict__ out, int d, int k) {
   __shared__ int rows[kMaxK];
   __shared__ float wts[kMaxK];
-  const int t = blockIdx.x;
+  const int t = blockIdx.y;
   if (threadIdx.x < k) {
     rows[threadIdx.x] = dest_row[(size_t)t * k + threadIdx.x];
     wts[threadIdx.x] = topk_w[(size_t)t * k + threadIdx.x];
   }
   __syncthreads();
   const int n4 = d >> 2;
-  for (int i = threadIdx.x; i < n4; i += blockDim.x) {
+  for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < n4; i += gridDim.x * blockDim.x) {
     float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
     for (int j = 0; j < k; ++j) {
       const float4 y = reinterpret_cast<const float4*>(y_sorted + (size_t)rows[j] * d)[i];
@@ -54,10 +54,11 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
 hipError_t launch_combine(const Dims& dm, const float* y_sorted, const int* dest_row,
                           const float* topk_w, void* out, hipStream_t s) {
   LaunchTimer tm("combine", s);
+  const dim3 grid((unsigned)((dm.d / 4 + 255) / 256), (unsigned)dm.T), block(256);
   if (dm.act == kF32)
-    combine_kernel<kF32><<<dm.T, 256, 0, s>>>(y_sorted, dest_row, topk_w, out, dm.d, dm.k);
+    combine_kernel<kF32><<<grid, block, 0, s>>>(y_sorted, dest_row, topk_w, out, dm.d, dm.k);
   else
-    combine_kernel<kBF16><<<dm.T, 256, 0, s>>>(y_sorted, dest_row, topk_w, out, dm.d, dm.k);
+    combine_kernel<kBF16><<<grid, block, 0, s>>>(y_sorted, dest_row, topk_w, out, dm.d, dm.k);
   return hipGetLastError();
 }
 

@@ -38,12 +38,35 @@ __device__ __forceinline__ float e8m0_to_f32(uint32_t s) {
   return __uint_as_float(bits);
 }
 
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+
 // Two E2M1 codes in byte `sel` of `w` -> fp32 pair (low nibble first), by
 // the gfx950 scaled-convert instruction with unit scale.
 template <int SEL>
 __device__ __forceinline__ float2 fp4x2_to_f32(uint32_t w) {
   auto v = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, SEL);
   return make_float2(v[0], v[1]);
+}
+
+// Two E2M1 codes in byte `sel` of `w` -> packed bf16 pair (low nibble in the
+// low half).  E2M1 values are exact in bf16.
+template <int SEL>
+__device__ __forceinline__ uint32_t fp4x2_to_bf16x2(uint32_t w) {
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, 1.0f, SEL));
+}
+
+// acc + a.lo*b.lo + a.hi*b.hi for packed bf16 pairs (v_dot2c_f32_bf16; the
+// bf16 products are exact in fp32).
+__device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float acc) {
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a),
+                                         __builtin_bit_cast(bf16x2_t, b), acc, false);
+}
+
+// Hide a value from loop-invariant code motion (an empty asm that "modifies"
+// it), so per-use conversions are not hoisted into extra live registers.
+__device__ __forceinline__ uint32_t opaque(uint32_t v) {
+  asm volatile("" : "+v"(v));
+  return v;
 }
 
 // ---------------------------------------------------------------------------

@@ -4,15 +4,20 @@
 // Small-batch decode waits on expert weights arriving from HBM, not on
 // arithmetic (SGLang-TorchTPU on TPU v7 page, "Introduction"), so these
 // kernels are built around the weight stream: every weight row of an active
-// expert is read exactly once with 16-byte non-temporal loads (all of a row's
-// loads in flight at once), applied in registers to every token routed to
-// that expert, and reduced in fp32 (TensorSharp Muse Spark report, "Answer
-// quality": bf16 partial sums cost accuracy).
+// expert is read exactly once with 16-byte non-temporal loads, all of a
+// wave's loads in flight together, and applied in registers to every token
+// routed to that expert with fp32 accumulation (TensorSharp Muse Spark report,
+// "Answer quality": bf16 partial sums cost accuracy).
 //
-// Work unit: one wave64 per weight row.  A 16-byte "chunk" of a row holds 4
-// fp32, 8 bf16 or 32 MX-FP4 codes (exactly one 32-element scale block); lane
-// l takes chunks l, l+64, ... so every load instruction reads 1 KiB of
-// contiguous row.  Rows longer than MAXC*64 chunks are streamed in segments.
+// Work unit: one wave64 per RPW weight rows of one active expert.  A 16-byte
+// "chunk" of a row holds 4 fp32, 8 bf16 or 32 MX-FP4 codes (exactly one
+// 32-element scale block); lane l takes chunks l, l+64, ... so each load
+// instruction reads 1 KiB of contiguous row.  The weight loads are issued
+// right after one scalar lookup of the slot's (expert, rows) entry, before the
+// token indices are resolved, so the index chain overlaps the weight stream.
+// Tokens are then processed one at a time against the weights held in
+// registers.  Rows longer than MAXC*64 chunks (MULTISEG) are streamed in
+// segments, re-reading the weights per token.
 #include "device.h"
 #include "internal.h"
 
@@ -23,8 +28,8 @@ template <int WF>
 struct WT;
 template <>
 struct WT<kF32> {
-  static constexpr int CE = 4;  // elements per 16-byte weight chunk
-  static constexpr int XB = 16; // activation bytes for one chunk
+  static constexpr int CE = 4;   // elements per 16-byte weight chunk
+  static constexpr int XB = 16;  // activation bytes matching one chunk
   __host__ __device__ static size_t row_bytes(int K) { return (size_t)K * 4; }
 };
 template <>
@@ -49,14 +54,6 @@ struct XChunk {
   u32x4 v[WT<WF>::XB / 16];
 };
 
-template <int WF>
-__device__ __forceinline__ XChunk<WF> load_x(const char* row, int c) {
-  XChunk<WF> x;
-#pragma unroll
-  for (int i = 0; i < WT<WF>::XB / 16; ++i) x.v[i] = ld16(row + (size_t)c * WT<WF>::XB + 16 * i);
-  return x;
-}
-
 // acc + <w, x> over one chunk.  For MX-FP4 the block scale is left out: the
 // caller multiplies the block's partial sum by it (one scale per chunk).
 template <int WF>
@@ -67,32 +64,21 @@ __device__ __forceinline__ float dot_chunk(const u32x4& w, const XChunk<WF>& x, 
     acc = fmaf(__uint_as_float(w.z), __uint_as_float(x.v[0].z), acc);
     acc = fmaf(__uint_as_float(w.w), __uint_as_float(x.v[0].w), acc);
   } else if constexpr (WF == kBF16) {
-    const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
-    const uint32_t xx[4] = {x.v[0].x, x.v[0].y, x.v[0].z, x.v[0].w};
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      acc = fmaf(bf16_lo(ww[i]), bf16_lo(xx[i]), acc);
-      acc = fmaf(bf16_hi(ww[i]), bf16_hi(xx[i]), acc);
-    }
+    acc = dot2_bf16(w.x, x.v[0].x, acc);
+    acc = dot2_bf16(w.y, x.v[0].y, acc);
+    acc = dot2_bf16(w.z, x.v[0].z, acc);
+    acc = dot2_bf16(w.w, x.v[0].w, acc);
   } else {
     // code word j holds elements 8j..8j+7 (byte b: elements 8j+2b, 8j+2b+1);
     // activation vector j holds the same 8 elements as 4 bf16 pairs.
     const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const uint32_t xx[4] = {x.v[j].x, x.v[j].y, x.v[j].z, x.v[j].w};
-      float2 p0 = fp4x2_to_f32<0>(ww[j]);
-      float2 p1 = fp4x2_to_f32<1>(ww[j]);
-      float2 p2 = fp4x2_to_f32<2>(ww[j]);
-      float2 p3 = fp4x2_to_f32<3>(ww[j]);
-      acc = fmaf(p0.x, bf16_lo(xx[0]), acc);
-      acc = fmaf(p0.y, bf16_hi(xx[0]), acc);
-      acc = fmaf(p1.x, bf16_lo(xx[1]), acc);
-      acc = fmaf(p1.y, bf16_hi(xx[1]), acc);
-      acc = fmaf(p2.x, bf16_lo(xx[2]), acc);
-      acc = fmaf(p2.y, bf16_hi(xx[2]), acc);
-      acc = fmaf(p3.x, bf16_lo(xx[3]), acc);
-      acc = fmaf(p3.y, bf16_hi(xx[3]), acc);
+      const uint32_t cw = opaque(ww[j]);
+      acc = dot2_bf16(fp4x2_to_bf16x2<0>(cw), x.v[j].x, acc);
+      acc = dot2_bf16(fp4x2_to_bf16x2<1>(cw), x.v[j].y, acc);
+      acc = dot2_bf16(fp4x2_to_bf16x2<2>(cw), x.v[j].z, acc);
+      acc = dot2_bf16(fp4x2_to_bf16x2<3>(cw), x.v[j].w, acc);
     }
   }
   return acc;
@@ -108,99 +94,124 @@ __device__ __forceinline__ void store_act(void* base, size_t i, float v) {
 
 __device__ __forceinline__ float silu(float z) { return z / (1.0f + expf(-z)); }
 
+// Weight rows of RPW consecutive outputs, one segment, in registers.
+template <int WF, int MAXC, int RPW>
+struct RowRegs {
+  u32x4 w[RPW][MAXC];
+  float s[RPW][MAXC];  // MX-FP4 block scales
+
+  __device__ __forceinline__ void load(const char* row0, size_t rb, const uint8_t* s0, size_t sb,
+                                       int nrows, int c0, int nchunks, int lane) {
+#pragma unroll
+    for (int r = 0; r < RPW; ++r) {
+#pragma unroll
+      for (int i = 0; i < MAXC; ++i) {
+        const int c = c0 + i * kWave + lane;
+        if (r < nrows && c < nchunks) {
+          w[r][i] = ld_stream16(row0 + r * rb + (size_t)c * 16);
+          if constexpr (WF == kMXFP4) s[r][i] = e8m0_to_f32(s0[r * sb + c]);
+        }
+      }
+    }
+  }
+};
+
+template <int WF>
+__device__ __forceinline__ XChunk<WF> load_x(const char* row, int c) {
+  XChunk<WF> x;
+#pragma unroll
+  for (int j = 0; j < WT<WF>::XB / 16; ++j) x.v[j] = ld16(row + (size_t)c * WT<WF>::XB + 16 * j);
+  return x;
+}
+
 struct GateUpArgs {
   const void* x;
   const void* wg;
   const void* wu;
   const uint8_t* sg;
   const uint8_t* su;
-  const int* offsets;
   const int* sorted_src;
-  const int* active;
+  const int* slot_info;
   const int* num_active;
   void* h;
   int d, f, k;
 };
 
 // h[r][n] = silu(<w_gate[e][n], x[t]>) * <w_up[e][n], x[t]> for every row r
-// of expert e (t = sorted_src[r] / k).  Block = 4 waves = 4 consecutive n of
-// one active expert.
-template <int WF, int MAXC, int MAXT>
+// of the slot's expert e (t = sorted_src[r] / k).  Block = 4 waves = 4*RPW
+// consecutive n of one active expert.
+template <int WF, int MAXC, int RPW, bool MULTISEG>
 __global__ __launch_bounds__(256) void gemv_gate_up_kernel(GateUpArgs a) {
   constexpr int CE = WT<WF>::CE;
+  constexpr int SEG = MAXC * kWave;
   const int lane = lane_id();
   const int wave = threadIdx.x >> 6;
-  const int tiles = (a.f + 3) >> 2;
+  const int RB = 4 * RPW;
+  const int tiles = (a.f + RB - 1) / RB;
   const int slot = blockIdx.x / tiles;
   if (slot >= *a.num_active) return;
-  const int n = (blockIdx.x - slot * tiles) * 4 + wave;
-  if (n >= a.f) return;
-  const int e = a.active[slot];
-  const int r0 = a.offsets[e];
-  const int ntok = a.offsets[e + 1] - r0;
+  const int n0 = (blockIdx.x - slot * tiles) * RB + wave * RPW;
+  if (n0 >= a.f) return;
+  const int e = a.slot_info[4 * slot + 0];
+  const int nrows = min(RPW, a.f - n0);
   const int nchunks = a.d / CE;
-  const int nseg = (nchunks + MAXC * kWave - 1) / (MAXC * kWave);
   const size_t rb = WT<WF>::row_bytes(a.d);
-  const char* gp = reinterpret_cast<const char*>(a.wg) + ((size_t)e * a.f + n) * rb;
-  const char* up = reinterpret_cast<const char*>(a.wu) + ((size_t)e * a.f + n) * rb;
-  const uint8_t* sgp = (WF == kMXFP4) ? a.sg + ((size_t)e * a.f + n) * (a.d / 32) : nullptr;
-  const uint8_t* sup = (WF == kMXFP4) ? a.su + ((size_t)e * a.f + n) * (a.d / 32) : nullptr;
-  const size_t xrb = (size_t)a.d * act_bytes<WF>();
-  const char* xb = reinterpret_cast<const char*>(a.x);
+  const size_t sb = (size_t)a.d / 32;
+  const size_t woff = (size_t)e * a.f + n0;
+  const char* gp = reinterpret_cast<const char*>(a.wg) + woff * rb;
+  const char* up = reinterpret_cast<const char*>(a.wu) + woff * rb;
+  const uint8_t* sgp = (WF == kMXFP4) ? a.sg + woff * sb : nullptr;
+  const uint8_t* sup = (WF == kMXFP4) ? a.su + woff * sb : nullptr;
 
-  u32x4 wg[MAXC], wu[MAXC];
-  float sgv[MAXC], suv[MAXC];
-  for (int g0 = 0; g0 < ntok; g0 += MAXT) {
-    const int ng = min(MAXT, ntok - g0);
-    const char* xr[MAXT];
+  RowRegs<WF, MAXC, RPW> G, U;
+  if (!MULTISEG) {  // whole rows, loaded once, before the token chain
+    G.load(gp, rb, sgp, sb, nrows, 0, nchunks, lane);
+    U.load(up, rb, sup, sb, nrows, 0, nchunks, lane);
+  }
+  const int r0 = a.slot_info[4 * slot + 1];
+  const int ntok = a.slot_info[4 * slot + 2];
+  const size_t xrb = (size_t)a.d * act_bytes<WF>();
+  const int nseg = MULTISEG ? (nchunks + SEG - 1) / SEG : 1;
+  for (int tt = 0; tt < ntok; ++tt) {
+    const char* xr = reinterpret_cast<const char*>(a.x) + (size_t)(a.sorted_src[r0 + tt] / a.k) * xrb;
+    float ag[RPW], au[RPW];
 #pragma unroll
-    for (int tt = 0; tt < MAXT; ++tt)
-      xr[tt] = xb + (size_t)(a.sorted_src[r0 + g0 + min(tt, ng - 1)] / a.k) * xrb;
-    float ag[MAXT], au[MAXT];
-#pragma unroll
-    for (int tt = 0; tt < MAXT; ++tt) ag[tt] = au[tt] = 0.f;
+    for (int r = 0; r < RPW; ++r) ag[r] = au[r] = 0.f;
     for (int seg = 0; seg < nseg; ++seg) {
-      const int cb = seg * MAXC * kWave + lane;
-      if (nseg > 1 || g0 == 0) {
+      const int c0 = seg * SEG;
+      if (MULTISEG) {
+        G.load(gp, rb, sgp, sb, nrows, c0, nchunks, lane);
+        U.load(up, rb, sup, sb, nrows, c0, nchunks, lane);
+      }
+      XChunk<WF> xc[MAXC];
 #pragma unroll
-        for (int i = 0; i < MAXC; ++i) {
-          const int c = cb + i * kWave;
-          if (c < nchunks) {
-            wg[i] = ld_stream16(gp + (size_t)c * 16);
-            wu[i] = ld_stream16(up + (size_t)c * 16);
-            if constexpr (WF == kMXFP4) {
-              sgv[i] = e8m0_to_f32(sgp[c]);
-              suv[i] = e8m0_to_f32(sup[c]);
-            }
-          }
-        }
+      for (int i = 0; i < MAXC; ++i) {
+        const int c = c0 + i * kWave + lane;
+        if (c < nchunks) xc[i] = load_x<WF>(xr, c);
       }
 #pragma unroll
       for (int i = 0; i < MAXC; ++i) {
-        const int c = cb + i * kWave;
+        const int c = c0 + i * kWave + lane;
         if (c < nchunks) {
 #pragma unroll
-          for (int tt = 0; tt < MAXT; ++tt) {
-            if (tt < ng) {
-              const XChunk<WF> xc = load_x<WF>(xr[tt], c);
-              if constexpr (WF == kMXFP4) {
-                ag[tt] = fmaf(dot_chunk<WF>(wg[i], xc, 0.f), sgv[i], ag[tt]);
-                au[tt] = fmaf(dot_chunk<WF>(wu[i], xc, 0.f), suv[i], au[tt]);
-              } else {
-                ag[tt] = dot_chunk<WF>(wg[i], xc, ag[tt]);
-                au[tt] = dot_chunk<WF>(wu[i], xc, au[tt]);
-              }
+          for (int r = 0; r < RPW; ++r) {
+            if constexpr (WF == kMXFP4) {
+              ag[r] = fmaf(dot_chunk<WF>(G.w[r][i], xc[i], 0.f), G.s[r][i], ag[r]);
+              au[r] = fmaf(dot_chunk<WF>(U.w[r][i], xc[i], 0.f), U.s[r][i], au[r]);
+            } else {
+              ag[r] = dot_chunk<WF>(G.w[r][i], xc[i], ag[r]);
+              au[r] = dot_chunk<WF>(U.w[r][i], xc[i], au[r]);
             }
           }
         }
       }
     }
 #pragma unroll
-    for (int tt = 0; tt < MAXT; ++tt) {
-      if (tt < ng) {
-        const float G = wave_sum(ag[tt]);
-        const float U = wave_sum(au[tt]);
-        if (lane == 0) store_act<WF>(a.h, (size_t)(r0 + g0 + tt) * a.f + n, silu(G) * U);
+    for (int r = 0; r < RPW; ++r) {
+      if (r < nrows) {
+        const float gs = wave_sum(ag[r]);
+        const float us = wave_sum(au[r]);
+        if (lane == 0) store_act<WF>(a.h, (size_t)(r0 + tt) * a.f + n0 + r, silu(gs) * us);
       }
     }
   }
@@ -210,229 +221,148 @@ struct DownArgs {
   const void* h;
   const void* wd;
   const uint8_t* sd;
-  const int* offsets;
-  const int* sorted_src;
-  const int* active;
+  const int* slot_info;
   const int* num_active;
-  const float* topk_w;
   float* y_sorted;
-  void* out;
-  int T, d, f, k;
+  int d, f;
 };
 
-// y_sorted[r][n] = <w_down[e][n], h[r]> for every row r of expert e.
-template <int WF, int MAXC, int MAXT>
+// y_sorted[r][n] = <w_down[e][n], h[r]> for every row r of the slot's expert.
+template <int WF, int MAXC, int RPW, bool MULTISEG>
 __global__ __launch_bounds__(256) void gemv_down_kernel(DownArgs a) {
   constexpr int CE = WT<WF>::CE;
+  constexpr int SEG = MAXC * kWave;
   const int lane = lane_id();
   const int wave = threadIdx.x >> 6;
-  const int tiles = (a.d + 3) >> 2;
+  const int RB = 4 * RPW;
+  const int tiles = (a.d + RB - 1) / RB;
   const int slot = blockIdx.x / tiles;
   if (slot >= *a.num_active) return;
-  const int n = (blockIdx.x - slot * tiles) * 4 + wave;
-  if (n >= a.d) return;
-  const int e = a.active[slot];
-  const int r0 = a.offsets[e];
-  const int ntok = a.offsets[e + 1] - r0;
+  const int n0 = (blockIdx.x - slot * tiles) * RB + wave * RPW;
+  if (n0 >= a.d) return;
+  const int e = a.slot_info[4 * slot + 0];
+  const int nrows = min(RPW, a.d - n0);
   const int nchunks = a.f / CE;
-  const int nseg = (nchunks + MAXC * kWave - 1) / (MAXC * kWave);
   const size_t rb = WT<WF>::row_bytes(a.f);
-  const char* wp = reinterpret_cast<const char*>(a.wd) + ((size_t)e * a.d + n) * rb;
-  const uint8_t* sp = (WF == kMXFP4) ? a.sd + ((size_t)e * a.d + n) * (a.f / 32) : nullptr;
-  const size_t hrb = (size_t)a.f * act_bytes<WF>();
-  const char* hb = reinterpret_cast<const char*>(a.h);
+  const size_t sb = (size_t)a.f / 32;
+  const size_t woff = (size_t)e * a.d + n0;
+  const char* wp = reinterpret_cast<const char*>(a.wd) + woff * rb;
+  const uint8_t* sp = (WF == kMXFP4) ? a.sd + woff * sb : nullptr;
 
-  u32x4 wv[MAXC];
-  float sv[MAXC];
-  for (int g0 = 0; g0 < ntok; g0 += MAXT) {
-    const int ng = min(MAXT, ntok - g0);
-    float acc[MAXT];
+  RowRegs<WF, MAXC, RPW> W;
+  if (!MULTISEG) W.load(wp, rb, sp, sb, nrows, 0, nchunks, lane);
+  const int r0 = a.slot_info[4 * slot + 1];
+  const int ntok = a.slot_info[4 * slot + 2];
+  const size_t hrb = (size_t)a.f * act_bytes<WF>();
+  const int nseg = MULTISEG ? (nchunks + SEG - 1) / SEG : 1;
+  for (int tt = 0; tt < ntok; ++tt) {
+    const char* hr = reinterpret_cast<const char*>(a.h) + (size_t)(r0 + tt) * hrb;
+    float acc[RPW];
 #pragma unroll
-    for (int tt = 0; tt < MAXT; ++tt) acc[tt] = 0.f;
+    for (int r = 0; r < RPW; ++r) acc[r] = 0.f;
     for (int seg = 0; seg < nseg; ++seg) {
-      const int cb = seg * MAXC * kWave + lane;
-      if (nseg > 1 || g0 == 0) {
+      const int c0 = seg * SEG;
+      if (MULTISEG) W.load(wp, rb, sp, sb, nrows, c0, nchunks, lane);
+      XChunk<WF> hc[MAXC];
 #pragma unroll
-        for (int i = 0; i < MAXC; ++i) {
-          const int c = cb + i * kWave;
-          if (c < nchunks) {
-            wv[i] = ld_stream16(wp + (size_t)c * 16);
-            if constexpr (WF == kMXFP4) sv[i] = e8m0_to_f32(sp[c]);
-          }
-        }
+      for (int i = 0; i < MAXC; ++i) {
+        const int c = c0 + i * kWave + lane;
+        if (c < nchunks) hc[i] = load_x<WF>(hr, c);
       }
 #pragma unroll
       for (int i = 0; i < MAXC; ++i) {
-        const int c = cb + i * kWave;
+        const int c = c0 + i * kWave + lane;
         if (c < nchunks) {
 #pragma unroll
-          for (int tt = 0; tt < MAXT; ++tt) {
-            if (tt < ng) {
-              const XChunk<WF> hc = load_x<WF>(hb + (size_t)(r0 + g0 + tt) * hrb, c);
-              if constexpr (WF == kMXFP4)
-                acc[tt] = fmaf(dot_chunk<WF>(wv[i], hc, 0.f), sv[i], acc[tt]);
-              else
-                acc[tt] = dot_chunk<WF>(wv[i], hc, acc[tt]);
-            }
-          }
-        }
-      }
-    }
-#pragma unroll
-    for (int tt = 0; tt < MAXT; ++tt) {
-      if (tt < ng) {
-        const float y = wave_sum(acc[tt]);
-        if (lane == 0) a.y_sorted[(size_t)(r0 + g0 + tt) * a.d + n] = y;
-      }
-    }
-  }
-}
-
-// Down projection fused with the weighted combine, for T <= TT tokens:
-// out[t][n] = sum over active experts e (ascending), over e's rows r with
-// token t, of topk_w[q] * <w_down[e][n], h[r]>.  One wave per output column
-// n; per-lane partial sums per token, one wave reduction per token at the end.
-template <int WF, int MAXC, int TT>
-__global__ __launch_bounds__(256) void gemv_down_combine_kernel(DownArgs a) {
-  constexpr int CE = WT<WF>::CE;
-  const int lane = lane_id();
-  const int n = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (n >= a.d) return;
-  const int na = *a.num_active;
-  const int nchunks = a.f / CE;
-  const int nseg = (nchunks + MAXC * kWave - 1) / (MAXC * kWave);
-  const size_t rb = WT<WF>::row_bytes(a.f);
-  const size_t hrb = (size_t)a.f * act_bytes<WF>();
-  const char* hb = reinterpret_cast<const char*>(a.h);
-
-  float acc[TT];
-#pragma unroll
-  for (int tt = 0; tt < TT; ++tt) acc[tt] = 0.f;
-  u32x4 wv[MAXC];
-  float sv[MAXC];
-  for (int s = 0; s < na; ++s) {
-    const int e = a.active[s];
-    const int r0 = a.offsets[e];
-    const int ntok = a.offsets[e + 1] - r0;
-    const char* wp = reinterpret_cast<const char*>(a.wd) + ((size_t)e * a.d + n) * rb;
-    const uint8_t* sp = (WF == kMXFP4) ? a.sd + ((size_t)e * a.d + n) * (a.f / 32) : nullptr;
-    for (int seg = 0; seg < nseg; ++seg) {
-      const int cb = seg * MAXC * kWave + lane;
-#pragma unroll
-      for (int i = 0; i < MAXC; ++i) {
-        const int c = cb + i * kWave;
-        if (c < nchunks) {
-          wv[i] = ld_stream16(wp + (size_t)c * 16);
-          if constexpr (WF == kMXFP4) sv[i] = e8m0_to_f32(sp[c]);
-        }
-      }
-      for (int rr = 0; rr < ntok; ++rr) {
-        const int q = a.sorted_src[r0 + rr];
-        const char* hr = hb + (size_t)(r0 + rr) * hrb;
-        float p = 0.f;
-#pragma unroll
-        for (int i = 0; i < MAXC; ++i) {
-          const int c = cb + i * kWave;
-          if (c < nchunks) {
-            const XChunk<WF> hc = load_x<WF>(hr, c);
+          for (int r = 0; r < RPW; ++r) {
             if constexpr (WF == kMXFP4)
-              p = fmaf(dot_chunk<WF>(wv[i], hc, 0.f), sv[i], p);
+              acc[r] = fmaf(dot_chunk<WF>(W.w[r][i], hc[i], 0.f), W.s[r][i], acc[r]);
             else
-              p = dot_chunk<WF>(wv[i], hc, p);
+              acc[r] = dot_chunk<WF>(W.w[r][i], hc[i], acc[r]);
           }
-        }
-        const float wt = a.topk_w[q];
-        if constexpr (TT == 1) {
-          acc[0] = fmaf(wt, p, acc[0]);
-        } else {
-          const int t = q / a.k;
-#pragma unroll
-          for (int tt = 0; tt < TT; ++tt)
-            if (tt == t) acc[tt] = fmaf(wt, p, acc[tt]);
         }
       }
     }
-  }
 #pragma unroll
-  for (int tt = 0; tt < TT; ++tt) {
-    if (tt < a.T) {
-      const float v = wave_sum(acc[tt]);
-      if (lane == 0) store_act<WF>(a.out, (size_t)tt * a.d + n, v);
+    for (int r = 0; r < RPW; ++r) {
+      if (r < nrows) {
+        const float y = wave_sum(acc[r]);
+        if (lane == 0) a.y_sorted[(size_t)(r0 + tt) * a.d + n0 + r] = y;
+      }
     }
   }
 }
 
-// Registers per lane for one row: the smallest supported MAXC covering the
-// row, capped at 16 (longer rows are streamed in segments).
-int pick_maxc(int nchunks) {
-  const int need = (nchunks + kWave - 1) / kWave;
-  static const int opts[] = {1, 2, 4, 6, 8, 12, 16};
-  for (int o : opts)
-    if (need <= o) return o;
-  return 16;
-}
-
-#define MOE_MAXC_SWITCH(MAXC, CALL)      \
-  switch (MAXC) {                        \
-    case 1: { constexpr int MC = 1; CALL; } break;   \
-    case 2: { constexpr int MC = 2; CALL; } break;   \
-    case 4: { constexpr int MC = 4; CALL; } break;   \
-    case 6: { constexpr int MC = 6; CALL; } break;   \
-    case 8: { constexpr int MC = 8; CALL; } break;   \
-    case 12: { constexpr int MC = 12; CALL; } break; \
-    default: { constexpr int MC = 16; CALL; } break; \
-  }
-
-#define MOE_WF_SWITCH(WFV, CALL)                            \
-  switch (WFV) {                                            \
-    case kF32: { constexpr int WF = kF32; CALL; } break;     \
-    case kBF16: { constexpr int WF = kBF16; CALL; } break;   \
-    default: { constexpr int WF = kMXFP4; CALL; } break;     \
-  }
-
+// ---------------------------------------------------------------- launch --
 int chunk_elems(int wf) { return wf == kF32 ? 4 : (wf == kBF16 ? 8 : 32); }
 
-constexpr int kGemvMaxT = 4;
+// Registers per lane for one row: the smallest supported MAXC covering the
+// row (MX-FP4 capped at 4: each chunk needs 64 B of activations).
+int pick_maxc(int nchunks, int wf) {
+  const int need = (nchunks + kWave - 1) / kWave;
+  static const int opts[] = {1, 2, 3, 4, 6, 8, 12, 16};
+  const int cap = wf == kMXFP4 ? 4 : 16;
+  for (int o : opts)
+    if (need <= o && o <= cap) return o;
+  return cap;
+}
+
+// Rows per wave so that a wave keeps about 12 chunks per matrix in flight.
+constexpr int rpw_for(int maxc) { return maxc >= 12 ? 1 : (maxc >= 6 ? 2 : 4); }
+
+#define MOE_MAXC_SWITCH(WFV, MAXC, CALL)                                              \
+  switch (MAXC) {                                                                     \
+    case 1: { constexpr int MC = 1; CALL; } break;                                    \
+    case 2: { constexpr int MC = 2; CALL; } break;                                    \
+    case 3: { constexpr int MC = 3; CALL; } break;                                    \
+    case 4: { constexpr int MC = 4; CALL; } break;                                    \
+    case 6: { if constexpr (WFV != kMXFP4) { constexpr int MC = 6; CALL; } } break;   \
+    case 8: { if constexpr (WFV != kMXFP4) { constexpr int MC = 8; CALL; } } break;   \
+    case 12: { if constexpr (WFV != kMXFP4) { constexpr int MC = 12; CALL; } } break; \
+    default: { if constexpr (WFV != kMXFP4) { constexpr int MC = 16; CALL; } } break; \
+  }
+
+#define MOE_WF_SWITCH(WFV, CALL)                          \
+  switch (WFV) {                                          \
+    case kF32: { constexpr int WF = kF32; CALL; } break;   \
+    case kBF16: { constexpr int WF = kBF16; CALL; } break; \
+    default: { constexpr int WF = kMXFP4; CALL; } break;   \
+  }
+
+#define MOE_SEG_SWITCH(MULTI, CALL)                 \
+  if (MULTI) { constexpr bool MS = true; CALL; }     \
+  else { constexpr bool MS = false; CALL; }
 
 }  // namespace
 
-hipError_t launch_gemv_gate_up(const Dims& dm, const void* x, const Plan& p, const int* sorted_src,
-                               const Weights& w, void* h, hipStream_t s) {
+hipError_t launch_gemv_gate_up(const Dims& dm, const void* x, const Plan& p, const Weights& w,
+                               void* h, hipStream_t s) {
   LaunchTimer tm("gemv_gate_up", s);
-  GateUpArgs a{x, w.wg, w.wu, w.sg, w.su, p.offsets, sorted_src, p.active, p.num_active, h,
+  GateUpArgs a{x, w.wg, w.wu, w.sg, w.su, p.sorted_src, p.slot_info, p.num_active, h,
                dm.d, dm.f, dm.k};
   const long long max_active = dm.Tk() < dm.E ? dm.Tk() : dm.E;
-  const dim3 grid((unsigned)(max_active * ((dm.f + 3) / 4))), block(256);
-  const int maxc = pick_maxc(dm.d / chunk_elems(dm.wfmt));
-  MOE_WF_SWITCH(dm.wfmt, MOE_MAXC_SWITCH(maxc, (gemv_gate_up_kernel<WF, MC, kGemvMaxT><<<grid, block, 0, s>>>(a))));
+  const int nchunks = dm.d / chunk_elems(dm.wfmt);
+  const int maxc = pick_maxc(nchunks, dm.wfmt);
+  const bool multi = nchunks > maxc * kWave;
+  const int rpw = rpw_for(maxc);
+  const dim3 grid((unsigned)(max_active * ((dm.f + 4 * rpw - 1) / (4 * rpw)))), block(256);
+  MOE_WF_SWITCH(dm.wfmt, MOE_MAXC_SWITCH(WF, maxc, MOE_SEG_SWITCH(multi, (
+      gemv_gate_up_kernel<WF, MC, rpw_for(MC), MS><<<grid, block, 0, s>>>(a)))));
   return hipGetLastError();
 }
 
 hipError_t launch_gemv_down(const Dims& dm, const void* h, const Plan& p, const Weights& w,
                             float* y_sorted, hipStream_t s) {
   LaunchTimer tm("gemv_down", s);
-  DownArgs a{h, w.wd, w.sd, p.offsets, p.sorted_src, p.active, p.num_active, nullptr,
-             y_sorted, nullptr, dm.T, dm.d, dm.f, dm.k};
+  DownArgs a{h, w.wd, w.sd, p.slot_info, p.num_active, y_sorted, dm.d, dm.f};
   const long long max_active = dm.Tk() < dm.E ? dm.Tk() : dm.E;
-  const dim3 grid((unsigned)(max_active * ((dm.d + 3) / 4))), block(256);
-  const int maxc = pick_maxc(dm.f / chunk_elems(dm.wfmt));
-  MOE_WF_SWITCH(dm.wfmt, MOE_MAXC_SWITCH(maxc, (gemv_down_kernel<WF, MC, kGemvMaxT><<<grid, block, 0, s>>>(a))));
-  return hipGetLastError();
-}
-
-hipError_t launch_gemv_down_combine(const Dims& dm, const void* h, const Plan& p,
-                                    const int* sorted_src, const float* topk_w,
-                                    const Weights& w, void* out, hipStream_t s) {
-  LaunchTimer tm("gemv_down_combine", s);
-  DownArgs a{h, w.wd, w.sd, p.offsets, sorted_src, p.active, p.num_active, topk_w,
-             nullptr, out, dm.T, dm.d, dm.f, dm.k};
-  const dim3 grid((unsigned)((dm.d + 3) / 4)), block(256);
-  const int maxc = pick_maxc(dm.f / chunk_elems(dm.wfmt));
-  if (dm.T == 1) {
-    MOE_WF_SWITCH(dm.wfmt, MOE_MAXC_SWITCH(maxc, (gemv_down_combine_kernel<WF, MC, 1><<<grid, block, 0, s>>>(a))));
-  } else {
-    MOE_WF_SWITCH(dm.wfmt, MOE_MAXC_SWITCH(maxc, (gemv_down_combine_kernel<WF, MC, kDecodeMaxT><<<grid, block, 0, s>>>(a))));
-  }
+  const int nchunks = dm.f / chunk_elems(dm.wfmt);
+  const int maxc = pick_maxc(nchunks, dm.wfmt);
+  const bool multi = nchunks > maxc * kWave;
+  const int rpw = rpw_for(maxc);
+  const dim3 grid((unsigned)(max_active * ((dm.d + 4 * rpw - 1) / (4 * rpw)))), block(256);
+  MOE_WF_SWITCH(dm.wfmt, MOE_MAXC_SWITCH(WF, maxc, MOE_SEG_SWITCH(multi, (
+      gemv_down_kernel<WF, MC, rpw_for(MC), MS><<<grid, block, 0, s>>>(a)))));
   return hipGetLastError();
 }
 

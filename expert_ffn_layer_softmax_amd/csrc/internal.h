@@ -15,8 +15,7 @@ enum Fmt : int { kF32 = 0, kBF16 = 1, kMXFP4 = 2 };
 // is sized for this value.
 constexpr int kGemmBM = 128;
 
-// Largest T handled by the fused decode path (down projection + combine in
-// one kernel; per-token accumulators live in registers).
+// Largest T routed and permuted by the single-workgroup decode kernel.
 constexpr int kDecodeMaxT = 16;
 
 struct Dims {
@@ -31,7 +30,7 @@ struct Weights {
 
 // Workspace layout (byte offsets, each 256-aligned).
 struct WsLayout {
-  size_t counts, offsets, sorted_src, dest_row, active, num_active, mtiles, num_mtiles;
+  size_t counts, offsets, sorted_src, dest_row, active, num_active, slot_info, mtiles, num_mtiles;
   size_t h, y_sorted, total;
 };
 WsLayout ws_layout(const Dims& dm);
@@ -44,6 +43,7 @@ struct Plan {
   int* dest_row;
   int* active;      // [E] experts with at least one routed pair, ascending
   int* num_active;  // [1]
+  int* slot_info;   // [E][4] per active slot: expert, first row, rows, 0
   int* mtiles;      // [2 * max_mtiles] (expert, first row) per m-tile of kGemmBM rows
   int* num_mtiles;  // [1]
 };
@@ -62,16 +62,16 @@ hipError_t launch_router_logits(const void* x, const void* w_r, float* logits, i
                                 int E, int act, hipStream_t s);
 hipError_t launch_route_topk(const float* logits, int T, int E, int k, int* topk_idx,
                              float* topk_w, hipStream_t s);
+// Route and permute in one workgroup for T <= kDecodeMaxT (T*k <= 1024).
+hipError_t launch_route_permute_small(const float* logits, int T, int E, int k, int* topk_idx,
+                                      float* topk_w, const Plan& p, hipStream_t s);
 hipError_t launch_permute(const int* topk_idx, int T, int E, int k, const Plan& p,
                           bool with_lists, hipStream_t s);
 hipError_t launch_plan_from_offsets(const int* offsets, int E, const Plan& p, hipStream_t s);
-hipError_t launch_gemv_gate_up(const Dims& dm, const void* x, const Plan& p, const int* sorted_src,
-                               const Weights& w, void* h, hipStream_t s);
+hipError_t launch_gemv_gate_up(const Dims& dm, const void* x, const Plan& p, const Weights& w,
+                               void* h, hipStream_t s);
 hipError_t launch_gemv_down(const Dims& dm, const void* h, const Plan& p, const Weights& w,
                             float* y_sorted, hipStream_t s);
-hipError_t launch_gemv_down_combine(const Dims& dm, const void* h, const Plan& p,
-                                    const int* sorted_src, const float* topk_w,
-                                    const Weights& w, void* out, hipStream_t s);
 hipError_t launch_combine(const Dims& dm, const float* y_sorted, const int* dest_row,
                           const float* topk_w, void* out, hipStream_t s);
 

@@ -1,12 +1,14 @@
 // Grouping of (token, slot) pairs by expert: a stable counting sort in one
-// workgroup.  Integer-only and atomic-order independent, so bit-exact.
+// workgroup.  Integer-only and independent of atomic order, so bit-exact.
 //
-// Beyond the four public outputs it can also write the execution plan the
-// expert kernels read: the ascending list of experts that received at least
-// one pair, and the list of m-tiles (expert, first row) of kGemmBM rows for
-// the grouped MFMA GEMMs.  Nothing here is read back by the host.
+// Besides the four public outputs it can write the execution plan the expert
+// kernels read: the ascending list of experts with at least one pair, a
+// per-slot (expert, first row, rows) table, and the list of m-tiles (expert,
+// first row) of kGemmBM rows for the grouped MFMA GEMMs.  Nothing here is read
+// back by the host.
 #include "device.h"
 #include "internal.h"
+#include "route_dev.h"
 
 namespace moe {
 namespace {
@@ -14,68 +16,78 @@ namespace {
 constexpr int kPermThreads = 1024;  // 16 waves
 constexpr int kMaxE = 1024;
 
-// Active-expert list and m-tile list from per-expert counts (thread e holds
-// counts[e]; threads >= E hold 0).  Barriers inside: all threads call.
-__device__ void write_lists(int c, int E, const Plan& p, int* tmp) {
+struct PermShared {
+  int hist[kMaxE];
+  int cursor[kMaxE];
+  int wave_cnt[kPermThreads / kWave][kMaxE];
+  int tmp[32];
+};
+
+// Active-expert list, slot table and m-tile list from per-expert counts
+// (thread e holds counts[e] and its exclusive prefix `first`; threads >= E
+// hold 0).  Contains barriers: every thread calls.
+__device__ void write_lists(int c, int first, int E, const Plan& p, int* tmp) {
   const int e = threadIdx.x;
   int total = 0;
   const int nz = (e < E && c > 0) ? 1 : 0;
   const int pos = block_exclusive_scan(nz, tmp, &total);
-  if (nz) p.active[pos] = e;
+  if (nz) {
+    p.active[pos] = e;
+    p.slot_info[4 * pos + 0] = e;
+    p.slot_info[4 * pos + 1] = first;
+    p.slot_info[4 * pos + 2] = c;
+    p.slot_info[4 * pos + 3] = 0;
+  }
   if (threadIdx.x == 0) *p.num_active = total;
   const int nt = (e < E) ? (c + kGemmBM - 1) / kGemmBM : 0;
   const int tpos = block_exclusive_scan(nt, tmp, &total);
   for (int i = 0; i < nt; ++i) {
     p.mtiles[2 * (tpos + i)] = e;
-    p.mtiles[2 * (tpos + i) + 1] = i * kGemmBM;
+    p.mtiles[2 * (tpos + i) + 1] = first + i * kGemmBM;
   }
   if (threadIdx.x == 0) *p.num_mtiles = total;
 }
 
-__global__ __launch_bounds__(kPermThreads) void permute_kernel(const int* __restrict__ topk_idx,
-                                                               int N, int E, Plan p,
-                                                               int with_lists) {
-  __shared__ int hist[kMaxE];
-  __shared__ int cursor[kMaxE];
-  __shared__ int wave_cnt[kPermThreads / kWave][kMaxE];
-  __shared__ int tmp[32];
+// Counting sort of N keys (key(q) in [0, E) after clamping) by one block of
+// kPermThreads threads.  Inside a wave, lanes with the same key are found by
+// one ballot per key bit; across waves, by per-wave counts in LDS.
+template <typename KeyFn>
+__device__ void permute_block(KeyFn key, int N, int E, const Plan& p, bool with_lists,
+                              PermShared& sh) {
   const int tid = threadIdx.x;
   const int lane = lane_id();
   const int wave = tid >> 6;
 
   for (int i = tid; i < E; i += kPermThreads) {
-    hist[i] = 0;
+    sh.hist[i] = 0;
 #pragma unroll
-    for (int w = 0; w < kPermThreads / kWave; ++w) wave_cnt[w][i] = 0;
+    for (int w = 0; w < kPermThreads / kWave; ++w) sh.wave_cnt[w][i] = 0;
   }
   __syncthreads();
   for (int q = tid; q < N; q += kPermThreads) {
-    const int e = min(max(topk_idx[q], 0), E - 1);
-    atomicAdd(&hist[e], 1);  // integer: order independent
+    const int e = min(max(key(q), 0), E - 1);
+    atomicAdd(&sh.hist[e], 1);  // integer: order independent
   }
   __syncthreads();
 
-  const int c = tid < E ? hist[tid] : 0;
+  const int c = tid < E ? sh.hist[tid] : 0;
   int total = 0;
-  const int excl = block_exclusive_scan(c, tmp, &total);
+  const int excl = block_exclusive_scan(c, sh.tmp, &total);
   if (tid < E) {
     p.counts[tid] = c;
     p.offsets[tid] = excl;
-    cursor[tid] = excl;
+    sh.cursor[tid] = excl;
   }
   if (tid == 0) p.offsets[E] = total;
-  if (with_lists) write_lists(c, E, p, tmp);
+  if (with_lists) write_lists(c, excl, E, p, sh.tmp);
   __syncthreads();
 
-  // Stable scatter, 1024 pairs per round in flat-id order.  Inside a wave,
-  // lanes with the same expert are found by a ballot per key bit; across
-  // waves, by per-wave counts in LDS.
   const int nbits = (E > 1) ? 32 - __clz(E - 1) : 0;
-  const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (kWave - lane));
+  const uint64_t lt_mask = (1ull << lane) - 1ull;
   for (int base = 0; base < N; base += kPermThreads) {
     const int q = base + tid;
     const bool valid = q < N;
-    const int e = valid ? min(max(topk_idx[q], 0), E - 1) : 0;
+    const int e = valid ? min(max(key(q), 0), E - 1) : 0;
     uint64_t peers = __ballot(valid);
     for (int b = 0; b < nbits; ++b) {
       const bool bit = (e >> b) & 1;
@@ -85,22 +97,29 @@ __global__ __launch_bounds__(kPermThreads) void permute_kernel(const int* __rest
     const int rank = __popcll(peers & lt_mask);
     const int cnt = __popcll(peers);
     const bool leader = valid && rank == 0;
-    if (leader) wave_cnt[wave][e] = cnt;
+    if (leader) sh.wave_cnt[wave][e] = cnt;
     __syncthreads();
     if (valid) {
       int prefix = 0;
-      for (int w = 0; w < wave; ++w) prefix += wave_cnt[w][e];
-      const int pos = cursor[e] + prefix + rank;
+      for (int w = 0; w < wave; ++w) prefix += sh.wave_cnt[w][e];
+      const int pos = sh.cursor[e] + prefix + rank;
       p.sorted_src[pos] = q;
       p.dest_row[q] = pos;
     }
     __syncthreads();
     if (leader) {
-      atomicAdd(&cursor[e], cnt);
-      wave_cnt[wave][e] = 0;
+      atomicAdd(&sh.cursor[e], cnt);
+      sh.wave_cnt[wave][e] = 0;
     }
     __syncthreads();
   }
+}
+
+__global__ __launch_bounds__(kPermThreads) void permute_kernel(const int* __restrict__ topk_idx,
+                                                               int N, int E, Plan p,
+                                                               int with_lists) {
+  __shared__ PermShared sh;
+  permute_block([&](int q) { return topk_idx[q]; }, N, E, p, with_lists != 0, sh);
 }
 
 __global__ __launch_bounds__(kPermThreads) void plan_kernel(const int* __restrict__ offsets, int E,
@@ -108,7 +127,32 @@ __global__ __launch_bounds__(kPermThreads) void plan_kernel(const int* __restric
   __shared__ int tmp[32];
   const int e = threadIdx.x;
   const int c = e < E ? offsets[e + 1] - offsets[e] : 0;
-  write_lists(c, E, p, tmp);
+  const int first = e < E ? offsets[e] : 0;
+  write_lists(c, first, E, p, tmp);
+}
+
+// Decode-sized layers (T <= 16, T*k <= 1024): wave t routes token t, then the
+// whole block sorts the T*k pairs from LDS.  One launch instead of two.
+template <int VPL>
+__global__ __launch_bounds__(kPermThreads) void route_permute_small_kernel(
+    const float* __restrict__ logits, int T, int E, int k, int* __restrict__ topk_idx,
+    float* __restrict__ topk_w, Plan p) {
+  __shared__ PermShared sh;
+  __shared__ int keys[kPermThreads];
+  const int lane = lane_id();
+  const int wave = threadIdx.x >> 6;
+  if (wave < T) {
+    int sel_i;
+    float sel_w;
+    route_token<VPL>(logits + (size_t)wave * E, E, k, sel_i, sel_w);
+    if (lane < k) {
+      topk_idx[wave * k + lane] = sel_i;
+      topk_w[wave * k + lane] = sel_w;
+      keys[wave * k + lane] = sel_i;
+    }
+  }
+  __syncthreads();
+  permute_block([&](int q) { return keys[q]; }, T * k, E, p, true, sh);
 }
 
 }  // namespace
@@ -123,6 +167,23 @@ hipError_t launch_permute(const int* topk_idx, int T, int E, int k, const Plan& 
 hipError_t launch_plan_from_offsets(const int* offsets, int E, const Plan& p, hipStream_t s) {
   LaunchTimer tm("plan", s);
   plan_kernel<<<1, kPermThreads, 0, s>>>(offsets, E, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_route_permute_small(const float* logits, int T, int E, int k, int* topk_idx,
+                                      float* topk_w, const Plan& p, hipStream_t s) {
+  LaunchTimer tm("route_permute", s);
+  const dim3 g(1), b(kPermThreads);
+  if (E <= 64)
+    route_permute_small_kernel<1><<<g, b, 0, s>>>(logits, T, E, k, topk_idx, topk_w, p);
+  else if (E <= 128)
+    route_permute_small_kernel<2><<<g, b, 0, s>>>(logits, T, E, k, topk_idx, topk_w, p);
+  else if (E <= 256)
+    route_permute_small_kernel<4><<<g, b, 0, s>>>(logits, T, E, k, topk_idx, topk_w, p);
+  else if (E <= 512)
+    route_permute_small_kernel<8><<<g, b, 0, s>>>(logits, T, E, k, topk_idx, topk_w, p);
+  else
+    route_permute_small_kernel<16><<<g, b, 0, s>>>(logits, T, E, k, topk_idx, topk_w, p);
   return hipGetLastError();
 }
 

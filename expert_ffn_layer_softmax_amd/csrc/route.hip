@@ -1,16 +1,8 @@
 // Router: logits GEMV (optional in-path stage) and top-k with renormalised
-// softmax weights.
-//
-// The layer sends each token to k of its E experts (SGLang-TorchTPU on TPU v7
-// page, "Introduction": 8 of 256 per layer).  The combine uses normalised
-// weights (TensorSharp Muse Spark report, "Performance" section); the reading
-// taken is a softmax over all E logits renormalised over the selected k, which
-// equals a softmax over the k selected logits.
-#include <float.h>
-#include <limits.h>
-
+// softmax weights (selection rule: route_dev.h).
 #include "device.h"
 #include "internal.h"
+#include "route_dev.h"
 
 namespace moe {
 namespace {
@@ -53,14 +45,7 @@ __global__ __launch_bounds__(256) void router_logits_kernel(const void* __restri
   }
 }
 
-// (value, index) order used for selection: larger value first, equal values
-// by smaller index.  No NaN in the domain, so this is a total order.
-__device__ __forceinline__ bool beats(float v, int i, float bv, int bi) {
-  return bi == INT_MAX ? (i != INT_MAX) : (i != INT_MAX && (v > bv || (v == bv && i < bi)));
-}
-
-// One wave per token; lane l holds logits l, l+64, ... (VPL of them).  k
-// rounds of wave argmax; the winner is marked taken.  Lane j keeps slot j.
+// One wave per token, four tokens per block.
 template <int VPL>
 __global__ __launch_bounds__(256) void route_topk_kernel(const float* __restrict__ logits, int T,
                                                          int E, int k, int* __restrict__ topk_idx,
@@ -68,55 +53,12 @@ __global__ __launch_bounds__(256) void route_topk_kernel(const float* __restrict
   const int lane = lane_id();
   const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (t >= T) return;
-  const float* row = logits + (size_t)t * E;
-  float v[VPL];
-  uint32_t taken = 0;
-#pragma unroll
-  for (int i = 0; i < VPL; ++i) {
-    const int e = lane + kWave * i;
-    if (e < E) {
-      v[i] = row[e];
-    } else {
-      v[i] = -FLT_MAX;
-      taken |= 1u << i;
-    }
-  }
-  float sel_v = 0.f;
-  int sel_i = 0;
-  for (int j = 0; j < k; ++j) {
-    float bv = 0.f;
-    int bi = INT_MAX;
-#pragma unroll
-    for (int i = 0; i < VPL; ++i) {
-      // indices grow with i, so a strict '>' keeps the lower index on ties
-      if (!((taken >> i) & 1u) && (bi == INT_MAX || v[i] > bv)) {
-        bv = v[i];
-        bi = lane + kWave * i;
-      }
-    }
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) {
-      const float ov = __shfl_xor(bv, off, kWave);
-      const int oi = __shfl_xor(bi, off, kWave);
-      if (beats(ov, oi, bv, bi)) {
-        bv = ov;
-        bi = oi;
-      }
-    }
-    if ((bi & (kWave - 1)) == lane) taken |= 1u << (bi >> 6);
-    if (lane == j) {
-      sel_v = bv;
-      sel_i = bi;
-    }
-  }
-  // Renormalised softmax over the k winners (slot 0 holds the maximum).
-  const float l0 = __shfl(sel_v, 0, kWave);
-  float ex = 0.f;
-  if (lane < k) ex = (sel_v == l0) ? 1.0f : expf(sel_v - l0);
-  const float sum = wave_sum(ex);
+  int sel_i;
+  float sel_w;
+  route_token<VPL>(logits + (size_t)t * E, E, k, sel_i, sel_w);
   if (lane < k) {
     topk_idx[(size_t)t * k + lane] = sel_i;
-    topk_w[(size_t)t * k + lane] = ex / sum;
+    topk_w[(size_t)t * k + lane] = sel_w;
   }
 }
 
