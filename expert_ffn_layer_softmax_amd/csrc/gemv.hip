@@ -100,14 +100,15 @@ struct RowRegs {
   u32x4 w[RPW][MAXC];
   float s[RPW][MAXC];  // MX-FP4 block scales
 
+  // chunks c = c0 + i*64 + lane for c < cend
   __device__ __forceinline__ void load(const char* row0, size_t rb, const uint8_t* s0, size_t sb,
-                                       int nrows, int c0, int nchunks, int lane) {
+                                       int nrows, int c0, int cend, int lane) {
 #pragma unroll
     for (int r = 0; r < RPW; ++r) {
 #pragma unroll
       for (int i = 0; i < MAXC; ++i) {
         const int c = c0 + i * kWave + lane;
-        if (r < nrows && c < nchunks) {
+        if (r < nrows && c < cend) {
           w[r][i] = ld_stream16(row0 + r * rb + (size_t)c * 16);
           if constexpr (WF == kMXFP4) s[r][i] = e8m0_to_f32(s0[r * sb + c]);
         }
@@ -138,35 +139,44 @@ struct GateUpArgs {
 };
 
 // h[r][n] = silu(<w_gate[e][n], x[t]>) * <w_up[e][n], x[t]> for every row r
-// of the slot's expert e (t = sorted_src[r] / k).  Block = 4 waves = 4*RPW
-// consecutive n of one active expert.
-template <int WF, int MAXC, int RPW, bool MULTISEG>
+// of the slot's expert e (t = sorted_src[r] / k).  Block = 4 waves; KS waves
+// share one group of RPW rows, each taking 1/KS of the reduction dimension
+// (more, lighter waves in flight), and their partial sums meet in LDS in a
+// fixed order.  A block covers 4/KS*RPW consecutive n of one active expert.
+template <int WF, int MAXC, int RPW, int KS, bool MULTISEG>
 __global__ __launch_bounds__(256) void gemv_gate_up_kernel(GateUpArgs a) {
+  static_assert(KS == 1 || !MULTISEG, "split reduction needs whole rows");
+  __shared__ float red[4][RPW][2];
   constexpr int CE = WT<WF>::CE;
   constexpr int SEG = MAXC * kWave;
   const int lane = lane_id();
   const int wave = threadIdx.x >> 6;
-  const int RB = 4 * RPW;
+  const int grp = wave / KS;
+  const int part = wave - grp * KS;
+  const int RB = (4 / KS) * RPW;
   const int tiles = (a.f + RB - 1) / RB;
   const int slot = blockIdx.x / tiles;
-  if (slot >= *a.num_active) return;
-  const int n0 = (blockIdx.x - slot * tiles) * RB + wave * RPW;
-  if (n0 >= a.f) return;
+  if (slot >= *a.num_active) return;  // uniform over the block
+  const int n0 = (blockIdx.x - slot * tiles) * RB + grp * RPW;
+  if (KS == 1 && n0 >= a.f) return;
   const int e = a.slot_info[4 * slot + 0];
-  const int nrows = min(RPW, a.f - n0);
+  const int nrows = max(0, min(RPW, a.f - n0));
   const int nchunks = a.d / CE;
+  const int cpp = (nchunks + KS - 1) / KS;  // chunks per part
+  const int cbeg = part * cpp;
+  const int cend = min(nchunks, cbeg + cpp);
   const size_t rb = WT<WF>::row_bytes(a.d);
   const size_t sb = (size_t)a.d / 32;
-  const size_t woff = (size_t)e * a.f + n0;
+  const size_t woff = (size_t)e * a.f + min(n0, a.f - 1);
   const char* gp = reinterpret_cast<const char*>(a.wg) + woff * rb;
   const char* up = reinterpret_cast<const char*>(a.wu) + woff * rb;
   const uint8_t* sgp = (WF == kMXFP4) ? a.sg + woff * sb : nullptr;
   const uint8_t* sup = (WF == kMXFP4) ? a.su + woff * sb : nullptr;
 
   RowRegs<WF, MAXC, RPW> G, U;
-  if (!MULTISEG) {  // whole rows, loaded once, before the token chain
-    G.load(gp, rb, sgp, sb, nrows, 0, nchunks, lane);
-    U.load(up, rb, sup, sb, nrows, 0, nchunks, lane);
+  if (!MULTISEG) {  // whole (part of the) rows, loaded once, before the token chain
+    G.load(gp, rb, sgp, sb, nrows, cbeg, cend, lane);
+    U.load(up, rb, sup, sb, nrows, cbeg, cend, lane);
   }
   const int r0 = a.slot_info[4 * slot + 1];
   const int ntok = a.slot_info[4 * slot + 2];
@@ -178,21 +188,21 @@ __global__ __launch_bounds__(256) void gemv_gate_up_kernel(GateUpArgs a) {
 #pragma unroll
     for (int r = 0; r < RPW; ++r) ag[r] = au[r] = 0.f;
     for (int seg = 0; seg < nseg; ++seg) {
-      const int c0 = seg * SEG;
+      const int c0 = cbeg + seg * SEG;
       if (MULTISEG) {
-        G.load(gp, rb, sgp, sb, nrows, c0, nchunks, lane);
-        U.load(up, rb, sup, sb, nrows, c0, nchunks, lane);
+        G.load(gp, rb, sgp, sb, nrows, c0, cend, lane);
+        U.load(up, rb, sup, sb, nrows, c0, cend, lane);
       }
       XChunk<WF> xc[MAXC];
 #pragma unroll
       for (int i = 0; i < MAXC; ++i) {
         const int c = c0 + i * kWave + lane;
-        if (c < nchunks) xc[i] = load_x<WF>(xr, c);
+        if (c < cend) xc[i] = load_x<WF>(xr, c);
       }
 #pragma unroll
       for (int i = 0; i < MAXC; ++i) {
         const int c = c0 + i * kWave + lane;
-        if (c < nchunks) {
+        if (c < cend) {
 #pragma unroll
           for (int r = 0; r < RPW; ++r) {
             if constexpr (WF == kMXFP4) {
@@ -206,13 +216,36 @@ __global__ __launch_bounds__(256) void gemv_gate_up_kernel(GateUpArgs a) {
         }
       }
     }
+    if constexpr (KS == 1) {
 #pragma unroll
-    for (int r = 0; r < RPW; ++r) {
-      if (r < nrows) {
+      for (int r = 0; r < RPW; ++r) {
+        if (r < nrows) {
+          const float gs = wave_sum(ag[r]);
+          const float us = wave_sum(au[r]);
+          if (lane == 0) store_act<WF>(a.h, (size_t)(r0 + tt) * a.f + n0 + r, silu(gs) * us);
+        }
+      }
+    } else {
+#pragma unroll
+      for (int r = 0; r < RPW; ++r) {
         const float gs = wave_sum(ag[r]);
         const float us = wave_sum(au[r]);
-        if (lane == 0) store_act<WF>(a.h, (size_t)(r0 + tt) * a.f + n0 + r, silu(gs) * us);
+        if (lane == 0) {
+          red[wave][r][0] = gs;
+          red[wave][r][1] = us;
+        }
       }
+      __syncthreads();
+      if (part == 0 && lane < nrows) {
+        float gs = 0.f, us = 0.f;
+#pragma unroll
+        for (int q = 0; q < KS; ++q) {
+          gs += red[grp * KS + q][lane][0];
+          us += red[grp * KS + q][lane][1];
+        }
+        store_act<WF>(a.h, (size_t)(r0 + tt) * a.f + n0 + lane, silu(gs) * us);
+      }
+      __syncthreads();
     }
   }
 }
@@ -293,6 +326,75 @@ __global__ __launch_bounds__(256) void gemv_down_kernel(DownArgs a) {
   }
 }
 
+struct DownCombineArgs {
+  const void* h;
+  const void* wd;
+  const uint8_t* sd;
+  const int* topk_idx;
+  const float* topk_w;
+  const int* dest_row;
+  void* out;
+  int d, f, k;
+};
+
+// Single token: down projection fused with the weighted combine.  Block =
+// k waves over the same RPW output rows, wave j on slot j's expert; the k
+// results meet in LDS and are summed in slot order (the combine kernel's
+// arithmetic), so no cross-block synchronisation is needed.
+template <int WF, int MAXC, int RPW>
+__global__ __launch_bounds__(1024) void gemv_down_combine_t1_kernel(DownCombineArgs a) {
+  __shared__ float ys[16][RPW];
+  constexpr int CE = WT<WF>::CE;
+  const int lane = lane_id();
+  const int j = threadIdx.x >> 6;
+  const int n0 = blockIdx.x * RPW;
+  const int nrows = min(RPW, a.d - n0);
+  const int e = a.topk_idx[j];
+  const int nchunks = a.f / CE;
+  const size_t rb = WT<WF>::row_bytes(a.f);
+  const size_t sb = (size_t)a.f / 32;
+  const size_t woff = (size_t)e * a.d + n0;
+  RowRegs<WF, MAXC, RPW> W;
+  W.load(reinterpret_cast<const char*>(a.wd) + woff * rb, rb,
+         (WF == kMXFP4) ? a.sd + woff * sb : nullptr, sb, nrows, 0, nchunks, lane);
+  const char* hr =
+      reinterpret_cast<const char*>(a.h) + (size_t)a.dest_row[j] * a.f * act_bytes<WF>();
+  XChunk<WF> hc[MAXC];
+#pragma unroll
+  for (int i = 0; i < MAXC; ++i) {
+    const int c = i * kWave + lane;
+    if (c < nchunks) hc[i] = load_x<WF>(hr, c);
+  }
+  float acc[RPW];
+#pragma unroll
+  for (int r = 0; r < RPW; ++r) acc[r] = 0.f;
+#pragma unroll
+  for (int i = 0; i < MAXC; ++i) {
+    const int c = i * kWave + lane;
+    if (c < nchunks) {
+#pragma unroll
+      for (int r = 0; r < RPW; ++r) {
+        if constexpr (WF == kMXFP4)
+          acc[r] = fmaf(dot_chunk<WF>(W.w[r][i], hc[i], 0.f), W.s[r][i], acc[r]);
+        else
+          acc[r] = dot_chunk<WF>(W.w[r][i], hc[i], acc[r]);
+      }
+    }
+  }
+#pragma unroll
+  for (int r = 0; r < RPW; ++r) {
+    const float y = wave_sum(acc[r]);
+    if (lane == 0) ys[j][r] = y;
+  }
+  __syncthreads();
+  if ((int)threadIdx.x < nrows) {
+    const int r = threadIdx.x;
+    float v = 0.f;
+    for (int q = 0; q < a.k; ++q) v = fmaf(a.topk_w[q], ys[q][r], v);
+    store_act<WF>(a.out, (size_t)n0 + r, v);
+  }
+}
+
 // ---------------------------------------------------------------- launch --
 int chunk_elems(int wf) { return wf == kF32 ? 4 : (wf == kBF16 ? 8 : 32); }
 
@@ -322,6 +424,17 @@ constexpr int rpw_for(int maxc) { return maxc >= 12 ? 1 : (maxc >= 6 ? 2 : 4); }
     default: { if constexpr (WFV != kMXFP4) { constexpr int MC = 16; CALL; } } break; \
   }
 
+#define MOE_MAXC12_SWITCH(WFV, MAXC, CALL)                                            \
+  switch (MAXC) {                                                                     \
+    case 1: { constexpr int MC = 1; CALL; } break;                                    \
+    case 2: { constexpr int MC = 2; CALL; } break;                                    \
+    case 3: { constexpr int MC = 3; CALL; } break;                                    \
+    case 4: { if constexpr (WFV != kMXFP4) { constexpr int MC = 4; CALL; } } break;   \
+    case 6: { if constexpr (WFV != kMXFP4) { constexpr int MC = 6; CALL; } } break;   \
+    case 8: { if constexpr (WFV != kMXFP4) { constexpr int MC = 8; CALL; } } break;   \
+    default: { if constexpr (WFV != kMXFP4) { constexpr int MC = 12; CALL; } } break; \
+  }
+
 #define MOE_WF_SWITCH(WFV, CALL)                          \
   switch (WFV) {                                          \
     case kF32: { constexpr int WF = kF32; CALL; } break;   \
@@ -344,10 +457,25 @@ hipError_t launch_gemv_gate_up(const Dims& dm, const void* x, const Plan& p, con
   const int nchunks = dm.d / chunk_elems(dm.wfmt);
   const int maxc = pick_maxc(nchunks, dm.wfmt);
   const bool multi = nchunks > maxc * kWave;
+  if (!multi && dm.wfmt != kMXFP4 && maxc >= 8) {
+    // long rows: two waves per row, each streaming half of it
+    const int maxc2 = pick_maxc((nchunks + 1) / 2, dm.wfmt);
+    const dim3 grid((unsigned)(max_active * ((dm.f + 1) / 2))), block(256);
+    if (dm.wfmt == kBF16) {
+      if (maxc2 <= 4) gemv_gate_up_kernel<kBF16, 4, 1, 2, false><<<grid, block, 0, s>>>(a);
+      else if (maxc2 <= 6) gemv_gate_up_kernel<kBF16, 6, 1, 2, false><<<grid, block, 0, s>>>(a);
+      else gemv_gate_up_kernel<kBF16, 8, 1, 2, false><<<grid, block, 0, s>>>(a);
+    } else {
+      if (maxc2 <= 4) gemv_gate_up_kernel<kF32, 4, 1, 2, false><<<grid, block, 0, s>>>(a);
+      else if (maxc2 <= 6) gemv_gate_up_kernel<kF32, 6, 1, 2, false><<<grid, block, 0, s>>>(a);
+      else gemv_gate_up_kernel<kF32, 8, 1, 2, false><<<grid, block, 0, s>>>(a);
+    }
+    return hipGetLastError();
+  }
   const int rpw = rpw_for(maxc);
   const dim3 grid((unsigned)(max_active * ((dm.f + 4 * rpw - 1) / (4 * rpw)))), block(256);
   MOE_WF_SWITCH(dm.wfmt, MOE_MAXC_SWITCH(WF, maxc, MOE_SEG_SWITCH(multi, (
-      gemv_gate_up_kernel<WF, MC, rpw_for(MC), MS><<<grid, block, 0, s>>>(a)))));
+      gemv_gate_up_kernel<WF, MC, rpw_for(MC), 1, MS><<<grid, block, 0, s>>>(a)))));
   return hipGetLastError();
 }
 
@@ -363,6 +491,28 @@ hipError_t launch_gemv_down(const Dims& dm, const void* h, const Plan& p, const 
   const dim3 grid((unsigned)(max_active * ((dm.d + 4 * rpw - 1) / (4 * rpw)))), block(256);
   MOE_WF_SWITCH(dm.wfmt, MOE_MAXC_SWITCH(WF, maxc, MOE_SEG_SWITCH(multi, (
       gemv_down_kernel<WF, MC, rpw_for(MC), MS><<<grid, block, 0, s>>>(a)))));
+  return hipGetLastError();
+}
+
+bool gemv_down_combine_t1_ok(const Dims& dm) {
+  // up to 1024 threads per block leave 128 VGPRs per lane: keep rows short
+  // enough that the weight registers fit without spilling
+  const int nchunks = dm.f / chunk_elems(dm.wfmt);
+  const int maxc = pick_maxc(nchunks, dm.wfmt);
+  const int limit = dm.wfmt == kMXFP4 ? 3 : 12;
+  return dm.T == 1 && dm.k <= 16 && nchunks <= maxc * kWave && maxc <= limit;
+}
+
+hipError_t launch_gemv_down_combine_t1(const Dims& dm, const void* h, const Plan& p,
+                                       const int* topk_idx, const float* topk_w,
+                                       const Weights& w, void* out, hipStream_t s) {
+  LaunchTimer tm("gemv_down_combine_t1", s);
+  DownCombineArgs a{h, w.wd, w.sd, topk_idx, topk_w, p.dest_row, out, dm.d, dm.f, dm.k};
+  const int maxc = pick_maxc(dm.f / chunk_elems(dm.wfmt), dm.wfmt);
+  const int rpw = rpw_for(maxc);
+  const dim3 grid((unsigned)((dm.d + rpw - 1) / rpw)), block(64 * dm.k);
+  MOE_WF_SWITCH(dm.wfmt, MOE_MAXC12_SWITCH(WF, maxc, (
+      gemv_down_combine_t1_kernel<WF, MC, rpw_for(MC)><<<grid, block, 0, s>>>(a))));
   return hipGetLastError();
 }
 

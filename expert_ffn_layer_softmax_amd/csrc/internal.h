@@ -65,6 +65,9 @@ hipError_t launch_route_topk(const float* logits, int T, int E, int k, int* topk
 // Route and permute in one workgroup for T <= kDecodeMaxT (T*k <= 1024).
 hipError_t launch_route_permute_small(const float* logits, int T, int E, int k, int* topk_idx,
                                       float* topk_w, const Plan& p, hipStream_t s);
+// T == 1: one wave routes the token and writes the whole plan.
+hipError_t launch_route_plan_t1(const float* logits, int E, int k, int* topk_idx, float* topk_w,
+                                const Plan& p, hipStream_t s);
 hipError_t launch_permute(const int* topk_idx, int T, int E, int k, const Plan& p,
                           bool with_lists, hipStream_t s);
 hipError_t launch_plan_from_offsets(const int* offsets, int E, const Plan& p, hipStream_t s);
@@ -72,6 +75,12 @@ hipError_t launch_gemv_gate_up(const Dims& dm, const void* x, const Plan& p, con
                                void* h, hipStream_t s);
 hipError_t launch_gemv_down(const Dims& dm, const void* h, const Plan& p, const Weights& w,
                             float* y_sorted, hipStream_t s);
+// T == 1 (k <= 16, one segment per row): down projection and weighted
+// combine in one kernel, writing `out` directly.
+bool gemv_down_combine_t1_ok(const Dims& dm);
+hipError_t launch_gemv_down_combine_t1(const Dims& dm, const void* h, const Plan& p,
+                                       const int* topk_idx, const float* topk_w,
+                                       const Weights& w, void* out, hipStream_t s);
 hipError_t launch_combine(const Dims& dm, const float* y_sorted, const int* dest_row,
                           const float* topk_w, void* out, hipStream_t s);
 

@@ -155,7 +155,67 @@ __global__ __launch_bounds__(kPermThreads) void route_permute_small_kernel(
   permute_block([&](int q) { return keys[q]; }, T * k, E, p, true, sh);
 }
 
+// Single-token layers: one wave routes the token and writes the whole plan.
+// The k selected experts are distinct, so pair j's sorted position is the
+// number of selected experts below its own.
+template <int VPL>
+__global__ __launch_bounds__(64) void route_plan_t1_kernel(const float* __restrict__ logits, int E,
+                                                           int k, int* __restrict__ topk_idx,
+                                                           float* __restrict__ topk_w, Plan p) {
+  const int lane = lane_id();
+  int sel_i;
+  float sel_w;
+  route_token<VPL>(logits, E, k, sel_i, sel_w);
+  int rank = 0;
+  for (int j = 0; j < k; ++j) rank += (__builtin_amdgcn_readlane(sel_i, j) < sel_i) ? 1 : 0;
+  if (lane < k) {
+    topk_idx[lane] = sel_i;
+    topk_w[lane] = sel_w;
+    p.sorted_src[rank] = lane;
+    p.dest_row[lane] = rank;
+    p.active[rank] = sel_i;
+    p.slot_info[4 * rank + 0] = sel_i;
+    p.slot_info[4 * rank + 1] = rank;
+    p.slot_info[4 * rank + 2] = 1;
+    p.slot_info[4 * rank + 3] = 0;
+    p.mtiles[2 * rank] = sel_i;
+    p.mtiles[2 * rank + 1] = rank;
+  }
+  for (int e = lane; e < E; e += kWave) {
+    int c = 0, below = 0;
+    for (int j = 0; j < k; ++j) {
+      const int o = __builtin_amdgcn_readlane(sel_i, j);
+      c += (o == e) ? 1 : 0;
+      below += (o < e) ? 1 : 0;
+    }
+    p.counts[e] = c;
+    p.offsets[e] = below;
+  }
+  if (lane == 0) {
+    p.offsets[E] = k;
+    *p.num_active = k;
+    *p.num_mtiles = k;
+  }
+}
+
 }  // namespace
+
+hipError_t launch_route_plan_t1(const float* logits, int E, int k, int* topk_idx, float* topk_w,
+                                const Plan& p, hipStream_t s) {
+  LaunchTimer tm("route_plan_t1", s);
+  const dim3 g(1), b(kWave);
+  if (E <= 64)
+    route_plan_t1_kernel<1><<<g, b, 0, s>>>(logits, E, k, topk_idx, topk_w, p);
+  else if (E <= 128)
+    route_plan_t1_kernel<2><<<g, b, 0, s>>>(logits, E, k, topk_idx, topk_w, p);
+  else if (E <= 256)
+    route_plan_t1_kernel<4><<<g, b, 0, s>>>(logits, E, k, topk_idx, topk_w, p);
+  else if (E <= 512)
+    route_plan_t1_kernel<8><<<g, b, 0, s>>>(logits, E, k, topk_idx, topk_w, p);
+  else
+    route_plan_t1_kernel<16><<<g, b, 0, s>>>(logits, E, k, topk_idx, topk_w, p);
+  return hipGetLastError();
+}
 
 hipError_t launch_permute(const int* topk_idx, int T, int E, int k, const Plan& p,
                           bool with_lists, hipStream_t s) {

@@ -96,6 +96,11 @@ SMALL = [
     ("f32_t3", 3, 96, 5, 5, 32, "f32", "f32"),
     ("f32_t64", 64, 128, 16, 4, 64, "f32", "f32"),
     ("f32_segd", 2, 4160, 3, 2, 32, "f32", "f32"),
+    ("bf16_t1_k16", 1, 512, 64, 16, 224, "bf16", "bf16"),
+    ("bf16_t1_k20", 1, 256, 32, 20, 64, "bf16", "bf16"),
+    ("f32_t1", 1, 128, 8, 3, 64, "f32", "f32"),
+    ("mx_t1_bigf", 1, 64, 4, 2, 8192, "bf16", "mxfp4"),
+    ("bf16_t1_bigf", 1, 64, 4, 2, 16384, "bf16", "bf16"),
 ]
 
 
@@ -155,6 +160,26 @@ def test_determinism_and_t0():
     e = torch.empty(0, 256, dtype=torch.bfloat16, device="cuda")
     r = moe_layer_forward(e, w, 4, logits=torch.empty(0, 16, device="cuda"))
     assert r["out"].shape == (0, 256)
+
+
+@pytest.mark.parametrize("wfmt,k", [("bf16", 8), ("mxfp4", 8), ("f32", 4), ("bf16", 16)])
+def test_single_token_fused_path_equals_stagewise(wfmt, k):
+    """The single-token layer (fused down+combine) is bit-identical to
+    route -> permute -> expert_ffn -> combine called one by one."""
+    from expert_ffn_layer_softmax_amd import (moe_combine, moe_expert_ffn, moe_layer_forward,
+                                              moe_permute, moe_route)
+    act = "f32" if wfmt == "f32" else "bf16"
+    wl = Workload("t1eq", T=1, d=1024, E=32, k=k, f=352, act=act, wfmt=wfmt, seed=31 + k,
+                  x_std=1.0, wg_std=1024 ** -0.5, wu_std=1024 ** -0.5, wd_std=352 ** -0.5)
+    x, w, _, logits = make_inputs(wl)
+    fused = moe_layer_forward(x, w, k, logits=logits)["out"]
+    idx, tw = moe_route(logits, k)
+    counts, offsets, sorted_src, dest_row = moe_permute(idx, wl.E)
+    y = moe_expert_ffn(x, offsets, sorted_src, k, w)
+    staged = moe_combine(y, dest_row, tw, x.dtype)
+    torch.cuda.synchronize()
+    assert torch.equal(fused.view(torch.int16) if act == "bf16" else fused.view(torch.int32),
+                       staged.view(torch.int16) if act == "bf16" else staged.view(torch.int32))
 
 
 # --------------------------------------------------- individual entry points
