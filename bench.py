@@ -64,7 +64,10 @@ def _source_digest(files) -> str:
 DOMINANT = {
     "decode": ("gemv_gate_up", ["expert_ffn_layer_softmax_amd/csrc/gemv.hip",
                                 "expert_ffn_layer_softmax_amd/csrc/device.h"]),
+    "prefill": ("gg_gate_up", ["expert_ffn_layer_softmax_amd/csrc/grouped_gemm.hip",
+                               "expert_ffn_layer_softmax_amd/csrc/device.h"]),
 }
+RIDGE_FLOP_PER_BYTE = BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9)
 
 
 def _traffic(kernel: str, workload: str, digest: str):
@@ -204,16 +207,27 @@ def main():
     torch.cuda.synchronize()
     moe_timing_stop()
     path = "decode" if wl.T <= 16 else "prefill"
-    kname, srcs = DOMINANT.get(path, DOMINANT["decode"])
+    kname, srcs = DOMINANT[path]
     n_launch, tot_ms = moe_timing_query(kname)
-    kernel_us = tot_ms * 1e3 / max(n_launch, 1)
+    if n_launch == 0:
+        raise RuntimeError(f"no timed launches of {kname}")
+    kernel_us = tot_ms * 1e3 / n_launch
     eb = _expert_bytes(wl)
     act_b = 4 if wl.act == "f32" else 2
     mean_uniq = sum(uniq[i % nsets] for i in range(args.steps)) / args.steps
-    # gate/up kernel: active experts' gate+up weights, x read, h written
+    # the gate/up kernel's algorithmic work: the active experts' gate and up
+    # weights read once, x read, h written; 2 FLOPs per MAC over T*k rows
     k_bytes = mean_uniq * eb["gate_up"] + wl.T * wl.d * act_b + wl.T * k * wl.f * act_b
-    achieved = k_bytes / (kernel_us * 1e-6) / 1e9
+    k_flops = 4.0 * wl.T * k * wl.d * wl.f
+    if k_flops / k_bytes > RIDGE_FLOP_PER_BYTE:
+        bound, unit, peak = "mfma", "TFLOP/s", BF16_PEAK_TFLOPS
+        achieved = k_flops / (kernel_us * 1e-6) / 1e12
+    else:
+        bound, unit, peak = "hbm", "GB/s", HBM_PEAK_GBS
+        achieved = k_bytes / (kernel_us * 1e-6) / 1e9
     step_bytes = (mean_uniq * eb["total"] + 2 * wl.T * wl.d * act_b + wl.T * wl.E * 4 + wl.T * k * 8)
+    step_flops = 6.0 * wl.T * k * wl.d * wl.f
+    t_floor = max(step_bytes / (HBM_PEAK_GBS * 1e9), step_flops / (BF16_PEAK_TFLOPS * 1e12))
     digest = _source_digest(srcs)
     traffic = _traffic(kname, wl.name, digest)
     breakdown = {}
@@ -229,12 +243,15 @@ def main():
         "dtype": "bf16" if wl.act == "bf16" else "f32", "data": "synthetic",
         "config": {"workload": wl.name, "T": wl.T, "d": wl.d, "E": wl.E, "k": k, "f": wl.f,
                    "weights": wl.wfmt, "logit_sets": nsets, "mean_unique_experts": round(mean_uniq, 2)},
-        "roofline": {"bound": "hbm", "kernel": kname, "achieved": round(achieved, 1),
-                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+        "roofline": {"bound": bound, "kernel": kname, "achieved": round(achieved, 1),
+                     "peak": peak, "unit": unit, "frac": round(achieved / peak, 4),
                      "traffic": traffic, "kernel_us": round(kernel_us, 2),
-                     "algorithmic_bytes_per_launch": int(k_bytes)},
-        "step": {"algorithmic_bytes": int(step_bytes),
+                     "algorithmic_bytes_per_launch": int(k_bytes),
+                     "algorithmic_flops_per_launch": k_flops},
+        "step": {"algorithmic_bytes": int(step_bytes), "algorithmic_flops": step_flops,
                  "hbm_frac": round(step_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                 "mfma_frac": round(step_flops / (ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4),
+                 "attainable_frac": round(t_floor / (ms * 1e-3), 4),
                  "kernel_us": breakdown},
     }
     if not args.no_cpu:

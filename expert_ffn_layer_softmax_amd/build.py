@@ -18,7 +18,7 @@ CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libmoe_mi355x.so")
 
-SOURCES = ["abi.cpp", "route.hip", "permute.hip", "gemv.hip", "combine.hip"]
+SOURCES = ["abi.cpp", "route.hip", "permute.hip", "gemv.hip", "combine.hip", "grouped_gemm.hip"]
 
 ARCH = "gfx950"
 COMMON = [

@@ -67,7 +67,7 @@ WsLayout ws_layout(const Dims& dm) {
   L.active = o;      o = align_up(o + E * 4);
   L.num_active = o;  o = align_up(o + 4);
   L.slot_info = o;   o = align_up(o + E * 16);
-  L.mtiles = o;      o = align_up(o + max_mtiles * 8);
+  L.mtiles = o;      o = align_up(o + max_mtiles * kMtileInts * 4);
   L.num_mtiles = o;  o = align_up(o + 4);
   L.h = o;           o = align_up(o + Tk * (size_t)dm.f * act);
   L.y_sorted = o;    o = align_up(o + Tk * (size_t)dm.d * 4);
@@ -135,6 +135,11 @@ moe_status_t check_weights(const moe_expert_weights_t* w, const Dims& dm, Weight
 // Expert FFN on a prepared plan (offsets, sorted_src, active list).
 hipError_t run_expert_ffn(const Dims& dm, const void* x, const Plan& p, const Weights& w,
                           void* h, float* y_sorted, hipStream_t s) {
+  if (grouped_gemm_ok(dm)) {
+    hipError_t e = launch_gg_gate_up(dm, x, p, w, h, s);
+    if (e != hipSuccess) return e;
+    return launch_gg_down(dm, h, p, w, y_sorted, s);
+  }
   hipError_t e = launch_gemv_gate_up(dm, x, p, w, h, s);
   if (e != hipSuccess) return e;
   return launch_gemv_down(dm, h, p, w, y_sorted, s);

@@ -12,8 +12,11 @@ namespace moe {
 enum Fmt : int { kF32 = 0, kBF16 = 1, kMXFP4 = 2 };
 
 // Rows per m-tile of the grouped MFMA GEMMs; the tile list in the workspace
-// is sized for this value.
+// is sized for this value.  Each m-tile entry holds kMtileInts ints:
+// expert, first row, rows in the tile, index of the expert's first m-tile,
+// number of m-tiles of the expert, 3 unused.
 constexpr int kGemmBM = 128;
+constexpr int kMtileInts = 8;
 
 // Largest T routed and permuted by the single-workgroup decode kernel.
 constexpr int kDecodeMaxT = 16;
@@ -44,7 +47,7 @@ struct Plan {
   int* active;      // [E] experts with at least one routed pair, ascending
   int* num_active;  // [1]
   int* slot_info;   // [E][4] per active slot: expert, first row, rows, 0
-  int* mtiles;      // [2 * max_mtiles] (expert, first row) per m-tile of kGemmBM rows
+  int* mtiles;      // [kMtileInts * max_mtiles] m-tile entries (see kMtileInts)
   int* num_mtiles;  // [1]
 };
 
@@ -81,6 +84,14 @@ bool gemv_down_combine_t1_ok(const Dims& dm);
 hipError_t launch_gemv_down_combine_t1(const Dims& dm, const void* h, const Plan& p,
                                        const int* topk_idx, const float* topk_w,
                                        const Weights& w, void* out, hipStream_t s);
+// Grouped MFMA GEMMs for many tokens per expert (bf16 or MX-FP4 weights,
+// bf16 activations).  gate/up: h = silu(x W_g^T) * (x W_u^T); down: y = h W_d^T.
+bool grouped_gemm_ok(const Dims& dm);
+size_t grouped_gemm_max_mtiles(const Dims& dm);
+hipError_t launch_gg_gate_up(const Dims& dm, const void* x, const Plan& p, const Weights& w,
+                             void* h, hipStream_t s);
+hipError_t launch_gg_down(const Dims& dm, const void* h, const Plan& p, const Weights& w,
+                          float* y_sorted, hipStream_t s);
 hipError_t launch_combine(const Dims& dm, const float* y_sorted, const int* dest_row,
                           const float* topk_w, void* out, hipStream_t s);
 

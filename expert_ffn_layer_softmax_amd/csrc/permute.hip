@@ -3,8 +3,8 @@
 //
 // Besides the four public outputs it can write the execution plan the expert
 // kernels read: the ascending list of experts with at least one pair, a
-// per-slot (expert, first row, rows) table, and the list of m-tiles (expert,
-// first row) of kGemmBM rows for the grouped MFMA GEMMs.  Nothing here is read
+// per-slot (expert, first row, rows) table, and the list of m-tiles of up to
+// kGemmBM rows for the grouped MFMA GEMMs (entry layout: internal.h).  Nothing here is read
 // back by the host.
 #include "device.h"
 #include "internal.h"
@@ -42,8 +42,12 @@ __device__ void write_lists(int c, int first, int E, const Plan& p, int* tmp) {
   const int nt = (e < E) ? (c + kGemmBM - 1) / kGemmBM : 0;
   const int tpos = block_exclusive_scan(nt, tmp, &total);
   for (int i = 0; i < nt; ++i) {
-    p.mtiles[2 * (tpos + i)] = e;
-    p.mtiles[2 * (tpos + i) + 1] = first + i * kGemmBM;
+    int* m = p.mtiles + kMtileInts * (tpos + i);
+    m[0] = e;
+    m[1] = first + i * kGemmBM;
+    m[2] = min(kGemmBM, c - i * kGemmBM);
+    m[3] = tpos;
+    m[4] = nt;
   }
   if (threadIdx.x == 0) *p.num_mtiles = total;
 }
@@ -178,8 +182,12 @@ __global__ __launch_bounds__(64) void route_plan_t1_kernel(const float* __restri
     p.slot_info[4 * rank + 1] = rank;
     p.slot_info[4 * rank + 2] = 1;
     p.slot_info[4 * rank + 3] = 0;
-    p.mtiles[2 * rank] = sel_i;
-    p.mtiles[2 * rank + 1] = rank;
+    int* m = p.mtiles + kMtileInts * rank;
+    m[0] = sel_i;
+    m[1] = rank;
+    m[2] = 1;
+    m[3] = rank;
+    m[4] = 1;
   }
   for (int e = lane; e < E; e += kWave) {
     int c = 0, below = 0;

@@ -101,6 +101,13 @@ SMALL = [
     ("f32_t1", 1, 128, 8, 3, 64, "f32", "f32"),
     ("mx_t1_bigf", 1, 64, 4, 2, 8192, "bf16", "mxfp4"),
     ("bf16_t1_bigf", 1, 64, 4, 2, 16384, "bf16", "bf16"),
+    # grouped MFMA GEMM path (T > 16, d and f multiples of 128)
+    ("gg_bf16_t17", 17, 256, 8, 2, 128, "bf16", "bf16"),
+    ("gg_bf16_t300", 300, 512, 16, 4, 384, "bf16", "bf16"),
+    ("gg_bf16_hot", 600, 384, 4, 2, 256, "bf16", "bf16"),      # ~300 rows/expert: 3 m-tiles
+    ("gg_bf16_ntail", 64, 640, 6, 3, 128, "bf16", "bf16"),     # down N=640: partial n-tile
+    ("gg_mx_t100", 100, 256, 8, 4, 256, "bf16", "mxfp4"),
+    ("gg_mx_hot", 700, 512, 5, 2, 384, "bf16", "mxfp4"),
 ]
 
 
@@ -250,6 +257,37 @@ def test_verify_bf16_full(full_bf16_weights):
     err = rel_l2(got, ref["out"])
     log(f"  rel_l2={err:.3e} unique experts={int((ref['counts'] > 0).sum())}")
     assert err <= 5e-3
+
+
+@pytest.mark.parametrize("name", ["prefill_bf16", "prefill_mxfp4"])
+def test_prefill_full_sampled(name, full_bf16_weights):
+    """T=4096 with skewed load: routing checked in full; outputs on sampled
+    tokens (each token's output depends only on its own row and logits)."""
+    wl = WORKLOADS[name]
+    log(f"{name} full (T=4096), sampled tokens")
+    w = full_bf16_weights if wl.wfmt == "bf16" else gen_expert_weights(wl, "cuda")
+    x, w, w_r, logits = make_inputs(wl, weights=w)
+    from expert_ffn_layer_softmax_amd import moe_layer_forward
+    res = moe_layer_forward(x, w, wl.k, logits=logits)
+    torch.cuda.synchronize()
+    lg = res["logits"].cpu().numpy()
+    check_routing(res, lg, wl.k, wl.E)
+    counts = np.bincount(res["topk_idx"].cpu().numpy().ravel(), minlength=wl.E)
+    log(f"  expert load: min {counts.min()} mean {counts.mean():.0f} max {counts.max()}")
+    rng = np.random.default_rng(7)
+    # include the tokens routed to the hottest expert's last rows (ragged m-tile)
+    hot = int(np.argmax(counts))
+    hot_tokens = np.nonzero((res["topk_idx"].cpu().numpy() == hot).any(1))[0]
+    S = np.unique(np.concatenate([rng.choice(wl.T, 4, replace=False), hot_tokens[-2:]]))
+    xh = to_host_act(x)
+    ref = oracle.layer(xh[S], lg[S], wl.k, expert_getter(w, wl.wfmt), E=wl.E)
+    got = to_host_act(res["out"])[S]
+    err = rel_l2(got, ref["out"])
+    log(f"  sampled tokens {S.tolist()}: rel_l2={err:.3e}")
+    assert err <= (MXFP4_TOL if wl.wfmt == "mxfp4" else 5e-3)
+    if wl.wfmt == "mxfp4":
+        del w
+        torch.cuda.empty_cache()
 
 
 def test_decode_mxfp4_full():
