@@ -14,7 +14,9 @@ import os
 import torch  # loaded first: the library then binds to torch's HIP runtime
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_PKG, "libmoe_mi355x.so")
+# MOE_MI355X_LIB may name another build of the same library (e.g. a tuning
+# variant); by default the in-tree build is loaded.
+LIB_PATH = os.environ.get("MOE_MI355X_LIB") or os.path.join(_PKG, "libmoe_mi355x.so")
 
 MOE_OK = 0
 MOE_DTYPE_F32, MOE_DTYPE_BF16, MOE_DTYPE_MXFP4 = 0, 1, 2

@@ -7,7 +7,7 @@
 #include <string>
 #include <vector>
 
-#include "../../include/moe.h"
+#include "moe.h"
 #include "internal.h"
 
 namespace moe {

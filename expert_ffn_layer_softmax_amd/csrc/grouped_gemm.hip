@@ -11,15 +11,36 @@
 // convert (the block scale is applied by the instruction), then fed to the
 // same MFMA.
 //
-// Tile: 128 rows (one m-tile of an expert) x 4 waves; each wave owns two
-// 32-column B operands (gate/up: the same 32 columns of W_gate and W_up, so
-// the SwiGLU epilogue is wave-local; down: 64 consecutive columns of W_down).
-// K advances 64 per step.  B (weights, read once from HBM) streams straight
-// into registers D steps ahead (plain cached loads: the other m-tiles of the
-// same panel read it from L2); A (activation rows, shared by the 4 waves)
-// goes through a D-deep register ring into a double-buffered, XOR-swizzled
-// LDS tile.  Both rings lead by D steps so that waiting for the oldest load
-// never waits for younger ones.
+// Two tile schemes, both 128 rows (one m-tile of an expert) x 8 waves (two
+// per SIMD), K advancing 64 per step:
+//
+// bf16 weights (gg_lds_kernel): 256 B-columns per tile (gate/up: 128
+// columns of W_gate and the same 128 of W_up, so the SwiGLU epilogue is
+// wave-local; down: 256 columns of W_down), K advancing 64 per step.  Both
+// operands go through double-buffered, XOR-swizzled LDS tiles.  512 threads
+// (8 waves, two per SIMD) fetch each step with 16-byte loads, 8 consecutive
+// threads per 128-byte row segment, into a D-deep register ring: loads for a
+// step are issued D steps before its MFMAs.  Every step issues the same loads
+// (past the end they re-read the last step), so waiting for the oldest ring
+// entry never waits for younger ones.  MX-FP4 weights are converted to bf16
+// (block scale applied by the instruction) on their way into LDS.  Waves form
+// a 2 (rows) x 4 (columns) grid, each owning 64 rows x (2 x 32) columns.
+//
+// MX-FP4 weights (gg_direct_b_kernel): h wave owns all
+// 128 rows and two 32-column B operands: gate/up: the same 32 columns of
+// W_gate and W_up (the SwiGLU epilogue stays wave-local), so a tile spans
+// 256 columns of each; down: 64 consecutive columns of W_down, 512 per tile.
+// K advances 64 per step.  A weight column belongs to exactly one wave, so
+// the weights stream straight from memory into registers, D steps ahead; the
+// activation rows, shared by all 8 waves, go through a D-deep register ring
+// into a double-buffered, XOR-swizzled LDS tile (8 threads per 128-byte row
+// segment, full cache lines).  Every step issues the same loads (past the end
+// they re-read the last step), so waiting for the oldest ring entry never
+// waits for younger ones.  Per substep a wave reads 4 A fragments from LDS for
+// 8 MFMAs; B never touches LDS.
+//
+// The weights are 4x smaller there, so streaming them per wave into
+// registers costs little and keeps LDS traffic to the shared activations.
 //
 // Tile order: logical tiles run expert by expert, n-tile by n-tile, m-tile
 // by m-tile, and each XCD (blockIdx % 8 under round-robin dispatch) takes a
@@ -37,7 +58,7 @@ typedef float f32x16_t __attribute__((ext_vector_type(16)));
 
 constexpr int BM = kGemmBM;  // 128
 constexpr int BK = 64;
-constexpr int kThreads = 256;
+constexpr int kThreads = 512;
 constexpr int kXcds = 8;
 
 struct GGArgs {
@@ -53,6 +74,18 @@ struct GGArgs {
   int K, N, k, ntiles;
 };
 
+// LDS tiles hold rows of 128 B (64 bf16 of K).  16-byte unit u of row r
+// lives at unit u ^ f(r), f(r) = (r & 7) ^ ((r >> 3) & 1): a fragment read
+// (16 consecutive rows, one unit) then touches 16 distinct 16-byte bank
+// groups, and so do 8 consecutive rows, and the row-wise stores of the
+// global fetch (8 units of one row per 8 lanes) stay conflict-free too.
+__device__ __forceinline__ int t_off(int row, int unit) {
+  const int f = (row & 7) ^ ((row >> 3) & 1);
+  return row * (BK * 2) + ((unit ^ f) << 4);
+}
+
+constexpr int kAPieces = BM * 8 / kThreads;  // 16-B pieces of A per thread per step
+
 template <int WF>
 struct BRegs;
 template <>
@@ -60,7 +93,7 @@ struct BRegs<kBF16> {  // 4 x 16 B per matrix per step: the lane's 32 K-values
   u32x4 v[2][4];
 };
 template <>
-struct BRegs<kMXFP4> {  // 16 B of codes and one scale per matrix per step
+struct BRegs<kMXFP4> {  // 16 B of codes (one 32-element block) and its scale per matrix
   u32x4 v[2];
   uint32_t s[2];
 };
@@ -99,19 +132,232 @@ __device__ __forceinline__ bf16x8_t b_frag(const BRegs<WF>& b, int m, int s) {
   }
 }
 
-// LDS A tile: 128 rows x 128 B; 16-byte unit u of row r lives at unit
-// u ^ (r & 7), so the 8 rows read together by a fragment hit 8 distinct
-// bank groups.
-__device__ __forceinline__ int a_off(int row, int unit) {
-  return row * (BK * 2) + ((unit ^ (row & 7)) << 4);
-}
+constexpr int BN = 256;                 // gg_lds_kernel: B-tile rows (weight columns) per tile
+constexpr int kBPieces = BN * 8 / kThreads;   // bf16 B pieces per thread per step
+
+// One step's global data held by a thread between its load and its LDS store.
+template <int WF>
+struct Stage;
+template <>
+struct Stage<kBF16> {
+  u32x4 a[kAPieces];
+  u32x4 b[kBPieces];
+};
+template <>
+struct Stage<kMXFP4> {  // B: 16 B of codes (one 32-element block) + its scale
+  u32x4 a[kAPieces];
+  u32x4 b;
+  uint32_t s;
+};
 
 template <int WF, bool GATEUP, int D>
-__global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GGArgs a) {
-  __shared__ __align__(16) char lds[2][BM * BK * 2];
+__global__ __launch_bounds__(kThreads) void gg_lds_kernel(GGArgs a) {
+  __shared__ __align__(16) char lds_a[2][BM * BK * 2];
+  __shared__ __align__(16) char lds_b[2][BN * BK * 2];
   const int tid = threadIdx.x;
   const int lane = lane_id();
   const int wave = tid >> 6;
+  const int wm = wave >> 2;  // 0..1: rows 64*wm ..
+  const int wn = wave & 3;   // 0..3: columns
+  const int half = lane >> 5;
+  const int cl = lane & 31;
+
+  // ---- tile
+  const int num_tiles = *a.num_mtiles * a.ntiles;
+  const int per_xcd = (num_tiles + kXcds - 1) / kXcds;
+  const int slot = blockIdx.x / kXcds;
+  if (slot >= per_xcd) return;
+  const int L = (blockIdx.x % kXcds) * per_xcd + slot;
+  if (L >= num_tiles) return;
+  const int* eq = a.mtiles + kMtileInts * (L / a.ntiles);
+  const int e = eq[0];
+  const int first_mt = eq[3];
+  const int nmt = eq[4];
+  const int local = L - first_mt * a.ntiles;
+  const int ntile = local / nmt;
+  const int* em = a.mtiles + kMtileInts * (first_mt + (local - ntile * nmt));
+  const int row0 = em[1];
+  const int nrows = em[2];
+  const int nbase = ntile * (GATEUP ? BN / 2 : BN);
+
+  // ---- global sources of this thread's pieces
+  const int unit = tid & 7;
+  const size_t a_rb = (size_t)a.K * 2;
+  const char* ap[kAPieces];
+#pragma unroll
+  for (int i = 0; i < kAPieces; ++i) {
+    const int r = (tid >> 3) + i * (kThreads / 8);
+    const int src = row0 + min(r, nrows - 1);
+    ap[i] = reinterpret_cast<const char*>(a.a_src) +
+            (GATEUP ? (size_t)(a.sorted_src[src] / a.k) : (size_t)src) * a_rb + unit * 16;
+  }
+  // B-tile row r -> weight matrix and column
+  auto bcol = [&](int r, const void*& w, const uint8_t*& sc) {
+    int col;
+    if (GATEUP) {
+      const bool up = r >= BN / 2;
+      w = up ? a.w1 : a.w0;
+      sc = up ? a.s1 : a.s0;
+      col = nbase + (up ? r - BN / 2 : r);
+    } else {
+      w = a.w0;
+      sc = a.s0;
+      col = nbase + r;
+    }
+    return min(col, a.N - 1);
+  };
+  constexpr int NBP = (WF == kBF16) ? kBPieces : 1;
+  const char* bp[NBP];
+  const uint8_t* sp = nullptr;
+  int b_unit0 = 0;  // MX-FP4: first LDS unit this thread's block fills
+  if constexpr (WF == kBF16) {
+#pragma unroll
+    for (int i = 0; i < kBPieces; ++i) {
+      const void* w;
+      const uint8_t* sc;
+      const int col = bcol((tid >> 3) + i * (kThreads / 8), w, sc);
+      bp[i] = reinterpret_cast<const char*>(w) + ((size_t)e * a.N + col) * a_rb + unit * 16;
+    }
+  } else {
+    const void* w;
+    const uint8_t* sc;
+    const int col = bcol(tid >> 1, w, sc);
+    const int hb = tid & 1;  // which 32-element block of the step
+    bp[0] = reinterpret_cast<const char*>(w) + ((size_t)e * a.N + col) * (a.K / 2) + hb * 16;
+    sp = sc + ((size_t)e * a.N + col) * (a.K / 32) + hb;
+    b_unit0 = hb * 4;
+  }
+
+  const int nk = a.K / BK;
+  Stage<WF> ring[D];
+  auto load_stage = [&](Stage<WF>& st, int kk) {
+#pragma unroll
+    for (int i = 0; i < kAPieces; ++i) st.a[i] = ld16(ap[i] + (size_t)kk * (BK * 2));
+    if constexpr (WF == kBF16) {
+#pragma unroll
+      for (int i = 0; i < kBPieces; ++i) st.b[i] = ld16(bp[i] + (size_t)kk * (BK * 2));
+    } else {
+      st.b = ld16(bp[0] + (size_t)kk * (BK / 2));
+      st.s = sp[2 * kk];
+    }
+  };
+  auto store_stage = [&](const Stage<WF>& st, int buf) {
+#pragma unroll
+    for (int i = 0; i < kAPieces; ++i)
+      *reinterpret_cast<u32x4*>(&lds_a[buf][t_off((tid >> 3) + i * (kThreads / 8), unit)]) = st.a[i];
+    if constexpr (WF == kBF16) {
+#pragma unroll
+      for (int i = 0; i < kBPieces; ++i)
+        *reinterpret_cast<u32x4*>(&lds_b[buf][t_off((tid >> 3) + i * (kThreads / 8), unit)]) = st.b[i];
+    } else {
+      const float scale = e8m0_to_f32(st.s);
+      const uint32_t cw[4] = {st.b.x, st.b.y, st.b.z, st.b.w};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        u32x4 r;
+        r.x = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(cw[j], scale, 0));
+        r.y = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(cw[j], scale, 1));
+        r.z = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(cw[j], scale, 2));
+        r.w = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(cw[j], scale, 3));
+        *reinterpret_cast<u32x4*>(&lds_b[buf][t_off(tid >> 1, b_unit0 + j)]) = r;
+      }
+    }
+  };
+
+  // fragment rows of this lane
+  int arow[2], brow[2];
+#pragma unroll
+  for (int mi = 0; mi < 2; ++mi) arow[mi] = 64 * wm + 32 * mi + cl;
+#pragma unroll
+  for (int m = 0; m < 2; ++m) brow[m] = GATEUP ? (m * (BN / 2) + 32 * wn + cl) : (64 * wn + 32 * m + cl);
+
+  f32x16_t acc[2][2];  // [matrix / column subtile][row subtile]
+#pragma unroll
+  for (int m = 0; m < 2; ++m)
+#pragma unroll
+    for (int mi = 0; mi < 2; ++mi) acc[m][mi] = f32x16_t{};
+
+  // ---- prologue: steps 0..D-1 in flight, step 0 into LDS
+#pragma unroll
+  for (int j = 0; j < D; ++j) load_stage(ring[j], min(j, nk - 1));
+  store_stage(ring[0], 0);
+  load_stage(ring[0], min(D, nk - 1));
+  __syncthreads();
+
+  // ---- main loop, unrolled by D so ring slots are static.  A last partial
+  // group (nk % D != 0) only skips the MFMAs.
+  for (int kk0 = 0; kk0 < nk; kk0 += D) {
+#pragma unroll
+    for (int j = 0; j < D; ++j) {
+      const int kk = kk0 + j;
+      if (kk < nk) {
+        const char* abuf = lds_a[kk & 1];
+        const char* bbuf = lds_b[kk & 1];
+        // fragments one substep ahead of the MFMAs that consume them
+        bf16x8_t af[2][2], bf[2][2];
+        auto read_frags = [&](int s, bf16x8_t* a2, bf16x8_t* b2) {
+#pragma unroll
+          for (int mi = 0; mi < 2; ++mi)
+            a2[mi] = *reinterpret_cast<const bf16x8_t*>(abuf + t_off(arow[mi], half * 4 + s));
+#pragma unroll
+          for (int m = 0; m < 2; ++m)
+            b2[m] = *reinterpret_cast<const bf16x8_t*>(bbuf + t_off(brow[m], half * 4 + s));
+        };
+        read_frags(0, af[0], bf[0]);
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+          if (s + 1 < 4) read_frags(s + 1, af[(s + 1) & 1], bf[(s + 1) & 1]);
+#pragma unroll
+          for (int m = 0; m < 2; ++m)
+#pragma unroll
+            for (int mi = 0; mi < 2; ++mi)
+              acc[m][mi] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[s & 1][mi], bf[s & 1][m],
+                                                                 acc[m][mi], 0, 0, 0);
+        }
+      }
+      const int jn = (j + 1) % D;
+      store_stage(ring[jn], (kk + 1) & 1);
+      load_stage(ring[jn], min(kk + 1 + D, nk - 1));
+      __syncthreads();
+    }
+  }
+
+  // ---- epilogue.  C layout of a 32x32 MFMA: lane holds column lane%32 and
+  // rows 8*(i/4) + 4*(lane/32) + i%4 for i in 0..15.
+#pragma unroll
+  for (int mi = 0; mi < 2; ++mi) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int row = 64 * wm + 32 * mi + 8 * (i >> 2) + 4 * half + (i & 3);
+      if (row < nrows) {
+        const size_t orow = (size_t)(row0 + row) * a.N;
+        if (GATEUP) {
+          const int col = nbase + 32 * wn + cl;
+          if (col < a.N) {
+            const float g = acc[0][mi][i];
+            const float u = acc[1][mi][i];
+            reinterpret_cast<uint16_t*>(a.out)[orow + col] = f32_to_bf16(g / (1.0f + expf(-g)) * u);
+          }
+        } else {
+#pragma unroll
+          for (int m = 0; m < 2; ++m) {
+            const int col = nbase + 64 * wn + 32 * m + cl;
+            if (col < a.N) reinterpret_cast<float*>(a.out)[orow + col] = acc[m][mi][i];
+          }
+        }
+      }
+    }
+  }
+}
+
+template <int WF, bool GATEUP, int D>
+__global__ __launch_bounds__(kThreads) void gg_direct_b_kernel(GGArgs a) {
+  __shared__ __align__(16) char lds_a[2][BM * BK * 2];
+  const int tid = threadIdx.x;
+  const int lane = lane_id();
+  const int wave = tid >> 6;
+  const int half = lane >> 5;
+  const int cl = lane & 31;
 
   // ---- tile
   const int num_tiles = *a.num_mtiles * a.ntiles;
@@ -131,73 +377,69 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GGArgs a) {
   const int nrows = em[2];
 
   // ---- B columns of this lane
-  const int half = lane >> 5;
-  const int cl = lane & 31;
   int col0, col1;
   if (GATEUP) {
-    col0 = ntile * 128 + wave * 32 + cl;
+    col0 = ntile * 256 + wave * 32 + cl;
     col1 = col0;
   } else {
-    col0 = ntile * 256 + wave * 64 + cl;
+    col0 = ntile * 512 + wave * 64 + cl;
     col1 = col0 + 32;
   }
   const int c0c = min(col0, a.N - 1);
   const int c1c = min(col1, a.N - 1);
-  const char* wbase0 = reinterpret_cast<const char*>(a.w0);
-  const char* wbase1 = reinterpret_cast<const char*>(GATEUP ? a.w1 : a.w0);
+  const char* wb0 = reinterpret_cast<const char*>(a.w0);
+  const char* wb1 = reinterpret_cast<const char*>(GATEUP ? a.w1 : a.w0);
   const char *p0, *p1;
   const uint8_t *q0 = nullptr, *q1 = nullptr;
   if constexpr (WF == kBF16) {
-    p0 = wbase0 + ((size_t)e * a.N + c0c) * a.K * 2 + half * 64;
-    p1 = wbase1 + ((size_t)e * a.N + c1c) * a.K * 2 + half * 64;
+    p0 = wb0 + ((size_t)e * a.N + c0c) * a.K * 2 + half * 64;
+    p1 = wb1 + ((size_t)e * a.N + c1c) * a.K * 2 + half * 64;
   } else {
-    p0 = wbase0 + ((size_t)e * a.N + c0c) * (a.K / 2) + half * 16;
-    p1 = wbase1 + ((size_t)e * a.N + c1c) * (a.K / 2) + half * 16;
+    p0 = wb0 + ((size_t)e * a.N + c0c) * (a.K / 2) + half * 16;
+    p1 = wb1 + ((size_t)e * a.N + c1c) * (a.K / 2) + half * 16;
     q0 = a.s0 + ((size_t)e * a.N + c0c) * (a.K / 32) + half;
     q1 = (GATEUP ? a.s1 : a.s0) + ((size_t)e * a.N + c1c) * (a.K / 32) + half;
   }
 
-  // ---- A rows staged by this thread: row tid/2, units (tid&1)*4 .. +3
-  const int arow = tid >> 1;
-  const int aunit = (tid & 1) * 4;
-  const int src_row = row0 + min(arow, nrows - 1);
+  // ---- A pieces of this thread: rows tid/8 + 64 i, unit tid%8
+  const int unit = tid & 7;
   const size_t a_rb = (size_t)a.K * 2;
-  const char* ap = reinterpret_cast<const char*>(a.a_src) +
-                   (GATEUP ? (size_t)(a.sorted_src[src_row] / a.k) : (size_t)src_row) * a_rb +
-                   aunit * 16;
+  const char* ap[kAPieces];
+#pragma unroll
+  for (int i = 0; i < kAPieces; ++i) {
+    const int r = (tid >> 3) + i * (kThreads / 8);
+    const int src = row0 + min(r, nrows - 1);
+    ap[i] = reinterpret_cast<const char*>(a.a_src) +
+            (GATEUP ? (size_t)(a.sorted_src[src] / a.k) : (size_t)src) * a_rb + unit * 16;
+  }
 
   const int nk = a.K / BK;
-  u32x4 areg[D][4];
-  BRegs<WF> breg[D];
+  u32x4 aring[D][kAPieces];
+  BRegs<WF> bring[D];
   auto load_a = [&](u32x4* r, int kk) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) r[j] = ld16(ap + (size_t)kk * (BK * 2) + 16 * j);
+    for (int i = 0; i < kAPieces; ++i) r[i] = ld16(ap[i] + (size_t)kk * (BK * 2));
   };
   auto store_a = [&](const u32x4* r, int buf) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
-      *reinterpret_cast<u32x4*>(&lds[buf][a_off(arow, aunit + j)]) = r[j];
+    for (int i = 0; i < kAPieces; ++i)
+      *reinterpret_cast<u32x4*>(&lds_a[buf][t_off((tid >> 3) + i * (kThreads / 8), unit)]) = r[i];
   };
 
-  f32x16_t acc0[4], acc1[4];
+  f32x16_t acc[2][4];  // [B operand][row subtile]
 #pragma unroll
-  for (int mi = 0; mi < 4; ++mi) {
-    acc0[mi] = f32x16_t{};
-    acc1[mi] = f32x16_t{};
-  }
+  for (int m = 0; m < 2; ++m)
+#pragma unroll
+    for (int mi = 0; mi < 4; ++mi) acc[m][mi] = f32x16_t{};
 
-  // ---- prologue: A and B of steps 0..D-1 in flight; A(0) into LDS.
-  // Every step issues the same loads (past the end they re-read the last
-  // step), so the load sequence is branch-free and the compiler's wait
-  // counts stay exact: waiting for the oldest ring entry never waits for the
-  // younger ones.
+  // ---- prologue: steps 0..D-1 in flight, step 0 into LDS
 #pragma unroll
   for (int j = 0; j < D; ++j) {
-    load_a(areg[j], min(j, nk - 1));
-    load_b<WF>(breg[j], p0, p1, q0, q1, min(j, nk - 1));
+    load_a(aring[j], min(j, nk - 1));
+    load_b<WF>(bring[j], p0, p1, q0, q1, min(j, nk - 1));
   }
-  store_a(areg[0], 0);
-  load_a(areg[0], min(D, nk - 1));
+  store_a(aring[0], 0);
+  load_a(aring[0], min(D, nk - 1));
   __syncthreads();
 
   // ---- main loop, unrolled by D so ring slots are static.  A last partial
@@ -207,25 +449,26 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GGArgs a) {
     for (int j = 0; j < D; ++j) {
       const int kk = kk0 + j;
       if (kk < nk) {
-        const char* abuf = lds[kk & 1];
+        const char* abuf = lds_a[kk & 1];
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
-          const bf16x8_t b0 = b_frag<WF>(breg[j], 0, s);
-          const bf16x8_t b1 = b_frag<WF>(breg[j], 1, s);
+          bf16x8_t af[4];
+#pragma unroll
+          for (int mi = 0; mi < 4; ++mi)
+            af[mi] = *reinterpret_cast<const bf16x8_t*>(abuf + t_off(32 * mi + cl, half * 4 + s));
+          const bf16x8_t b0 = b_frag<WF>(bring[j], 0, s);
+          const bf16x8_t b1 = b_frag<WF>(bring[j], 1, s);
 #pragma unroll
           for (int mi = 0; mi < 4; ++mi) {
-            const int row = mi * 32 + cl;
-            const bf16x8_t af =
-                *reinterpret_cast<const bf16x8_t*>(abuf + a_off(row, half * 4 + s));
-            acc0[mi] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, b0, acc0[mi], 0, 0, 0);
-            acc1[mi] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, b1, acc1[mi], 0, 0, 0);
+            acc[0][mi] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[mi], b0, acc[0][mi], 0, 0, 0);
+            acc[1][mi] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[mi], b1, acc[1][mi], 0, 0, 0);
           }
         }
       }
-      load_b<WF>(breg[j], p0, p1, q0, q1, min(kk + D, nk - 1));
+      load_b<WF>(bring[j], p0, p1, q0, q1, min(kk + D, nk - 1));
       const int jn = (j + 1) % D;
-      store_a(areg[jn], (kk + 1) & 1);
-      load_a(areg[jn], min(kk + 1 + D, nk - 1));
+      store_a(aring[jn], (kk + 1) & 1);
+      load_a(aring[jn], min(kk + 1 + D, nk - 1));
       __syncthreads();
     }
   }
@@ -236,38 +479,42 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GGArgs a) {
   for (int mi = 0; mi < 4; ++mi) {
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
-      const int row = mi * 32 + 8 * (i >> 2) + 4 * half + (i & 3);
+      const int row = 32 * mi + 8 * (i >> 2) + 4 * half + (i & 3);
       if (row < nrows) {
         const size_t orow = (size_t)(row0 + row) * a.N;
         if (GATEUP) {
           if (col0 < a.N) {
-            const float g = acc0[mi][i];
-            const float u = acc1[mi][i];
-            reinterpret_cast<uint16_t*>(a.out)[orow + col0] =
-                f32_to_bf16(g / (1.0f + expf(-g)) * u);
+            const float g = acc[0][mi][i];
+            const float u = acc[1][mi][i];
+            reinterpret_cast<uint16_t*>(a.out)[orow + col0] = f32_to_bf16(g / (1.0f + expf(-g)) * u);
           }
         } else {
-          if (col0 < a.N) reinterpret_cast<float*>(a.out)[orow + col0] = acc0[mi][i];
-          if (col1 < a.N) reinterpret_cast<float*>(a.out)[orow + col1] = acc1[mi][i];
+          if (col0 < a.N) reinterpret_cast<float*>(a.out)[orow + col0] = acc[0][mi][i];
+          if (col1 < a.N) reinterpret_cast<float*>(a.out)[orow + col1] = acc[1][mi][i];
         }
       }
     }
   }
 }
 
-#ifndef MOE_GG_DEPTH
-#define MOE_GG_DEPTH 4
-#endif
-constexpr int kDepth = MOE_GG_DEPTH;  // K-steps of loads in flight
+// K-steps of loads in flight (register budget of two waves per SIMD).
+constexpr int kDepthLds = 2;     // gg_lds_kernel, bf16 weights
+constexpr int kDepthDirect = 2;  // gg_direct_b_kernel, MX-FP4 weights
+
+// Output columns per tile: gate/up counts columns of each of W_gate, W_up.
+int tile_cols(const Dims& dm, bool gateup) {
+  const int base = dm.wfmt == kMXFP4 ? 256 : 128;
+  return gateup ? base : 2 * base;
+}
 
 template <bool GATEUP>
 hipError_t launch_gg(const Dims& dm, const GGArgs& a, hipStream_t s) {
   const size_t max_tiles = grouped_gemm_max_mtiles(dm) * (size_t)a.ntiles;
   const dim3 grid((unsigned)((max_tiles + kXcds - 1) / kXcds * kXcds)), block(kThreads);
   if (dm.wfmt == kMXFP4)
-    grouped_gemm_kernel<kMXFP4, GATEUP, kDepth><<<grid, block, 0, s>>>(a);
+    gg_direct_b_kernel<kMXFP4, GATEUP, kDepthDirect><<<grid, block, 0, s>>>(a);
   else
-    grouped_gemm_kernel<kBF16, GATEUP, kDepth><<<grid, block, 0, s>>>(a);
+    gg_lds_kernel<kBF16, GATEUP, kDepthLds><<<grid, block, 0, s>>>(a);
   return hipGetLastError();
 }
 
@@ -287,16 +534,18 @@ size_t grouped_gemm_max_mtiles(const Dims& dm) {
 hipError_t launch_gg_gate_up(const Dims& dm, const void* x, const Plan& p, const Weights& w,
                              void* h, hipStream_t s) {
   LaunchTimer tm("gg_gate_up", s);
+  const int tc = tile_cols(dm, true);
   GGArgs a{x, p.sorted_src, w.wg, w.wu, w.sg, w.su, p.mtiles, p.num_mtiles, h,
-           dm.d, dm.f, dm.k, (dm.f + 127) / 128};
+           dm.d, dm.f, dm.k, (dm.f + tc - 1) / tc};
   return launch_gg<true>(dm, a, s);
 }
 
 hipError_t launch_gg_down(const Dims& dm, const void* h, const Plan& p, const Weights& w,
                           float* y_sorted, hipStream_t s) {
   LaunchTimer tm("gg_down", s);
+  const int tc = tile_cols(dm, false);
   GGArgs a{h, nullptr, w.wd, nullptr, w.sd, nullptr, p.mtiles, p.num_mtiles, y_sorted,
-           dm.f, dm.d, dm.k, (dm.d + 255) / 256};
+           dm.f, dm.d, dm.k, (dm.d + tc - 1) / tc};
   return launch_gg<false>(dm, a, s);
 }
 
