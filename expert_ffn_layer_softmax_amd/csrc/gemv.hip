@@ -99,10 +99,28 @@ template <int WF, int MAXC, int RPW>
 struct RowRegs {
   u32x4 w[RPW][MAXC];
   float s[RPW][MAXC];  // MX-FP4 block scales
+  uint32_t sw[RPW];    // MX-FP4: this lane's word of 4 scale bytes, until unpack()
+  bool words;
 
-  // chunks c = c0 + i*64 + lane for c < cend
+  // Issue the loads of chunks c = c0 + i*64 + lane (c < cend).  MX-FP4 block
+  // scales (one byte per chunk) are fetched four to a lane with 32-bit loads
+  // issued before the weight loads; unpack() hands them to the lanes that use
+  // them with a lane shuffle (byte loads per chunk would double the load
+  // instructions of the stream).
   __device__ __forceinline__ void load(const char* row0, size_t rb, const uint8_t* s0, size_t sb,
                                        int nrows, int c0, int cend, int lane) {
+    words = (WF == kMXFP4) && ((sb & 3) == 0) && ((c0 & 3) == 0);
+    if constexpr (WF == kMXFP4) {
+      if (words) {
+        const int q = (c0 >> 2) + lane;  // scale word of chunks 4q .. 4q+3
+#pragma unroll
+        for (int r = 0; r < RPW; ++r) {
+          sw[r] = 0x7f7f7f7fu;
+          if (r < nrows && 4 * q < cend && lane < MAXC * 16)
+            sw[r] = *reinterpret_cast<const uint32_t*>(s0 + r * sb + 4 * (size_t)q);
+        }
+      }
+    }
 #pragma unroll
     for (int r = 0; r < RPW; ++r) {
 #pragma unroll
@@ -110,10 +128,33 @@ struct RowRegs {
         const int c = c0 + i * kWave + lane;
         if (r < nrows && c < cend) {
           w[r][i] = ld_stream16(row0 + r * rb + (size_t)c * 16);
-          if constexpr (WF == kMXFP4) s[r][i] = e8m0_to_f32(s0[r * sb + c]);
+          if constexpr (WF == kMXFP4) {
+            if (!words) s[r][i] = e8m0_to_f32(s0[r * sb + c]);
+          }
         }
       }
     }
+  }
+  // Scales into s[][] (MX-FP4 word path).  Every lane of the wave must call.
+  __device__ __forceinline__ void unpack(int lane) {
+    if constexpr (WF == kMXFP4) {
+      if (words) {
+#pragma unroll
+        for (int r = 0; r < RPW; ++r) {
+#pragma unroll
+          for (int i = 0; i < MAXC; ++i) {
+            const int cl = i * kWave + lane;  // chunk relative to c0
+            const uint32_t v = __shfl(sw[r], (cl >> 2) & (kWave - 1), kWave);
+            s[r][i] = e8m0_to_f32((v >> (8 * (cl & 3))) & 0xffu);
+          }
+        }
+      }
+    }
+  }
+  __device__ __forceinline__ void load_all(const char* row0, size_t rb, const uint8_t* s0, size_t sb,
+                                           int nrows, int c0, int cend, int lane) {
+    load(row0, rb, s0, sb, nrows, c0, cend, lane);
+    unpack(lane);
   }
 };
 
@@ -175,8 +216,8 @@ __global__ __launch_bounds__(256) void gemv_gate_up_kernel(GateUpArgs a) {
 
   RowRegs<WF, MAXC, RPW> G, U;
   if (!MULTISEG) {  // whole (part of the) rows, loaded once, before the token chain
-    G.load(gp, rb, sgp, sb, nrows, cbeg, cend, lane);
-    U.load(up, rb, sup, sb, nrows, cbeg, cend, lane);
+    G.load_all(gp, rb, sgp, sb, nrows, cbeg, cend, lane);
+    U.load_all(up, rb, sup, sb, nrows, cbeg, cend, lane);
   }
   const int r0 = a.slot_info[4 * slot + 1];
   const int ntok = a.slot_info[4 * slot + 2];
@@ -190,8 +231,8 @@ __global__ __launch_bounds__(256) void gemv_gate_up_kernel(GateUpArgs a) {
     for (int seg = 0; seg < nseg; ++seg) {
       const int c0 = cbeg + seg * SEG;
       if (MULTISEG) {
-        G.load(gp, rb, sgp, sb, nrows, c0, cend, lane);
-        U.load(up, rb, sup, sb, nrows, c0, cend, lane);
+        G.load_all(gp, rb, sgp, sb, nrows, c0, cend, lane);
+        U.load_all(up, rb, sup, sb, nrows, c0, cend, lane);
       }
       XChunk<WF> xc[MAXC];
 #pragma unroll
@@ -250,6 +291,75 @@ __global__ __launch_bounds__(256) void gemv_gate_up_kernel(GateUpArgs a) {
   }
 }
 
+// Single token (one row per slot): each wave walks R consecutive rows of its
+// expert, issuing the next row's loads before computing the current one, so a
+// wave keeps a row in flight for its whole life and the per-wave start-up
+// (slot lookup, token index, activation loads) is paid once per R rows.
+template <int WF, int MAXC, int R>
+__global__ __launch_bounds__(256) void gemv_gate_up_t1_rows_kernel(GateUpArgs a) {
+  constexpr int CE = WT<WF>::CE;
+  const int lane = lane_id();
+  const int wave = threadIdx.x >> 6;
+  const int RB = 4 * R;
+  const int tiles = (a.f + RB - 1) / RB;
+  const int slot = blockIdx.x / tiles;
+  if (slot >= *a.num_active) return;
+  const int n0 = (blockIdx.x - slot * tiles) * RB + wave * R;
+  if (n0 >= a.f) return;
+  const int e = a.slot_info[4 * slot + 0];
+  const int nrows = min(R, a.f - n0);
+  const int nchunks = a.d / CE;
+  const size_t rb = WT<WF>::row_bytes(a.d);
+  const size_t sb = (size_t)a.d / 32;
+  const size_t woff = (size_t)e * a.f + n0;
+  const char* gp = reinterpret_cast<const char*>(a.wg) + woff * rb;
+  const char* up = reinterpret_cast<const char*>(a.wu) + woff * rb;
+  const uint8_t* sgp = (WF == kMXFP4) ? a.sg + woff * sb : nullptr;
+  const uint8_t* sup = (WF == kMXFP4) ? a.su + woff * sb : nullptr;
+
+  RowRegs<WF, MAXC, 1> G[2], U[2];
+  G[0].load(gp, rb, sgp, sb, 1, 0, nchunks, lane);
+  U[0].load(up, rb, sup, sb, 1, 0, nchunks, lane);
+  const int r0 = a.slot_info[4 * slot + 1];
+  const char* xr = reinterpret_cast<const char*>(a.x) +
+                   (size_t)(a.sorted_src[r0] / a.k) * a.d * act_bytes<WF>();
+  XChunk<WF> xc[MAXC];
+#pragma unroll
+  for (int i = 0; i < MAXC; ++i) {
+    const int c = i * kWave + lane;
+    if (c < nchunks) xc[i] = load_x<WF>(xr, c);
+  }
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    if (r < nrows) {
+      const int cur = r & 1;
+      if (r + 1 < nrows) {
+        G[cur ^ 1].load(gp + (r + 1) * rb, rb, sgp + (r + 1) * sb, sb, 1, 0, nchunks, lane);
+        U[cur ^ 1].load(up + (r + 1) * rb, rb, sup + (r + 1) * sb, sb, 1, 0, nchunks, lane);
+      }
+      G[cur].unpack(lane);
+      U[cur].unpack(lane);
+      float ag = 0.f, au = 0.f;
+#pragma unroll
+      for (int i = 0; i < MAXC; ++i) {
+        const int c = i * kWave + lane;
+        if (c < nchunks) {
+          if constexpr (WF == kMXFP4) {
+            ag = fmaf(dot_chunk<WF>(G[cur].w[0][i], xc[i], 0.f), G[cur].s[0][i], ag);
+            au = fmaf(dot_chunk<WF>(U[cur].w[0][i], xc[i], 0.f), U[cur].s[0][i], au);
+          } else {
+            ag = dot_chunk<WF>(G[cur].w[0][i], xc[i], ag);
+            au = dot_chunk<WF>(U[cur].w[0][i], xc[i], au);
+          }
+        }
+      }
+      const float gs = wave_sum(ag);
+      const float us = wave_sum(au);
+      if (lane == 0) store_act<WF>(a.h, (size_t)r0 * a.f + n0 + r, silu(gs) * us);
+    }
+  }
+}
+
 struct DownArgs {
   const void* h;
   const void* wd;
@@ -283,7 +393,7 @@ __global__ __launch_bounds__(256) void gemv_down_kernel(DownArgs a) {
   const uint8_t* sp = (WF == kMXFP4) ? a.sd + woff * sb : nullptr;
 
   RowRegs<WF, MAXC, RPW> W;
-  if (!MULTISEG) W.load(wp, rb, sp, sb, nrows, 0, nchunks, lane);
+  if (!MULTISEG) W.load_all(wp, rb, sp, sb, nrows, 0, nchunks, lane);
   const int r0 = a.slot_info[4 * slot + 1];
   const int ntok = a.slot_info[4 * slot + 2];
   const size_t hrb = (size_t)a.f * act_bytes<WF>();
@@ -295,7 +405,7 @@ __global__ __launch_bounds__(256) void gemv_down_kernel(DownArgs a) {
     for (int r = 0; r < RPW; ++r) acc[r] = 0.f;
     for (int seg = 0; seg < nseg; ++seg) {
       const int c0 = seg * SEG;
-      if (MULTISEG) W.load(wp, rb, sp, sb, nrows, c0, nchunks, lane);
+      if (MULTISEG) W.load_all(wp, rb, sp, sb, nrows, c0, nchunks, lane);
       XChunk<WF> hc[MAXC];
 #pragma unroll
       for (int i = 0; i < MAXC; ++i) {
@@ -341,8 +451,8 @@ struct DownCombineArgs {
 // k waves over the same RPW output rows, wave j on slot j's expert; the k
 // results meet in LDS and are summed in slot order (the combine kernel's
 // arithmetic), so no cross-block synchronisation is needed.
-template <int WF, int MAXC, int RPW>
-__global__ __launch_bounds__(1024) void gemv_down_combine_t1_kernel(DownCombineArgs a) {
+template <int WF, int MAXC, int RPW, int NTH>
+__global__ __launch_bounds__(NTH) void gemv_down_combine_t1_kernel(DownCombineArgs a) {
   __shared__ float ys[16][RPW];
   constexpr int CE = WT<WF>::CE;
   const int lane = lane_id();
@@ -355,8 +465,8 @@ __global__ __launch_bounds__(1024) void gemv_down_combine_t1_kernel(DownCombineA
   const size_t sb = (size_t)a.f / 32;
   const size_t woff = (size_t)e * a.d + n0;
   RowRegs<WF, MAXC, RPW> W;
-  W.load(reinterpret_cast<const char*>(a.wd) + woff * rb, rb,
-         (WF == kMXFP4) ? a.sd + woff * sb : nullptr, sb, nrows, 0, nchunks, lane);
+  W.load_all(reinterpret_cast<const char*>(a.wd) + woff * rb, rb,
+             (WF == kMXFP4) ? a.sd + woff * sb : nullptr, sb, nrows, 0, nchunks, lane);
   const char* hr =
       reinterpret_cast<const char*>(a.h) + (size_t)a.dest_row[j] * a.f * act_bytes<WF>();
   XChunk<WF> hc[MAXC];
@@ -409,8 +519,12 @@ int pick_maxc(int nchunks, int wf) {
   return cap;
 }
 
+// Rows walked per wave by the single-token MX-FP4 gate/up kernel.
+constexpr int kT1Rows = 8;
+
 // Rows per wave so that a wave keeps about 12 chunks per matrix in flight.
-constexpr int rpw_for(int maxc) { return maxc >= 12 ? 1 : (maxc >= 6 ? 2 : 4); }
+constexpr int rpw_for(int maxc) { return maxc >= 12 ? 1 : (maxc >= 6 ? 2 : (maxc >= 3 ? 1 : 4)); }
+constexpr int rpw_t1_small(int maxc) { return maxc <= 2 ? 8 : rpw_for(maxc); }
 
 #define MOE_MAXC_SWITCH(WFV, MAXC, CALL)                                              \
   switch (MAXC) {                                                                     \
@@ -472,6 +586,17 @@ hipError_t launch_gemv_gate_up(const Dims& dm, const void* x, const Plan& p, con
     }
     return hipGetLastError();
   }
+  if (dm.T == 1 && dm.wfmt == kMXFP4 && !multi) {
+    // short rows: each wave walks kT1Rows rows with the next row in flight
+    const dim3 grid((unsigned)(max_active * ((dm.f + 4 * kT1Rows - 1) / (4 * kT1Rows)))), block(256);
+    switch (maxc) {
+      case 1: gemv_gate_up_t1_rows_kernel<kMXFP4, 1, kT1Rows><<<grid, block, 0, s>>>(a); break;
+      case 2: gemv_gate_up_t1_rows_kernel<kMXFP4, 2, kT1Rows><<<grid, block, 0, s>>>(a); break;
+      case 3: gemv_gate_up_t1_rows_kernel<kMXFP4, 3, kT1Rows><<<grid, block, 0, s>>>(a); break;
+      default: gemv_gate_up_t1_rows_kernel<kMXFP4, 4, kT1Rows><<<grid, block, 0, s>>>(a); break;
+    }
+    return hipGetLastError();
+  }
   const int rpw = rpw_for(maxc);
   const dim3 grid((unsigned)(max_active * ((dm.f + 4 * rpw - 1) / (4 * rpw)))), block(256);
   MOE_WF_SWITCH(dm.wfmt, MOE_MAXC_SWITCH(WF, maxc, MOE_SEG_SWITCH(multi, (
@@ -509,10 +634,18 @@ hipError_t launch_gemv_down_combine_t1(const Dims& dm, const void* h, const Plan
   LaunchTimer tm("gemv_down_combine_t1", s);
   DownCombineArgs a{h, w.wd, w.sd, topk_idx, topk_w, p.dest_row, out, dm.d, dm.f, dm.k};
   const int maxc = pick_maxc(dm.f / chunk_elems(dm.wfmt), dm.wfmt);
-  const int rpw = rpw_for(maxc);
-  const dim3 grid((unsigned)((dm.d + rpw - 1) / rpw)), block(64 * dm.k);
-  MOE_WF_SWITCH(dm.wfmt, MOE_MAXC12_SWITCH(WF, maxc, (
-      gemv_down_combine_t1_kernel<WF, MC, rpw_for(MC)><<<grid, block, 0, s>>>(a))));
+  const dim3 block(64 * dm.k);
+  if (dm.k <= 8) {  // 512-thread blocks: up to 256 registers, twice the short rows per wave
+    const int rpw = rpw_t1_small(maxc);
+    const dim3 grid((unsigned)((dm.d + rpw - 1) / rpw));
+    MOE_WF_SWITCH(dm.wfmt, MOE_MAXC12_SWITCH(WF, maxc, (
+        gemv_down_combine_t1_kernel<WF, MC, rpw_t1_small(MC), 512><<<grid, block, 0, s>>>(a))));
+  } else {
+    const int rpw = rpw_for(maxc);
+    const dim3 grid((unsigned)((dm.d + rpw - 1) / rpw));
+    MOE_WF_SWITCH(dm.wfmt, MOE_MAXC12_SWITCH(WF, maxc, (
+        gemv_down_combine_t1_kernel<WF, MC, rpw_for(MC), 1024><<<grid, block, 0, s>>>(a))));
+  }
   return hipGetLastError();
 }
 
