@@ -11,42 +11,35 @@
 // convert (the block scale is applied by the instruction), then fed to the
 // same MFMA.
 //
-// Two tile schemes, both 128 rows (one m-tile of an expert) x 8 waves (two
-// per SIMD), K advancing 64 per step:
+// Every kernel works on tiles of 128 rows (one m-tile of an expert) with 8
+// waves (two per SIMD), K advancing 64 per step, and skips the 32-row
+// sub-tiles of an m-tile that hold no rows of the expert (skewed routing
+// leaves most m-tiles partly filled).
 //
-// bf16 weights (gg_lds_kernel): 256 B-columns per tile (gate/up: 128
+// gg_dma_kernel (bf16 weights): 256 weight rows per tile (gate/up: 128
 // columns of W_gate and the same 128 of W_up, so the SwiGLU epilogue is
-// wave-local; down: 256 columns of W_down), K advancing 64 per step.  Both
-// operands go through double-buffered, XOR-swizzled LDS tiles.  512 threads
-// (8 waves, two per SIMD) fetch each step with 16-byte loads, 8 consecutive
-// threads per 128-byte row segment, into a D-deep register ring: loads for a
-// step are issued D steps before its MFMAs.  Every step issues the same loads
-// (past the end they re-read the last step), so waiting for the oldest ring
-// entry never waits for younger ones.  MX-FP4 weights are converted to bf16
-// (block scale applied by the instruction) on their way into LDS.  Waves form
-// a 2 (rows) x 4 (columns) grid, each owning 64 rows x (2 x 32) columns.
+// wave-local; down: 256 columns of W_down).  Both operands are fetched with
+// global_load_lds straight into three XOR-swizzled LDS stages, two steps
+// ahead of the MFMAs; waves form a 2 (rows) x 4 (columns) grid of 64 x 64.
 //
-// MX-FP4 weights (gg_direct_b_kernel): h wave owns all
-// 128 rows and two 32-column B operands: gate/up: the same 32 columns of
-// W_gate and W_up (the SwiGLU epilogue stays wave-local), so a tile spans
-// 256 columns of each; down: 64 consecutive columns of W_down, 512 per tile.
-// K advances 64 per step.  A weight column belongs to exactly one wave, so
-// the weights stream straight from memory into registers, D steps ahead; the
-// activation rows, shared by all 8 waves, go through a D-deep register ring
-// into a double-buffered, XOR-swizzled LDS tile (8 threads per 128-byte row
-// segment, full cache lines).  Every step issues the same loads (past the end
-// they re-read the last step), so waiting for the oldest ring entry never
-// waits for younger ones.  Per substep a wave reads 4 A fragments from LDS for
-// 8 MFMAs; B never touches LDS.
+// gg_mx_group_kernel (MX-FP4 weights, K % 256 == 0): the same tile and wave
+// grid; activation rows as above, weight codes fetched in whole cache lines
+// (four K-steps of a row per line) into group buffers two groups ahead, and
+// converted to bf16 in registers by the gfx950 scaled convert (block scale
+// applied by the instruction) just before their MFMAs.
 //
-// The weights are 4x smaller there, so streaming them per wave into
-// registers costs little and keeps LDS traffic to the shared activations.
+// gg_direct_b_kernel (MX-FP4 weights, other K): each wave owns all 128 rows
+// and two 32-column weight operands that stream from memory into a register
+// ring; the activation rows go through a register ring into double-buffered
+// LDS.
 //
 // Tile order: logical tiles run expert by expert, n-tile by n-tile, m-tile
 // by m-tile, and each XCD (blockIdx % 8 under round-robin dispatch) takes a
 // contiguous range.  The m-tiles of one (expert, n-tile) panel therefore run
 // together on one XCD and share the weight panel through its L2; the n-tiles
 // of one expert follow each other there and reuse its activation rows.
+#include <type_traits>
+
 #include "device.h"
 #include "internal.h"
 
@@ -132,223 +125,7 @@ __device__ __forceinline__ bf16x8_t b_frag(const BRegs<WF>& b, int m, int s) {
   }
 }
 
-constexpr int BN = 256;                 // gg_lds_kernel: B-tile rows (weight columns) per tile
-constexpr int kBPieces = BN * 8 / kThreads;   // bf16 B pieces per thread per step
-
-// One step's global data held by a thread between its load and its LDS store.
-template <int WF>
-struct Stage;
-template <>
-struct Stage<kBF16> {
-  u32x4 a[kAPieces];
-  u32x4 b[kBPieces];
-};
-template <>
-struct Stage<kMXFP4> {  // B: 16 B of codes (one 32-element block) + its scale
-  u32x4 a[kAPieces];
-  u32x4 b;
-  uint32_t s;
-};
-
-template <int WF, bool GATEUP, int D>
-__global__ __launch_bounds__(kThreads) void gg_lds_kernel(GGArgs a) {
-  __shared__ __align__(16) char lds_a[2][BM * BK * 2];
-  __shared__ __align__(16) char lds_b[2][BN * BK * 2];
-  const int tid = threadIdx.x;
-  const int lane = lane_id();
-  const int wave = tid >> 6;
-  const int wm = wave >> 2;  // 0..1: rows 64*wm ..
-  const int wn = wave & 3;   // 0..3: columns
-  const int half = lane >> 5;
-  const int cl = lane & 31;
-
-  // ---- tile
-  const int num_tiles = *a.num_mtiles * a.ntiles;
-  const int per_xcd = (num_tiles + kXcds - 1) / kXcds;
-  const int slot = blockIdx.x / kXcds;
-  if (slot >= per_xcd) return;
-  const int L = (blockIdx.x % kXcds) * per_xcd + slot;
-  if (L >= num_tiles) return;
-  const int* eq = a.mtiles + kMtileInts * (L / a.ntiles);
-  const int e = eq[0];
-  const int first_mt = eq[3];
-  const int nmt = eq[4];
-  const int local = L - first_mt * a.ntiles;
-  const int ntile = local / nmt;
-  const int* em = a.mtiles + kMtileInts * (first_mt + (local - ntile * nmt));
-  const int row0 = em[1];
-  const int nrows = em[2];
-  const int nbase = ntile * (GATEUP ? BN / 2 : BN);
-
-  // ---- global sources of this thread's pieces
-  const int unit = tid & 7;
-  const size_t a_rb = (size_t)a.K * 2;
-  const char* ap[kAPieces];
-#pragma unroll
-  for (int i = 0; i < kAPieces; ++i) {
-    const int r = (tid >> 3) + i * (kThreads / 8);
-    const int src = row0 + min(r, nrows - 1);
-    ap[i] = reinterpret_cast<const char*>(a.a_src) +
-            (GATEUP ? (size_t)(a.sorted_src[src] / a.k) : (size_t)src) * a_rb + unit * 16;
-  }
-  // B-tile row r -> weight matrix and column
-  auto bcol = [&](int r, const void*& w, const uint8_t*& sc) {
-    int col;
-    if (GATEUP) {
-      const bool up = r >= BN / 2;
-      w = up ? a.w1 : a.w0;
-      sc = up ? a.s1 : a.s0;
-      col = nbase + (up ? r - BN / 2 : r);
-    } else {
-      w = a.w0;
-      sc = a.s0;
-      col = nbase + r;
-    }
-    return min(col, a.N - 1);
-  };
-  constexpr int NBP = (WF == kBF16) ? kBPieces : 1;
-  const char* bp[NBP];
-  const uint8_t* sp = nullptr;
-  int b_unit0 = 0;  // MX-FP4: first LDS unit this thread's block fills
-  if constexpr (WF == kBF16) {
-#pragma unroll
-    for (int i = 0; i < kBPieces; ++i) {
-      const void* w;
-      const uint8_t* sc;
-      const int col = bcol((tid >> 3) + i * (kThreads / 8), w, sc);
-      bp[i] = reinterpret_cast<const char*>(w) + ((size_t)e * a.N + col) * a_rb + unit * 16;
-    }
-  } else {
-    const void* w;
-    const uint8_t* sc;
-    const int col = bcol(tid >> 1, w, sc);
-    const int hb = tid & 1;  // which 32-element block of the step
-    bp[0] = reinterpret_cast<const char*>(w) + ((size_t)e * a.N + col) * (a.K / 2) + hb * 16;
-    sp = sc + ((size_t)e * a.N + col) * (a.K / 32) + hb;
-    b_unit0 = hb * 4;
-  }
-
-  const int nk = a.K / BK;
-  Stage<WF> ring[D];
-  auto load_stage = [&](Stage<WF>& st, int kk) {
-#pragma unroll
-    for (int i = 0; i < kAPieces; ++i) st.a[i] = ld16(ap[i] + (size_t)kk * (BK * 2));
-    if constexpr (WF == kBF16) {
-#pragma unroll
-      for (int i = 0; i < kBPieces; ++i) st.b[i] = ld16(bp[i] + (size_t)kk * (BK * 2));
-    } else {
-      st.b = ld16(bp[0] + (size_t)kk * (BK / 2));
-      st.s = sp[2 * kk];
-    }
-  };
-  auto store_stage = [&](const Stage<WF>& st, int buf) {
-#pragma unroll
-    for (int i = 0; i < kAPieces; ++i)
-      *reinterpret_cast<u32x4*>(&lds_a[buf][t_off((tid >> 3) + i * (kThreads / 8), unit)]) = st.a[i];
-    if constexpr (WF == kBF16) {
-#pragma unroll
-      for (int i = 0; i < kBPieces; ++i)
-        *reinterpret_cast<u32x4*>(&lds_b[buf][t_off((tid >> 3) + i * (kThreads / 8), unit)]) = st.b[i];
-    } else {
-      const float scale = e8m0_to_f32(st.s);
-      const uint32_t cw[4] = {st.b.x, st.b.y, st.b.z, st.b.w};
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        u32x4 r;
-        r.x = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(cw[j], scale, 0));
-        r.y = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(cw[j], scale, 1));
-        r.z = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(cw[j], scale, 2));
-        r.w = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(cw[j], scale, 3));
-        *reinterpret_cast<u32x4*>(&lds_b[buf][t_off(tid >> 1, b_unit0 + j)]) = r;
-      }
-    }
-  };
-
-  // fragment rows of this lane
-  int arow[2], brow[2];
-#pragma unroll
-  for (int mi = 0; mi < 2; ++mi) arow[mi] = 64 * wm + 32 * mi + cl;
-#pragma unroll
-  for (int m = 0; m < 2; ++m) brow[m] = GATEUP ? (m * (BN / 2) + 32 * wn + cl) : (64 * wn + 32 * m + cl);
-
-  f32x16_t acc[2][2];  // [matrix / column subtile][row subtile]
-#pragma unroll
-  for (int m = 0; m < 2; ++m)
-#pragma unroll
-    for (int mi = 0; mi < 2; ++mi) acc[m][mi] = f32x16_t{};
-
-  // ---- prologue: steps 0..D-1 in flight, step 0 into LDS
-#pragma unroll
-  for (int j = 0; j < D; ++j) load_stage(ring[j], min(j, nk - 1));
-  store_stage(ring[0], 0);
-  load_stage(ring[0], min(D, nk - 1));
-  __syncthreads();
-
-  // ---- main loop, unrolled by D so ring slots are static.  A last partial
-  // group (nk % D != 0) only skips the MFMAs.
-  for (int kk0 = 0; kk0 < nk; kk0 += D) {
-#pragma unroll
-    for (int j = 0; j < D; ++j) {
-      const int kk = kk0 + j;
-      if (kk < nk) {
-        const char* abuf = lds_a[kk & 1];
-        const char* bbuf = lds_b[kk & 1];
-        // fragments one substep ahead of the MFMAs that consume them
-        bf16x8_t af[2][2], bf[2][2];
-        auto read_frags = [&](int s, bf16x8_t* a2, bf16x8_t* b2) {
-#pragma unroll
-          for (int mi = 0; mi < 2; ++mi)
-            a2[mi] = *reinterpret_cast<const bf16x8_t*>(abuf + t_off(arow[mi], half * 4 + s));
-#pragma unroll
-          for (int m = 0; m < 2; ++m)
-            b2[m] = *reinterpret_cast<const bf16x8_t*>(bbuf + t_off(brow[m], half * 4 + s));
-        };
-        read_frags(0, af[0], bf[0]);
-#pragma unroll
-        for (int s = 0; s < 4; ++s) {
-          if (s + 1 < 4) read_frags(s + 1, af[(s + 1) & 1], bf[(s + 1) & 1]);
-#pragma unroll
-          for (int m = 0; m < 2; ++m)
-#pragma unroll
-            for (int mi = 0; mi < 2; ++mi)
-              acc[m][mi] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[s & 1][mi], bf[s & 1][m],
-                                                                 acc[m][mi], 0, 0, 0);
-        }
-      }
-      const int jn = (j + 1) % D;
-      store_stage(ring[jn], (kk + 1) & 1);
-      load_stage(ring[jn], min(kk + 1 + D, nk - 1));
-      __syncthreads();
-    }
-  }
-
-  // ---- epilogue.  C layout of a 32x32 MFMA: lane holds column lane%32 and
-  // rows 8*(i/4) + 4*(lane/32) + i%4 for i in 0..15.
-#pragma unroll
-  for (int mi = 0; mi < 2; ++mi) {
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int row = 64 * wm + 32 * mi + 8 * (i >> 2) + 4 * half + (i & 3);
-      if (row < nrows) {
-        const size_t orow = (size_t)(row0 + row) * a.N;
-        if (GATEUP) {
-          const int col = nbase + 32 * wn + cl;
-          if (col < a.N) {
-            const float g = acc[0][mi][i];
-            const float u = acc[1][mi][i];
-            reinterpret_cast<uint16_t*>(a.out)[orow + col] = f32_to_bf16(g / (1.0f + expf(-g)) * u);
-          }
-        } else {
-#pragma unroll
-          for (int m = 0; m < 2; ++m) {
-            const int col = nbase + 64 * wn + 32 * m + cl;
-            if (col < a.N) reinterpret_cast<float*>(a.out)[orow + col] = acc[m][mi][i];
-          }
-        }
-      }
-    }
-  }
-}
+constexpr int BN = 256;  // weight rows per tile of gg_dma_kernel and gg_mx_group_kernel
 
 template <int WF, bool GATEUP, int D>
 __global__ __launch_bounds__(kThreads) void gg_direct_b_kernel(GGArgs a) {
@@ -497,13 +274,504 @@ __global__ __launch_bounds__(kThreads) void gg_direct_b_kernel(GGArgs a) {
   }
 }
 
+// ---- bf16 weights, streamed straight into LDS.
+//
+// Tile of 128 rows x 256 weight rows, 8 waves in a 2 x 4 grid of 64 x 64.
+// The global loads write LDS directly
+// (global_load_lds_dwordx4: lane i of a wave lands 16 bytes at M0 + 16 i), so
+// no register ring and no LDS store instructions are needed, and three
+// 48 KB stages fit in LDS: loads run two K-steps ahead of the MFMAs.  Each
+// DMA instruction fills 8 LDS rows of 128 B; lane i takes row i/8 and stores
+// into slot i%8 the global 16-byte unit (i%8) ^ f(row), so the stage ends up in
+// the XOR-swizzled layout of t_off.
+//
+// A wave waits only for its own DMAs of the stage it is about to read (the
+// loads of one wave complete in issue order), then the block barrier makes
+// every wave's part visible.  The compiler's workgroup fence would wait for
+// all outstanding loads, including the ones two steps ahead, so the barrier is
+// the bare instruction, fenced against compiler reordering only.
+//
+// Row sub-tiles of 32 past the m-tile's rows are skipped: a wave runs its
+// MFMAs only on the sub-tiles that hold rows of the expert.
+constexpr int kStages = 3;
+constexpr int kStageA = BM * BK * 2;          // 16 KB
+constexpr int kStageB = BN * BK * 2;          // 32 KB
+constexpr int kStageBytes = kStageA + kStageB;
+constexpr int kWaves = kThreads / kWave;      // 8
+constexpr int kDmaA = kStageA / (kWave * 16) / kWaves;  // DMA instructions per wave per stage
+constexpr int kDmaB = kStageB / (kWave * 16) / kWaves;
+constexpr int kDmaPerStage = kDmaA + kDmaB;   // 6
+
+typedef __attribute__((address_space(3))) void lds_void_t;
+
+// AUX: cache policy of the load (0: default, 2: non-temporal).
+template <int AUX>
+__device__ __forceinline__ void dma16(const char* g, char* lds) {
+  __builtin_amdgcn_global_load_lds(g, (lds_void_t*)lds, 16, 0, AUX);
+}
+constexpr int kAuxA = 0;  // activation rows: reused by every n-tile of the m-tile
+constexpr int kAuxB = 0;  // weight panel
+
+// Wait until at most N of this wave's vector-memory operations are
+// outstanding and its LDS reads have returned, then join the block.
+template <int N>
+__device__ __forceinline__ void wait_and_barrier() {
+  static_assert(N >= 0 && N < 64, "vmcnt field");
+  asm volatile("" ::: "memory");
+  // vmcnt(N) (bits 3:0 and 15:14), expcnt(7), lgkmcnt(0)
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (0 << 8));
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// MFMAs of one K-step on LDS stage `st` for the VM valid row sub-tiles
+// (of two) of this wave; fragments are read one substep ahead.
+template <int VM>
+__device__ __forceinline__ void dma_step(const char* st, const int* aoff, const int* boff,
+                                         f32x16_t (&acc)[2][2]) {
+  if constexpr (VM > 0) {
+    const char* abuf = st;
+    const char* bbuf = st + kStageA;
+    bf16x8_t af[2][2], bf[2][2];
+    auto rd = [&](int s, bf16x8_t* a2, bf16x8_t* b2) {
+#pragma unroll
+      for (int mi = 0; mi < VM; ++mi)
+        a2[mi] = *reinterpret_cast<const bf16x8_t*>(abuf + aoff[4 * mi + s]);
+#pragma unroll
+      for (int m = 0; m < 2; ++m) b2[m] = *reinterpret_cast<const bf16x8_t*>(bbuf + boff[4 * m + s]);
+    };
+    rd(0, af[0], bf[0]);
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      if (s + 1 < 4) rd(s + 1, af[(s + 1) & 1], bf[(s + 1) & 1]);
+#pragma unroll
+      for (int m = 0; m < 2; ++m)
+#pragma unroll
+        for (int mi = 0; mi < VM; ++mi)
+          acc[m][mi] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[s & 1][mi], bf[s & 1][m],
+                                                             acc[m][mi], 0, 0, 0);
+    }
+  }
+}
+
+template <bool GATEUP>
+__global__ __launch_bounds__(kThreads) void gg_dma_kernel(GGArgs a) {
+  __shared__ __align__(1024) char lds[kStages * kStageBytes];
+  const int tid = threadIdx.x;
+  const int lane = lane_id();
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave >> 2;  // 0..1: rows 64*wm ..
+  const int wn = wave & 3;   // 0..3: columns
+  const int half = lane >> 5;
+  const int cl = lane & 31;
+
+  // ---- tile (same logical order and XCD mapping as the other kernels)
+  const int num_tiles = *a.num_mtiles * a.ntiles;
+  const int per_xcd = (num_tiles + kXcds - 1) / kXcds;
+  const int slot = blockIdx.x / kXcds;
+  if (slot >= per_xcd) return;
+  const int L = (blockIdx.x % kXcds) * per_xcd + slot;
+  if (L >= num_tiles) return;
+  const int* eq = a.mtiles + kMtileInts * (L / a.ntiles);
+  const int e = eq[0];
+  const int first_mt = eq[3];
+  const int nmt = eq[4];
+  const int local = L - first_mt * a.ntiles;
+  const int ntile = local / nmt;
+  const int* em = a.mtiles + kMtileInts * (first_mt + (local - ntile * nmt));
+  const int row0 = em[1];
+  const int nrows = em[2];
+  const int nbase = ntile * (GATEUP ? BN / 2 : BN);
+
+  // ---- DMA sources: instruction j of this wave fills LDS rows 8j.. of its
+  // share; lane -> (row, slot), global unit slot ^ f(row).
+  const size_t rb = (size_t)a.K * 2;
+  const int slot16 = lane & 7;
+  const char* asrc[kDmaA];
+#pragma unroll
+  for (int j = 0; j < kDmaA; ++j) {
+    const int r = (kDmaA * 8) * wave + 8 * j + (lane >> 3);
+    const int f = (r & 7) ^ ((r >> 3) & 1);
+    const int src = row0 + min(r, nrows - 1);
+    asrc[j] = reinterpret_cast<const char*>(a.a_src) +
+              (GATEUP ? (size_t)(a.sorted_src[src] / a.k) : (size_t)src) * rb + ((slot16 ^ f) << 4);
+  }
+  const char* bsrc[kDmaB];
+#pragma unroll
+  for (int j = 0; j < kDmaB; ++j) {
+    const int r = (kDmaB * 8) * wave + 8 * j + (lane >> 3);
+    const int f = (r & 7) ^ ((r >> 3) & 1);
+    const void* w = a.w0;
+    int col;
+    if (GATEUP) {
+      const bool up = r >= BN / 2;
+      w = up ? a.w1 : a.w0;
+      col = nbase + (up ? r - BN / 2 : r);
+    } else {
+      col = nbase + r;
+    }
+    col = min(col, a.N - 1);
+    bsrc[j] = reinterpret_cast<const char*>(w) + ((size_t)e * a.N + col) * rb + ((slot16 ^ f) << 4);
+  }
+  char* const adst = lds + (kDmaA * 8) * wave * (BK * 2);
+  char* const bdst = lds + kStageA + (kDmaB * 8) * wave * (BK * 2);
+  auto issue = [&](int kk, int stage) {
+    const size_t go = (size_t)kk * (BK * 2);
+    const int so = stage * kStageBytes;
+#pragma unroll
+    for (int j = 0; j < kDmaA; ++j) dma16<kAuxA>(asrc[j] + go, adst + so + j * 8 * (BK * 2));
+#pragma unroll
+    for (int j = 0; j < kDmaB; ++j) dma16<kAuxB>(bsrc[j] + go, bdst + so + j * 8 * (BK * 2));
+  };
+
+  // ---- fragment offsets inside a stage: [sub-tile or matrix][substep]
+  int aoff[8], boff[8];
+#pragma unroll
+  for (int mi = 0; mi < 2; ++mi)
+#pragma unroll
+    for (int s = 0; s < 4; ++s) aoff[4 * mi + s] = t_off(64 * wm + 32 * mi + cl, half * 4 + s);
+#pragma unroll
+  for (int m = 0; m < 2; ++m) {
+    const int br = GATEUP ? (m * (BN / 2) + 32 * wn + cl) : (64 * wn + 32 * m + cl);
+#pragma unroll
+    for (int s = 0; s < 4; ++s) boff[4 * m + s] = t_off(br, half * 4 + s);
+  }
+
+  f32x16_t acc[2][2];
+#pragma unroll
+  for (int m = 0; m < 2; ++m)
+#pragma unroll
+    for (int mi = 0; mi < 2; ++mi) acc[m][mi] = f32x16_t{};
+
+  // valid 32-row sub-tiles of this wave's 64 rows (block-uniform per wave)
+  const int vm = min(max((nrows + 31) / 32 - 2 * wm, 0), 2);
+  const int nk = a.K / BK;
+
+  issue(0, 0);
+  if (nk > 1) issue(1, 1);
+  // The loop is instantiated per sub-tile count so the accumulators keep
+  // fixed registers.
+  auto main_loop = [&](auto vm_c) {
+    constexpr int VM = decltype(vm_c)::value;
+    int stage = 0;
+    for (int kk = 0; kk < nk; ++kk) {
+      if (kk + 1 < nk)
+        wait_and_barrier<kDmaPerStage>();
+      else
+        wait_and_barrier<0>();
+      if (kk + 2 < nk) issue(kk + 2, stage == 0 ? 2 : stage - 1);
+      dma_step<VM>(lds + stage * kStageBytes, aoff, boff, acc);
+      stage = stage == kStages - 1 ? 0 : stage + 1;
+    }
+  };
+  if (vm == 2)
+    main_loop(std::integral_constant<int, 2>{});
+  else if (vm == 1)
+    main_loop(std::integral_constant<int, 1>{});
+  else
+    main_loop(std::integral_constant<int, 0>{});
+
+  // ---- epilogue (C layout of a 32x32 MFMA: lane holds column lane%32 and
+  // rows 8*(i/4) + 4*(lane/32) + i%4 for i in 0..15)
+#pragma unroll
+  for (int mi = 0; mi < 2; ++mi) {
+    if (mi < vm) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int row = 64 * wm + 32 * mi + 8 * (i >> 2) + 4 * half + (i & 3);
+        if (row < nrows) {
+          const size_t orow = (size_t)(row0 + row) * a.N;
+          if (GATEUP) {
+            const int col = nbase + 32 * wn + cl;
+            if (col < a.N) {
+              const float g = acc[0][mi][i];
+              const float u = acc[1][mi][i];
+              reinterpret_cast<uint16_t*>(a.out)[orow + col] = f32_to_bf16(g / (1.0f + expf(-g)) * u);
+            }
+          } else {
+#pragma unroll
+            for (int m = 0; m < 2; ++m) {
+              const int col = nbase + 64 * wn + 32 * m + cl;
+              if (col < a.N) reinterpret_cast<float*>(a.out)[orow + col] = acc[m][mi][i];
+            }
+          }
+        }
+      }
+    }
+  }
+}
+
+// ---- MX-FP4 weights, cache-line groups of codes in LDS.
+//
+// A weight row's codes for one K-step are 32 bytes, a quarter of a 128-byte
+// line; fetched step by step, a line is needed again three steps later, by
+// which time the streaming traffic of the XCD has pushed it out of L2 and it
+// is read from HBM again (counters showed about 2.5x the code bytes).  Here
+// the codes travel in groups of four K-steps: each DMA instruction fills 8
+// weight rows x 128 bytes (whole lines, 8 lanes per line), a group of 256
+// weight rows x 4 steps is 32 KB, and three group buffers let a group be
+// issued two groups ahead of its use, one instruction per wave per step.  The
+// block scales of a group (8 bytes per weight row) arrive with one 4-byte
+// DMA per lane at the group's first step.  The activation tile and the
+// 2 x 4 wave grid are those of gg_dma_kernel (64 rows x two 32-column
+// operands per wave, wave-local SwiGLU); codes are converted to bf16 (scale
+// applied by the instruction) just before their MFMAs.
+//
+// Per step the loads are issued codes, [scales,] activations, so the
+// activation DMAs of a step are its youngest loads and a step waits for the
+// activation stage issued two steps earlier by counting the loads of the
+// previous step alone; groups are older still.  Requires K % 256 == 0.
+constexpr int kGroupSteps = 4;
+constexpr int kGroupBufs = 3;
+constexpr int kCodesGroup = BN * 128;                 // 32 KB: 256 weight rows x one line
+constexpr int kScalesGroup = BN * 8;                  // 2 KB
+constexpr int kMx4A = 3;                              // activation stages
+constexpr int kMx4Lds = kMx4A * kStageA + kGroupBufs * (kCodesGroup + kScalesGroup);
+constexpr int kCodeDmaPerStep = kCodesGroup / (kWave * 16) / kWaves / kGroupSteps;  // 1
+static_assert(kCodeDmaPerStep == 1, "one code DMA per wave per step");
+static_assert(kScalesGroup == kWaves * kWave * 4, "one scale DMA per wave per group");
+
+// MFMAs of one K-step for the VM valid row sub-tiles of this wave.  `cb` and
+// `sb` are the group's code and scale buffers, p the step's place in it.
+template <int VM>
+__device__ __forceinline__ void mx4_step(const char* st, const char* cb, const char* sb, int p,
+                                         const int* aoff, const int* brow, int half,
+                                         f32x16_t (&acc)[2][2]) {
+  if constexpr (VM > 0) {
+    BRegs<kMXFP4> b;
+#pragma unroll
+    for (int m = 0; m < 2; ++m) {
+      const int u = 2 * p + half;  // the lane's 32-element block inside the line
+      b.v[m] = *reinterpret_cast<const u32x4*>(cb + brow[m] * 128 + ((u ^ (brow[m] & 7)) << 4));
+      b.s[m] = static_cast<uint8_t>(sb[brow[m] * 8 + u]);
+    }
+    bf16x8_t af[2][2];
+#pragma unroll
+    for (int mi = 0; mi < VM; ++mi) af[0][mi] = *reinterpret_cast<const bf16x8_t*>(st + aoff[4 * mi]);
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      if (s + 1 < 4) {
+#pragma unroll
+        for (int mi = 0; mi < VM; ++mi)
+          af[(s + 1) & 1][mi] = *reinterpret_cast<const bf16x8_t*>(st + aoff[4 * mi + s + 1]);
+      }
+      const bf16x8_t b0 = b_frag<kMXFP4>(b, 0, s);
+      const bf16x8_t b1 = b_frag<kMXFP4>(b, 1, s);
+#pragma unroll
+      for (int mi = 0; mi < VM; ++mi) {
+        acc[0][mi] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[s & 1][mi], b0, acc[0][mi], 0, 0, 0);
+        acc[1][mi] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[s & 1][mi], b1, acc[1][mi], 0, 0, 0);
+      }
+    }
+  }
+}
+
+template <bool GATEUP>
+__global__ __launch_bounds__(kThreads) void gg_mx_group_kernel(GGArgs a) {
+  __shared__ __align__(1024) char lds[kMx4Lds];
+  char* const lds_a = lds;
+  char* const lds_c = lds + kMx4A * kStageA;
+  char* const lds_s = lds_c + kGroupBufs * kCodesGroup;
+  const int tid = threadIdx.x;
+  const int lane = lane_id();
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave >> 2;
+  const int wn = wave & 3;
+  const int half = lane >> 5;
+  const int cl = lane & 31;
+
+  // ---- tile (as in the other kernels)
+  const int num_tiles = *a.num_mtiles * a.ntiles;
+  const int per_xcd = (num_tiles + kXcds - 1) / kXcds;
+  const int slot = blockIdx.x / kXcds;
+  if (slot >= per_xcd) return;
+  const int L = (blockIdx.x % kXcds) * per_xcd + slot;
+  if (L >= num_tiles) return;
+  const int* eq = a.mtiles + kMtileInts * (L / a.ntiles);
+  const int e = eq[0];
+  const int first_mt = eq[3];
+  const int nmt = eq[4];
+  const int local = L - first_mt * a.ntiles;
+  const int ntile = local / nmt;
+  const int* em = a.mtiles + kMtileInts * (first_mt + (local - ntile * nmt));
+  const int row0 = em[1];
+  const int nrows = em[2];
+  const int nbase = ntile * (GATEUP ? BN / 2 : BN);
+
+  // weight row r of the tile (0..255) -> its codes and scales
+  auto wrow = [&](int r, const char*& code, const uint8_t*& scale) {
+    const void* w = a.w0;
+    const uint8_t* sc = a.s0;
+    int col;
+    if (GATEUP) {
+      const bool up = r >= BN / 2;
+      w = up ? a.w1 : a.w0;
+      sc = up ? a.s1 : a.s0;
+      col = nbase + (up ? r - BN / 2 : r);
+    } else {
+      col = nbase + r;
+    }
+    col = min(col, a.N - 1);
+    code = reinterpret_cast<const char*>(w) + ((size_t)e * a.N + col) * (a.K / 2);
+    scale = sc + ((size_t)e * a.N + col) * (a.K / 32);
+  };
+
+  // ---- activation DMA sources (see gg_dma_kernel)
+  const size_t rb = (size_t)a.K * 2;
+  const int slot16 = lane & 7;
+  const char* asrc[kDmaA];
+#pragma unroll
+  for (int j = 0; j < kDmaA; ++j) {
+    const int r = (kDmaA * 8) * wave + 8 * j + (lane >> 3);
+    const int f = (r & 7) ^ ((r >> 3) & 1);
+    const int src = row0 + min(r, nrows - 1);
+    asrc[j] = reinterpret_cast<const char*>(a.a_src) +
+              (GATEUP ? (size_t)(a.sorted_src[src] / a.k) : (size_t)src) * rb + ((slot16 ^ f) << 4);
+  }
+  char* const adst = lds_a + (kDmaA * 8) * wave * (BK * 2);
+
+  // ---- code DMA sources: at group place p, wave w fills weight rows
+  // 32 w + 8 p + lane/8, line slot lane%8 <- global unit (lane%8) ^ (row & 7)
+  const char* csrc[kGroupSteps];
+#pragma unroll
+  for (int p = 0; p < kGroupSteps; ++p) {
+    const int r = 32 * wave + 8 * p + (lane >> 3);
+    const char* code;
+    const uint8_t* scale;
+    wrow(r, code, scale);
+    csrc[p] = code + ((slot16 ^ (r & 7)) << 4);
+  }
+  // ---- scale DMA source: dword lane of wave w covers weight row (64 w +
+  // lane) / 2, bytes 4 ((64 w + lane) % 2) .. +3 of the group's 8
+  const uint8_t* ssrc;
+  {
+    const int d = kWave * wave + lane;
+    const char* code;
+    wrow(d >> 1, code, ssrc);
+    ssrc += 4 * (d & 1);
+  }
+  const int nk = a.K / BK;
+  const int ng = nk / kGroupSteps;
+
+  // Loads for group g / step kk go to that group's / step's buffer; past the
+  // end they re-read the last group or step, still into the buffer that is
+  // free at that point.
+  auto issue_codes = [&](int g, int p) {  // part p of group g
+    char* d = lds_c + (g % kGroupBufs) * kCodesGroup + (32 * wave + 8 * p) * 128;
+    dma16<0>(csrc[p] + (size_t)min(g, ng - 1) * 128, d);
+  };
+  auto issue_scales = [&](int g) {
+    char* d = lds_s + (g % kGroupBufs) * kScalesGroup + wave * kWave * 4;
+    __builtin_amdgcn_global_load_lds(ssrc + (size_t)min(g, ng - 1) * 8, (lds_void_t*)d, 4, 0, 0);
+  };
+  auto issue_a = [&](int kk) {
+    char* d = adst + (kk % kMx4A) * kStageA;
+    const size_t go = (size_t)min(kk, nk - 1) * (BK * 2);
+#pragma unroll
+    for (int j = 0; j < kDmaA; ++j) dma16<kAuxA>(asrc[j] + go, d + j * 8 * (BK * 2));
+  };
+
+  // ---- fragment offsets
+  int aoff[8], brow[2];
+#pragma unroll
+  for (int mi = 0; mi < 2; ++mi)
+#pragma unroll
+    for (int s = 0; s < 4; ++s) aoff[4 * mi + s] = t_off(64 * wm + 32 * mi + cl, half * 4 + s);
+#pragma unroll
+  for (int m = 0; m < 2; ++m) brow[m] = GATEUP ? (m * (BN / 2) + 32 * wn + cl) : (64 * wn + 32 * m + cl);
+
+  f32x16_t acc[2][2];
+#pragma unroll
+  for (int m = 0; m < 2; ++m)
+#pragma unroll
+    for (int mi = 0; mi < 2; ++mi) acc[m][mi] = f32x16_t{};
+
+  const int vm = min(max((nrows + 31) / 32 - 2 * wm, 0), 2);
+
+  // ---- prologue: groups 0 and 1, then activation steps 0 and 1 (youngest)
+#pragma unroll
+  for (int g = 0; g < 2; ++g) {
+#pragma unroll
+    for (int p = 0; p < kGroupSteps; ++p) issue_codes(g, p);
+    issue_scales(g);
+  }
+  asm volatile("" ::: "memory");  // activation DMAs are the youngest loads
+  issue_a(0);
+  issue_a(1);
+
+  auto main_loop = [&](auto vm_c) {
+    constexpr int VM = decltype(vm_c)::value;
+    for (int g = 0; g < ng; ++g) {
+      const char* cb = lds_c + (g % kGroupBufs) * kCodesGroup;
+      const char* sb = lds_s + (g % kGroupBufs) * kScalesGroup;
+#pragma unroll
+      for (int p = 0; p < kGroupSteps; ++p) {
+        const int kk = kGroupSteps * g + p;
+        // loads younger than activation stage kk: those of step kk-1 (three,
+        // four after a group's first step); at step 0 only stage 1's two
+        if (p == 1)
+          wait_and_barrier<4>();
+        else if (p == 0)
+          wait_and_barrier<2>();
+        else
+          wait_and_barrier<3>();
+        issue_codes(g + 2, p);
+        if (p == 0) issue_scales(g + 2);
+        asm volatile("" ::: "memory");  // activation DMAs are the step's youngest loads
+        issue_a(kk + 2);
+        mx4_step<VM>(lds_a + (kk % kMx4A) * kStageA, cb, sb, p, aoff, brow, half, acc);
+      }
+    }
+  };
+  if (vm == 2)
+    main_loop(std::integral_constant<int, 2>{});
+  else if (vm == 1)
+    main_loop(std::integral_constant<int, 1>{});
+  else
+    main_loop(std::integral_constant<int, 0>{});
+  // the clamped loads past the end must land before the block's LDS is released
+  __builtin_amdgcn_s_waitcnt(0);
+
+  // ---- epilogue (as gg_dma_kernel)
+#pragma unroll
+  for (int mi = 0; mi < 2; ++mi) {
+    if (mi < vm) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int row = 64 * wm + 32 * mi + 8 * (i >> 2) + 4 * half + (i & 3);
+        if (row < nrows) {
+          const size_t orow = (size_t)(row0 + row) * a.N;
+          if (GATEUP) {
+            const int col = nbase + 32 * wn + cl;
+            if (col < a.N) {
+              const float g = acc[0][mi][i];
+              const float u = acc[1][mi][i];
+              reinterpret_cast<uint16_t*>(a.out)[orow + col] = f32_to_bf16(g / (1.0f + expf(-g)) * u);
+            }
+          } else {
+#pragma unroll
+            for (int m = 0; m < 2; ++m) {
+              const int col = nbase + 64 * wn + 32 * m + cl;
+              if (col < a.N) reinterpret_cast<float*>(a.out)[orow + col] = acc[m][mi][i];
+            }
+          }
+        }
+      }
+    }
+  }
+}
+
 // K-steps of loads in flight (register budget of two waves per SIMD).
-constexpr int kDepthLds = 2;     // gg_lds_kernel, bf16 weights
 constexpr int kDepthDirect = 2;  // gg_direct_b_kernel, MX-FP4 weights
+
+// MX-FP4 GEMMs whose K (d for gate/up, f for down) holds whole code groups
+// use gg_mx_group_kernel; others fall back to gg_direct_b_kernel.
+bool mx_grouped(int K) { return K % (kGroupSteps * BK) == 0; }
 
 // Output columns per tile: gate/up counts columns of each of W_gate, W_up.
 int tile_cols(const Dims& dm, bool gateup) {
-  const int base = dm.wfmt == kMXFP4 ? 256 : 128;
+  const int K = gateup ? dm.d : dm.f;
+  const int base = (dm.wfmt == kMXFP4 && !mx_grouped(K)) ? 256 : 128;
   return gateup ? base : 2 * base;
 }
 
@@ -511,10 +779,12 @@ template <bool GATEUP>
 hipError_t launch_gg(const Dims& dm, const GGArgs& a, hipStream_t s) {
   const size_t max_tiles = grouped_gemm_max_mtiles(dm) * (size_t)a.ntiles;
   const dim3 grid((unsigned)((max_tiles + kXcds - 1) / kXcds * kXcds)), block(kThreads);
-  if (dm.wfmt == kMXFP4)
+  if (dm.wfmt == kMXFP4 && mx_grouped(a.K))
+    gg_mx_group_kernel<GATEUP><<<grid, block, 0, s>>>(a);
+  else if (dm.wfmt == kMXFP4)
     gg_direct_b_kernel<kMXFP4, GATEUP, kDepthDirect><<<grid, block, 0, s>>>(a);
   else
-    gg_lds_kernel<kBF16, GATEUP, kDepthLds><<<grid, block, 0, s>>>(a);
+    gg_dma_kernel<GATEUP><<<grid, block, 0, s>>>(a);
   return hipGetLastError();
 }
 

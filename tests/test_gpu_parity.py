@@ -101,13 +101,17 @@ SMALL = [
     ("f32_t1", 1, 128, 8, 3, 64, "f32", "f32"),
     ("mx_t1_bigf", 1, 64, 4, 2, 8192, "bf16", "mxfp4"),
     ("bf16_t1_bigf", 1, 64, 4, 2, 16384, "bf16", "bf16"),
-    # grouped MFMA GEMM path (T > 16, d and f multiples of 128)
+    # grouped MFMA GEMM path (T > 16, d and f multiples of 64)
     ("gg_bf16_t17", 17, 256, 8, 2, 128, "bf16", "bf16"),
     ("gg_bf16_t300", 300, 512, 16, 4, 384, "bf16", "bf16"),
     ("gg_bf16_hot", 600, 384, 4, 2, 256, "bf16", "bf16"),      # ~300 rows/expert: 3 m-tiles
     ("gg_bf16_ntail", 64, 640, 6, 3, 128, "bf16", "bf16"),     # down N=640: partial n-tile
+    ("gg_bf16_oddk", 70, 320, 6, 2, 192, "bf16", "bf16"),      # odd K-step counts
     ("gg_mx_t100", 100, 256, 8, 4, 256, "bf16", "mxfp4"),
     ("gg_mx_hot", 700, 512, 5, 2, 384, "bf16", "mxfp4"),
+    ("gg_mx_ntail", 90, 640, 6, 2, 256, "bf16", "mxfp4"),      # down N=640: partial n-tile
+    ("gg_mx_oddk", 80, 320, 6, 2, 192, "bf16", "mxfp4"),       # K % 128 != 0 on both GEMMs
+    ("gg_mx_gtail", 150, 512, 6, 2, 320, "bf16", "mxfp4"),     # gate/up N=320: partial n-tile
 ]
 
 
