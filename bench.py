@@ -13,6 +13,7 @@ stream inside this run), and the CPU oracle timed on a bounded sample.
 from __future__ import annotations
 
 import argparse
+import dataclasses
 import hashlib
 import json
 import os
@@ -36,6 +37,16 @@ def _parse():
     p.add_argument("--cpu-seconds", type=float, default=12.0,
                    help="CPU oracle sample budget (seconds of oracle work)")
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle leg")
+    p.add_argument("--T", type=int, default=None,
+                   help="override the workload's token count; the name gets a _T<n> suffix")
+    p.add_argument("--sweep", default=None,
+                   help="comma-separated token counts: one JSON line per T (weights generated once)")
+    p.add_argument("--layers", type=int, default=1,
+                   help="chain this many layers per step, each with its own weights (out of one "
+                        "layer is x of the next); tokens/s counts each token once per step")
+    p.add_argument("--graph", action="store_true",
+                   help="replay each step from a captured HIP graph (one graph per logit-set "
+                        "offset, rotated) instead of launching it")
     return p.parse_args()
 
 
@@ -134,64 +145,89 @@ def cpu_baseline(wl, x, w, logit_sets, budget_s: float):
                       f"{len(os.sched_getaffinity(0))} cores"}
 
 
-def main():
-    args = _parse()
-    if args.gpus != 1:
-        print(f"bench.py measures one GPU only (got --gpus {args.gpus}); this library has no "
-              "multi-GPU path", file=sys.stderr)
-        sys.exit(2)
+def measure(wl, ws_list, args, with_cpu: bool):
+    """Time `args.steps` steps of `args.layers` chained layers of workload `wl`
+    (weights `ws_list[i]` for layer i) and return the JSON record."""
+    import ctypes
 
     import torch
 
     from expert_ffn_layer_softmax_amd import (moe_layer_forward, moe_timing_names, moe_timing_query,
                                               moe_timing_start, moe_timing_stop)
-    from synth import WORKLOADS, gen_expert_weights, gen_logits, gen_x
+    from expert_ffn_layer_softmax_amd import _lib as L
+    from synth import gen_logits, gen_x
 
-    wl = WORKLOADS[args.workload]
-    assert not wl.router, "bench workloads route by pre-drawn logits"
     dev = torch.device("cuda:0")
-    print(f"[bench] generating {wl.name} inputs", file=sys.stderr, flush=True)
+    nl = len(ws_list)
     x = gen_x(wl.T, wl.d, wl.act, wl.seed, dev, std=wl.x_std)
-    w = gen_expert_weights(wl, dev)
     sets = gen_logits(wl.T, wl.E, wl.seed, dev, sets=wl.logit_sets, bias_std=wl.bias_std)
     nsets = sets.shape[0]
     k = wl.k
-    out = torch.empty(wl.T, wl.d, dtype=x.dtype, device=dev)
+    # layer i reads acts[i] and writes acts[i + 1]; acts[0] is x
+    acts = [x] + [torch.empty(wl.T, wl.d, dtype=x.dtype, device=dev) for _ in range(nl)]
     topk_idx = torch.empty(wl.T, k, dtype=torch.int32, device=dev)
     topk_w = torch.empty(wl.T, k, dtype=torch.float32, device=dev)
-    res = moe_layer_forward(x, w, k, logits=sets[0], topk_idx=topk_idx, topk_w=topk_w, out=out)
+    res = moe_layer_forward(x, ws_list[0], k, logits=sets[0], topk_idx=topk_idx, topk_w=topk_w,
+                            out=acts[1])
     ws = res["workspace"]
 
     # Steps call the C entry point directly with pre-marshalled arguments, so
     # host-side Python work does not pace the GPU.
-    import ctypes
-
-    from expert_ffn_layer_softmax_amd import _lib as L
-    wfmt = L._wfmt(w)
+    wfmt = L._wfmt(ws_list[0])
     dims = L._dims(wl.T, wl.d, wl.E, k, wl.f, L._ACT[x.dtype], wfmt)
-    wts = L._weights(w, wl.E, wl.d, wl.f, wfmt, dev)
-    stream = L._stream(x)
+    wts = [L._weights(w, wl.E, wl.d, wl.f, wfmt, dev) for w in ws_list]
     lptr = [ctypes.c_void_p(sets[i].data_ptr()) for i in range(nsets)]
-    fixed = [ctypes.c_void_p(t.data_ptr()) for t in (x, topk_idx, topk_w, out, ws)]
+    aptr = [ctypes.c_void_p(t.data_ptr()) for t in acts]
+    fixed = [ctypes.c_void_p(t.data_ptr()) for t in (topk_idx, topk_w, ws)]
     fwd = L.lib.moe_layer_forward
-    dref, wref = ctypes.byref(dims), ctypes.byref(wts)
+    dref, wref = ctypes.byref(dims), [ctypes.byref(t) for t in wts]
     wsn = ws.numel()
 
-    def step(i):
-        st = fwd(dref, fixed[0], None, lptr[i % nsets], wref, fixed[1], fixed[2], fixed[3], fixed[4],
-                 wsn, stream)
-        if st != 0:
-            raise L.MoeError(st, "moe_layer_forward")
+    def launch(i, stream):
+        for layer in range(nl):
+            st = fwd(dref, aptr[layer], None, lptr[(i + layer) % nsets], wref[layer], fixed[0],
+                     fixed[1], aptr[layer + 1], fixed[2], wsn, stream)
+            if st != 0:
+                raise L.MoeError(st, "moe_layer_forward")
 
-    # unique experts per step (for algorithmic bytes), from the device's routing
+    stream0 = L._stream(x)
+
+    def step(i):
+        launch(i, stream0)
+
+    # unique experts per layer call (for algorithmic bytes), from the device's routing
     uniq = []
     for i in range(nsets):
-        step(i)
+        fwd(dref, aptr[0], None, lptr[i], wref[0], fixed[0], fixed[1], aptr[1], fixed[2], wsn, stream0)
         uniq.append(int(torch.unique(topk_idx).numel()))
+
+    graphs = None
+    if args.graph:
+        # one graph per logit-set offset; replays rotate through them
+        ng = min(nsets, 8)
+        graphs = []
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            for i in range(ng):
+                launch(i, ctypes.c_void_p(side.cuda_stream))  # warm-up on the capture stream
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        for i in range(ng):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                launch(i, ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
+            graphs.append(g)
+        torch.cuda.synchronize()
+
+        def step(i):  # noqa: F811
+            graphs[i % len(graphs)].replay()
+
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
-    print(f"[bench] timing {args.steps} steps", file=sys.stderr, flush=True)
+    print(f"[bench] {wl.name}: timing {args.steps} steps of {nl} layer(s)"
+          f"{' from HIP graphs' if graphs else ''}", file=sys.stderr, flush=True)
     t0 = time.perf_counter()
     for i in range(args.steps):
         step(i)
@@ -200,13 +236,15 @@ def main():
     ms = el * 1e3 / args.steps
     tokens_per_s = wl.T * args.steps / el
 
-    # per-kernel HIP-event durations on the launch stream (separate pass)
+    # per-kernel HIP-event durations on the launch stream (separate pass of
+    # launched steps; graph replays carry no events)
     moe_timing_start()
     for i in range(args.steps):
-        step(i)
+        launch(i, stream0)
     torch.cuda.synchronize()
     moe_timing_stop()
-    path = "decode" if wl.T <= 16 else "prefill"
+    # the path the library took: the grouped GEMM kernels ran, or the GEMV ones
+    path = "prefill" if moe_timing_query("gg_gate_up")[0] > 0 else "decode"
     kname, srcs = DOMINANT[path]
     n_launch, tot_ms = moe_timing_query(kname)
     if n_launch == 0:
@@ -214,7 +252,7 @@ def main():
     kernel_us = tot_ms * 1e3 / n_launch
     eb = _expert_bytes(wl)
     act_b = 4 if wl.act == "f32" else 2
-    mean_uniq = sum(uniq[i % nsets] for i in range(args.steps)) / args.steps
+    mean_uniq = sum(uniq) / len(uniq)
     # the gate/up kernel's algorithmic work: the active experts' gate and up
     # weights read once, x read, h written; 2 FLOPs per MAC over T*k rows
     k_bytes = mean_uniq * eb["gate_up"] + wl.T * wl.d * act_b + wl.T * k * wl.f * act_b
@@ -225,24 +263,30 @@ def main():
     else:
         bound, unit, peak = "hbm", "GB/s", HBM_PEAK_GBS
         achieved = k_bytes / (kernel_us * 1e-6) / 1e9
-    step_bytes = (mean_uniq * eb["total"] + 2 * wl.T * wl.d * act_b + wl.T * wl.E * 4 + wl.T * k * 8)
-    step_flops = 6.0 * wl.T * k * wl.d * wl.f
+    layer_bytes = (mean_uniq * eb["total"] + 2 * wl.T * wl.d * act_b + wl.T * wl.E * 4 + wl.T * k * 8)
+    layer_flops = 6.0 * wl.T * k * wl.d * wl.f
+    step_bytes, step_flops = nl * layer_bytes, nl * layer_flops
     t_floor = max(step_bytes / (HBM_PEAK_GBS * 1e9), step_flops / (BF16_PEAK_TFLOPS * 1e12))
     digest = _source_digest(srcs)
-    traffic = _traffic(kname, wl.name, digest)
+    traffic = _traffic(kname, wl.name, digest) if nl == 1 else None
     breakdown = {}
     for kn in moe_timing_names():
         n, t = moe_timing_query(kn)
         if n:
             breakdown[kn] = round(t * 1e3 / n, 2)
 
+    cfg = {"workload": wl.name, "T": wl.T, "d": wl.d, "E": wl.E, "k": k, "f": wl.f,
+           "weights": wl.wfmt, "logit_sets": nsets, "mean_unique_experts": round(mean_uniq, 2)}
+    if nl > 1:
+        cfg["layers"] = nl
+    if graphs:
+        cfg["hip_graph"] = True
     rec = {
         "metric": METRIC, "value": round(tokens_per_s, 2), "unit": "tokens/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 5),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "bf16" if wl.act == "bf16" else "f32", "data": "synthetic",
-        "config": {"workload": wl.name, "T": wl.T, "d": wl.d, "E": wl.E, "k": k, "f": wl.f,
-                   "weights": wl.wfmt, "logit_sets": nsets, "mean_unique_experts": round(mean_uniq, 2)},
+        "config": cfg,
         "roofline": {"bound": bound, "kernel": kname, "achieved": round(achieved, 1),
                      "peak": peak, "unit": unit, "frac": round(achieved / peak, 4),
                      "traffic": traffic, "kernel_us": round(kernel_us, 2),
@@ -254,11 +298,43 @@ def main():
                  "attainable_frac": round(t_floor / (ms * 1e-3), 4),
                  "kernel_us": breakdown},
     }
-    if not args.no_cpu:
+    if with_cpu:
         print("[bench] CPU oracle baseline", file=sys.stderr, flush=True)
-        rec["cpu_baseline"] = cpu_baseline(wl, x, w, sets, args.cpu_seconds)
+        rec["cpu_baseline"] = cpu_baseline(wl, x, ws_list[0], sets, args.cpu_seconds)
     else:
         rec["cpu_baseline"] = None
+    return rec
+
+
+def main():
+    args = _parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (got --gpus {args.gpus}); this library has no "
+              "multi-GPU path", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    from synth import WORKLOADS, gen_expert_weights
+
+    base = WORKLOADS[args.workload]
+    assert not base.router, "bench workloads route by pre-drawn logits"
+    if args.layers < 1:
+        raise SystemExit("--layers must be >= 1")
+    dev = torch.device("cuda:0")
+    print(f"[bench] generating {base.name} weights for {args.layers} layer(s)", file=sys.stderr, flush=True)
+    # each layer's experts come from their own seed
+    ws_list = [gen_expert_weights(dataclasses.replace(base, seed=base.seed + 7919 * i), dev)
+               for i in range(args.layers)]
+    if args.sweep:
+        for T in [int(t) for t in args.sweep.split(",")]:
+            wl = dataclasses.replace(base, T=T, name=f"{base.name}_T{T}")
+            print(json.dumps(measure(wl, ws_list, args, with_cpu=False)), flush=True)
+        return
+    wl = base
+    if args.T is not None:
+        wl = dataclasses.replace(base, T=args.T, name=f"{base.name}_T{args.T}")
+    rec = measure(wl, ws_list, args, with_cpu=not args.no_cpu and args.layers == 1)
     print(json.dumps(rec), flush=True)
 
 

@@ -791,7 +791,7 @@ hipError_t launch_gg(const Dims& dm, const GGArgs& a, hipStream_t s) {
 }  // namespace
 
 bool grouped_gemm_ok(const Dims& dm) {
-  return dm.act == kBF16 && (dm.wfmt == kBF16 || dm.wfmt == kMXFP4) && dm.T > kDecodeMaxT &&
+  return dm.act == kBF16 && (dm.wfmt == kBF16 || dm.wfmt == kMXFP4) && dm.T >= kGemmMinT &&
          dm.d % BK == 0 && dm.f % BK == 0;
 }
 

@@ -21,6 +21,13 @@ constexpr int kMtileInts = 8;
 // Largest T routed and permuted by the single-workgroup decode kernel.
 constexpr int kDecodeMaxT = 16;
 
+// Smallest T that takes the grouped MFMA GEMMs (bf16 activations).  Below it
+// the GEMV kernels stream each active expert's weights once per layer and are
+// faster; measured at d=6144, E=256, k=8, f=2816 on MI355X: T=32 GEMV 2.64 ms
+// vs MFMA 2.83 ms, T=64 GEMV 3.90 ms vs MFMA 3.71 ms (bf16 weights; MX-FP4
+// crosses over between the same T).
+constexpr int kGemmMinT = 48;
+
 struct Dims {
   int T, d, E, k, f, act, wfmt;
   long long Tk() const { return (long long)T * k; }

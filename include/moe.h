@@ -140,9 +140,10 @@ moe_status_t moe_combine(const moe_dims_t* dims, const float* y_sorted, const in
 /* The whole layer: [router logits] -> route -> permute -> expert FFN ->
  * combine.  If w_router is non-NULL, logits[T][E] = x . w_router^T (fp32
  * accumulation) is written to `logits`; otherwise `logits` is read as input.
- * topk_idx / topk_w receive the routing.  For T <= 16 the down projection is
- * fused with the combine (the per-token sum runs in ascending expert order
- * instead of slot order; still deterministic).
+ * topk_idx / topk_w receive the routing.  For T == 1 (k <= 16) the down
+ * projection is fused with the combine; the per-token sum keeps slot order
+ * and the combine's arithmetic, so the result equals the stage-wise path bit
+ * for bit.
  * workspace must hold moe_workspace_size(dims) bytes. */
 moe_status_t moe_layer_forward(const moe_dims_t* dims, const void* x, const void* w_router,
                                float* logits, const moe_expert_weights_t* weights,

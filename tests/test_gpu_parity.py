@@ -101,8 +101,10 @@ SMALL = [
     ("f32_t1", 1, 128, 8, 3, 64, "f32", "f32"),
     ("mx_t1_bigf", 1, 64, 4, 2, 8192, "bf16", "mxfp4"),
     ("bf16_t1_bigf", 1, 64, 4, 2, 16384, "bf16", "bf16"),
-    # grouped MFMA GEMM path (T > 16, d and f multiples of 64)
-    ("gg_bf16_t17", 17, 256, 8, 2, 128, "bf16", "bf16"),
+    ("bf16_t47", 47, 320, 16, 4, 192, "bf16", "bf16"),          # largest T on the GEMV path
+    ("mx_t47", 47, 320, 16, 4, 192, "bf16", "mxfp4"),
+    # grouped MFMA GEMM path (T >= 48, d and f multiples of 64)
+    ("gg_bf16_t48", 48, 256, 8, 2, 128, "bf16", "bf16"),
     ("gg_bf16_t300", 300, 512, 16, 4, 384, "bf16", "bf16"),
     ("gg_bf16_hot", 600, 384, 4, 2, 256, "bf16", "bf16"),      # ~300 rows/expert: 3 m-tiles
     ("gg_bf16_ntail", 64, 640, 6, 3, 128, "bf16", "bf16"),     # down N=640: partial n-tile
