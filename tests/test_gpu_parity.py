@@ -195,6 +195,43 @@ def test_single_token_fused_path_equals_stagewise(wfmt, k):
                        staged.view(torch.int16) if act == "bf16" else staged.view(torch.int32))
 
 
+# ------------------------------------------------------------ HIP graphs
+@pytest.mark.parametrize("T,wfmt", [(1, "bf16"), (16, "bf16"), (100, "bf16"), (100, "mxfp4")])
+def test_hip_graph_replay(T, wfmt):
+    """A captured layer replays to the eager result, bit for bit, after eager
+    calls with other routing have rewritten the same workspace and outputs."""
+    from expert_ffn_layer_softmax_amd import moe_layer_forward
+    log(f"graph T={T} {wfmt}")
+    k = 8
+    wl = Workload("graph", T=T, d=512, E=32, k=k, f=256, act="bf16", wfmt=wfmt, seed=71 + T,
+                  x_std=1.0, wg_std=512 ** -0.5, wu_std=512 ** -0.5, wd_std=256 ** -0.5)
+    x, w, _, logits = make_inputs(wl)
+    other_logits = torch.randn(T, wl.E, generator=torch.Generator().manual_seed(T)).cuda()
+    eager = moe_layer_forward(x, w, k, logits=logits)
+    ref_out, ref_idx = eager["out"].clone(), eager["topk_idx"].clone()
+    ws = eager["workspace"]
+    out = torch.empty_like(ref_out)
+    idx = torch.empty_like(ref_idx)
+    tw = torch.empty(T, k, dtype=torch.float32, device="cuda")
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        moe_layer_forward(x, w, k, logits=logits, topk_idx=idx, topk_w=tw, out=out, workspace=ws)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        moe_layer_forward(x, w, k, logits=logits, topk_idx=idx, topk_w=tw, out=out, workspace=ws)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        moe_layer_forward(x, w, k, logits=other_logits, topk_idx=idx, topk_w=tw, out=out, workspace=ws)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(idx, ref_idx)
+        assert torch.equal(out.view(torch.int16), ref_out.view(torch.int16))
+
+
 # --------------------------------------------------- individual entry points
 @pytest.mark.parametrize("wfmt,T", [("bf16", 7), ("bf16", 64), ("mxfp4", 23), ("f32", 9)])
 def test_stagewise_entry_points(wfmt, T):
