@@ -9,8 +9,10 @@ from .moe_oracle import (  # noqa: F401
     E2M1_VALUES,
     combine,
     decode_bf16,
+    decode_e4m3,
     decode_e8m0,
     decode_mxfp4,
+    decode_nvfp4,
     dense_layer,
     expert_ffn,
     layer,

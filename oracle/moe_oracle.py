@@ -28,7 +28,9 @@ Storage convention (the reduction dimension is innermost):
 bf16 values are passed as their raw ``uint16`` bit patterns and MX-FP4 weights
 as ``uint8`` codes (two E2M1 values per byte, even element in the low nibble)
 plus ``uint8`` E8M0 scales, one per 32 consecutive elements along the
-reduction dimension.
+reduction dimension.  NVFP4 weights (the pages' own 4-bit expert format:
+SGLang-TorchTPU on TPU v7 page, "Results") use the same codes with one E4M3
+scale byte per 16 consecutive elements and one fp32 scale per weight matrix.
 
 Every function below is pinned by ``tests/test_oracle_*.py`` against brute
 force, closed forms, invariants or library routines; none is "parity unpinned".
@@ -79,6 +81,41 @@ def decode_mxfp4(codes: np.ndarray, scales: np.ndarray) -> np.ndarray:
     sc = decode_e8m0(scales)
     assert sc.shape == blocks.shape[:-1], (sc.shape, blocks.shape)
     return (blocks * sc[..., None]).reshape(val.shape)
+
+
+def decode_e4m3(b: np.ndarray) -> np.ndarray:
+    """OCP FP8 E4M3 bytes -> fp64.  1 sign bit, 4 exponent bits with bias 7,
+    3 mantissa bits; exponent field 0 holds the subnormals m/8 * 2**-6; there
+    are no infinities and S.1111.111 is NaN (largest finite value 448)."""
+    b = np.asarray(b, dtype=np.uint8).astype(np.int64)
+    sign = b >> 7
+    e = (b >> 3) & 0xF
+    m = b & 0x7
+    mag = np.where(e == 0, (m / 8.0) * 2.0 ** -6, (1.0 + m / 8.0) * np.ldexp(1.0, e - 7))
+    val = np.where(sign == 1, -mag, mag)
+    return np.where((e == 0xF) & (m == 0x7), np.nan, val)
+
+
+def decode_nvfp4(codes: np.ndarray, scales: np.ndarray, tensor_scale) -> np.ndarray:
+    """NVFP4 block-scaled weights -> fp64.
+
+    ``codes[..., K/2]`` as in MX-FP4 (element 2i in the low nibble);
+    ``scales[..., K/16]`` holds one E4M3 byte for each run of 16 consecutive
+    elements along the last axis; ``tensor_scale`` is the matrix's fp32 scale.
+    value = E2M1(code) * E4M3(scale) * tensor_scale.
+    """
+    codes = np.asarray(codes, dtype=np.uint8)
+    lo = codes & 0x0F
+    hi = codes >> 4
+    nib = np.stack([lo, hi], axis=-1).reshape(*codes.shape[:-1], codes.shape[-1] * 2)
+    mag = E2M1_VALUES[nib & 0x7]
+    val = np.where(nib & 0x8, -mag, mag)
+    K = val.shape[-1]
+    assert K % 16 == 0, "NVFP4 rows must hold whole 16-element blocks"
+    blocks = val.reshape(*val.shape[:-1], K // 16, 16)
+    sc = decode_e4m3(scales)
+    assert sc.shape == blocks.shape[:-1], (sc.shape, blocks.shape)
+    return (blocks * sc[..., None]).reshape(val.shape) * float(np.float32(tensor_scale))
 
 
 # ----------------------------------------------------------------------------

@@ -25,7 +25,7 @@ class Workload:
     k: int
     f: int
     act: str            # "f32" | "bf16"
-    wfmt: str           # "f32" | "bf16" | "mxfp4"
+    wfmt: str           # "f32" | "bf16" | "mxfp4" | "nvfp4"
     router: bool = False        # logits computed from x and W_r inside the layer
     logit_sets: int = 1         # pre-generated logit sets, rotated per call
     bias_std: float = 0.0       # per-expert logit bias (skewed load)
@@ -62,6 +62,12 @@ WORKLOADS = {
                              wfmt="mxfp4", logit_sets=64, seed=20261207),
     "prefill_mxfp4": Workload("prefill_mxfp4", T=4096, d=D, E=E_, k=K_, f=F, act="bf16",
                               wfmt="mxfp4", bias_std=0.5, seed=20261207),
+    # The pages' own 4-bit format: E2M1 values, one E4M3 scale per 16 elements
+    # and one fp32 scale per weight matrix.
+    "decode_nvfp4": Workload("decode_nvfp4", T=1, d=D, E=E_, k=K_, f=F, act="bf16",
+                             wfmt="nvfp4", logit_sets=64, seed=20261208),
+    "prefill_nvfp4": Workload("prefill_nvfp4", T=4096, d=D, E=E_, k=K_, f=F, act="bf16",
+                              wfmt="nvfp4", bias_std=0.5, seed=20261208),
 }
 
 
@@ -122,16 +128,47 @@ def quantize_mxfp4(w: torch.Tensor):
     s = torch.clamp(e + 127, 1, 254)
     scale = torch.exp2(s - 127)
     v = blocks / scale[..., None]
-    mag = v.abs()
-    mids = torch.tensor(_E2M1_MID, dtype=torch.float32, device=w.device)
-    code = torch.bucketize(mag, mids, right=False)           # nearest, ties -> lower
-    tie = (mag[..., None] == mids).any(dim=-1)
-    code = torch.where(tie & (code % 2 == 1), code + 1, code)  # ties -> even code
-    code = torch.clamp(code, max=7)
-    code = code | torch.where(torch.signbit(v), 8, 0)
-    code = code.to(torch.uint8).reshape(*wf.shape[:-1], K)
+    code = _e2m1_codes(v).to(torch.uint8).reshape(*wf.shape[:-1], K)
     packed = code[..., 0::2] | (code[..., 1::2] << 4)
     return packed.contiguous(), s.to(torch.uint8).contiguous()
+
+
+def _e2m1_codes(v: torch.Tensor) -> torch.Tensor:
+    """Nearest E2M1 code (ties to the even code, saturating at +-6) for each
+    value of ``v``, with the sign in bit 3."""
+    mag = v.abs()
+    mids = torch.tensor(_E2M1_MID, dtype=torch.float32, device=v.device)
+    code = torch.bucketize(mag, mids, right=False)
+    tie = (mag[..., None] == mids).any(dim=-1)
+    code = torch.where(tie & (code % 2 == 1), code + 1, code)
+    code = torch.clamp(code, max=7)
+    return code | torch.where(torch.signbit(v), 8, 0)
+
+
+def quantize_nvfp4(w: torch.Tensor):
+    """NVFP4 quantisation of one matrix ``w[..., K]`` (K % 16 == 0).
+
+    Tensor scale ts = amax|w| / (6 * 448) (fp32; 1 for an all-zero matrix), so
+    every block scale fits E4M3.  Block scale per 16 elements: amax / 6 / ts,
+    cast to E4M3 (round to nearest even).  Elements: w / (scale * ts) rounded
+    to the nearest E2M1 value (ties to the even code), saturating at +-6.
+    Returns ``(codes uint8[..., K/2], scales uint8[..., K/16] (E4M3 bytes),
+    ts float)`` with element 2i in the low nibble of byte i.
+    """
+    K = w.shape[-1]
+    assert K % 16 == 0
+    wf = w.to(torch.float32)
+    amax = float(wf.abs().max())
+    ts = torch.tensor(amax / (6.0 * 448.0) if amax > 0 else 1.0, dtype=torch.float32).item()
+    blocks = wf.reshape(*wf.shape[:-1], K // 16, 16)
+    bs = (blocks.abs().amax(dim=-1) / 6.0 / ts).clamp(max=448.0)
+    bs8 = bs.to(torch.float8_e4m3fn)
+    bsv = bs8.to(torch.float32)
+    denom = (bsv * ts)[..., None]
+    v = torch.where(denom > 0, blocks / torch.where(denom > 0, denom, 1.0), torch.zeros_like(blocks))
+    code = _e2m1_codes(v).to(torch.uint8).reshape(*wf.shape[:-1], K)
+    packed = code[..., 0::2] | (code[..., 1::2] << 4)
+    return packed.contiguous(), bs8.view(torch.uint8).contiguous(), ts
 
 
 def gen_expert_weights(wl: Workload, device="cpu", experts=None):
@@ -140,12 +177,26 @@ def gen_expert_weights(wl: Workload, device="cpu", experts=None):
     bf16/f32: ``w_gate, w_up: [E][f][d]``, ``w_down: [E][d][f]``.
     mxfp4: uint8 codes ``[E][f][d/2]``, ``[E][d][f/2]`` and E8M0 scales
     ``[E][f][d/32]``, ``[E][d][f/32]`` under ``s_gate, s_up, s_down``.
+    nvfp4: the same codes, E4M3 scales (dtype float8_e4m3fn) ``[E][f][d/16]``,
+    ``[E][d][f/16]`` and fp32 matrix scales ``[E]`` under ``t_gate, t_up, t_down``.
     Expert e is drawn from its own seed, so any subset can be regenerated.
     """
     E, d, f = wl.E, wl.d, wl.f
     experts = range(E) if experts is None else experts
     n = len(experts)
-    if wl.wfmt == "mxfp4":
+    if wl.wfmt == "nvfp4":
+        out = dict(
+            w_gate=torch.empty(n, f, d // 2, dtype=torch.uint8, device=device),
+            w_up=torch.empty(n, f, d // 2, dtype=torch.uint8, device=device),
+            w_down=torch.empty(n, d, f // 2, dtype=torch.uint8, device=device),
+            s_gate=torch.empty(n, f, d // 16, dtype=torch.float8_e4m3fn, device=device),
+            s_up=torch.empty(n, f, d // 16, dtype=torch.float8_e4m3fn, device=device),
+            s_down=torch.empty(n, d, f // 16, dtype=torch.float8_e4m3fn, device=device),
+            t_gate=torch.empty(n, dtype=torch.float32, device=device),
+            t_up=torch.empty(n, dtype=torch.float32, device=device),
+            t_down=torch.empty(n, dtype=torch.float32, device=device),
+        )
+    elif wl.wfmt == "mxfp4":
         out = dict(
             w_gate=torch.empty(n, f, d // 2, dtype=torch.uint8, device=device),
             w_up=torch.empty(n, f, d // 2, dtype=torch.uint8, device=device),
@@ -166,7 +217,13 @@ def gen_expert_weights(wl: Workload, device="cpu", experts=None):
         wg = torch.randn(f, d, generator=g, device=device) * wl.wg_std
         wu = torch.randn(f, d, generator=g, device=device) * wl.wu_std
         wd = torch.randn(d, f, generator=g, device=device) * wl.wd_std
-        if wl.wfmt == "mxfp4":
+        if wl.wfmt == "nvfp4":
+            for name, w in (("gate", wg), ("up", wu), ("down", wd)):
+                c, s, t = quantize_nvfp4(w)
+                out["w_" + name][i] = c
+                out["s_" + name][i] = s.view(torch.float8_e4m3fn)
+                out["t_" + name][i] = t
+        elif wl.wfmt == "mxfp4":
             for name, w in (("gate", wg), ("up", wu), ("down", wd)):
                 c, s = quantize_mxfp4(w)
                 out["w_" + name][i] = c

@@ -1,6 +1,6 @@
-"""Pins for the oracle's input decoders: bf16, E8M0 and MX-FP4 (E2M1).
+"""Pins for the oracle's input decoders: bf16, E8M0, MX-FP4 (E2M1), E4M3 and NVFP4.
 
-bf16 and E8M0 are checked against torch's own dtype conversions; E2M1 against
+bf16, E8M0 and E4M3 are checked against torch's own dtype conversions; E2M1 against
 the format's bit-field definition (sign, two exponent bits with bias 1, one
 mantissa bit, subnormals at exponent 0) and the OCP quantiser's error bound.
 """
@@ -9,8 +9,8 @@ import numpy as np
 import pytest
 import torch
 
-from oracle import E2M1_VALUES, decode_bf16, decode_e8m0, decode_mxfp4
-from synth import quantize_mxfp4
+from oracle import E2M1_VALUES, decode_bf16, decode_e4m3, decode_e8m0, decode_mxfp4, decode_nvfp4
+from synth import quantize_mxfp4, quantize_nvfp4
 
 
 def test_bf16_decode_matches_torch(rng):
@@ -110,3 +110,60 @@ def test_mxfp4_shapes(shape, rng):
     assert codes.shape == (*shape[:-1], shape[-1] // 2)
     assert scales.shape == (*shape[:-1], shape[-1] // 32)
     assert decode_mxfp4(codes.numpy(), scales.numpy()).shape == shape
+
+
+# ----------------------------------------------------------------- NVFP4
+# The pages run expert weights in NVFP4 (SGLang-TorchTPU on TPU v7 page,
+# "Results"): E2M1 values, one OCP FP8 E4M3 scale per 16 elements, one fp32
+# scale per matrix.
+
+def test_e4m3_decode_matches_torch():
+    b = np.arange(256, dtype=np.uint8)
+    ref = torch.from_numpy(b).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    got = decode_e4m3(b)
+    assert np.array_equal(np.isnan(got), np.isnan(ref))
+    ok = ~np.isnan(ref)
+    np.testing.assert_array_equal(got[ok], ref[ok])
+    assert np.nanmax(got) == 448.0 and got[1] == 2.0 ** -9       # largest, smallest subnormal
+    assert got[0x38] == 1.0 and got[0xB8] == -1.0 and np.isnan(got[0x7F]) and np.isnan(got[0xFF])
+
+
+def test_nvfp4_blocks_of_16_and_tensor_scale():
+    codes = np.full((2, 16), 0x22, dtype=np.uint8)    # every element 1.0
+    scales = np.array([[0x38, 0x40], [0x3C, 0x01]], dtype=np.uint8)  # 1.0, 2.0 | 1.5, 2^-9
+    vals = decode_nvfp4(codes, scales, 0.25)
+    np.testing.assert_array_equal(vals[0, :16], 0.25)
+    np.testing.assert_array_equal(vals[0, 16:], 0.5)
+    np.testing.assert_array_equal(vals[1, :16], 0.375)
+    np.testing.assert_array_equal(vals[1, 16:], 0.25 * 2.0 ** -9)
+
+
+def test_nvfp4_reduces_to_e2m1_table():
+    codes = np.array([[c | ((c + 1) << 4) for c in range(0, 16, 2)]], dtype=np.uint8)
+    vals = decode_nvfp4(codes, np.array([[0x38]], dtype=np.uint8), 1.0)
+    np.testing.assert_array_equal(vals[0], [_e2m1_from_bits(c) for c in range(16)])
+
+
+def test_nvfp4_roundtrip_error_bound(rng):
+    w = torch.tensor(rng.normal(size=(8, 256)) * 0.02, dtype=torch.float32)
+    codes, scales, ts = quantize_nvfp4(w)
+    deq = decode_nvfp4(codes.numpy(), scales.numpy(), ts)
+    wb = w.numpy().astype(np.float64)
+    # the tensor scale puts the largest block scale at 448
+    assert np.isclose(np.abs(wb).max() / (6 * 448), ts, rtol=1e-6)
+    sc = decode_e4m3(scales.numpy()) * float(np.float32(ts))
+    err = np.abs(deq - wb).reshape(8, 16, 16) / sc[..., None]
+    # E2M1 steps are at most 2, and the E4M3 block scale is rounded by at
+    # most 1/16 relative, so every element lies within one unit of the block
+    assert np.all(err <= 1.0 + 1e-9)
+    assert np.linalg.norm(deq - wb) / np.linalg.norm(wb) < 0.12
+
+
+def test_nvfp4_products_exact_in_bf16(rng):
+    """E2M1 x E4M3 has at most 6 significant bits, so a weight without its
+    fp32 matrix scale is exact in bf16 (what the MFMA path feeds)."""
+    w = torch.tensor(rng.normal(size=(4, 512)) * 0.02, dtype=torch.float32)
+    codes, scales, _ = quantize_nvfp4(w)
+    deq = decode_nvfp4(codes.numpy(), scales.numpy(), 1.0)
+    as_bf16 = torch.tensor(deq).to(torch.bfloat16).to(torch.float64).numpy()
+    np.testing.assert_array_equal(deq, as_bf16)
