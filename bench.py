@@ -52,9 +52,10 @@ def _parse():
 
 def _expert_bytes(wl) -> dict:
     d, f = wl.d, wl.f
-    if wl.wfmt == "mxfp4":
-        gu = 2 * (f * d // 2 + f * d // 32)
-        dn = d * f // 2 + d * f // 32
+    if wl.wfmt in ("mxfp4", "nvfp4"):
+        sd = 32 if wl.wfmt == "mxfp4" else 16   # elements per scale byte
+        gu = 2 * (f * d // 2 + f * d // sd)
+        dn = d * f // 2 + d * f // sd
     else:
         b = 4 if wl.wfmt == "f32" else 2
         gu = 2 * f * d * b
@@ -109,9 +110,11 @@ def cpu_baseline(wl, x, w, logit_sets, budget_s: float):
         threads = 1
 
     def raw(t):
-        if wl.wfmt == "mxfp4":
-            return t.cpu().numpy()
-        return t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+        if t.dtype == torch.bfloat16:
+            return t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+        if t.dtype == torch.float8_e4m3fn:
+            return t.contiguous().view(torch.uint8).cpu().numpy()
+        return t.cpu().numpy()
 
     xh_raw = raw(x)
     T = wl.T
@@ -128,6 +131,11 @@ def cpu_baseline(wl, x, w, logit_sets, budget_s: float):
             h = host[e]
             if wl.wfmt == "mxfp4":
                 return tuple(oracle.decode_mxfp4(h["w_" + n], h["s_" + n]) for n in ("gate", "up", "down"))
+            if wl.wfmt == "nvfp4":
+                return tuple(oracle.decode_nvfp4(h["w_" + n], h["s_" + n], h["t_" + n])
+                             for n in ("gate", "up", "down"))
+            if wl.wfmt == "f32":
+                return tuple(h["w_" + n].astype(np.float64) for n in ("gate", "up", "down"))
             return tuple(oracle.decode_bf16(h["w_" + n]) for n in ("gate", "up", "down"))
 
         t0 = time.perf_counter()

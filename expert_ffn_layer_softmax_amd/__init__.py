@@ -12,6 +12,7 @@ from ._lib import (  # noqa: F401
     MOE_DTYPE_BF16,
     MOE_DTYPE_F32,
     MOE_DTYPE_MXFP4,
+    MOE_DTYPE_NVFP4,
     MoeError,
     lib,
     moe_combine,

@@ -19,7 +19,7 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.environ.get("MOE_MI355X_LIB") or os.path.join(_PKG, "libmoe_mi355x.so")
 
 MOE_OK = 0
-MOE_DTYPE_F32, MOE_DTYPE_BF16, MOE_DTYPE_MXFP4 = 0, 1, 2
+MOE_DTYPE_F32, MOE_DTYPE_BF16, MOE_DTYPE_MXFP4, MOE_DTYPE_NVFP4 = 0, 1, 2, 3
 
 if not os.path.exists(LIB_PATH):
     raise ImportError(
@@ -37,7 +37,8 @@ class MoeDims(ctypes.Structure):
 
 class MoeExpertWeights(ctypes.Structure):
     _fields_ = [("w_gate", ctypes.c_void_p), ("w_up", ctypes.c_void_p), ("w_down", ctypes.c_void_p),
-                ("s_gate", ctypes.c_void_p), ("s_up", ctypes.c_void_p), ("s_down", ctypes.c_void_p)]
+                ("s_gate", ctypes.c_void_p), ("s_up", ctypes.c_void_p), ("s_down", ctypes.c_void_p),
+                ("t_gate", ctypes.c_void_p), ("t_up", ctypes.c_void_p), ("t_down", ctypes.c_void_p)]
 
 
 _vp, _i32, _sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t
@@ -113,6 +114,17 @@ def _dims(T, d, E, k, f, act, wfmt) -> MoeDims:
 
 
 def _weights(w: dict, E, d, f, wfmt, device) -> MoeExpertWeights:
+    if wfmt == MOE_DTYPE_NVFP4:
+        _need(w["w_gate"], "w_gate", torch.uint8, (E, f, d // 2), device)
+        _need(w["w_up"], "w_up", torch.uint8, (E, f, d // 2), device)
+        _need(w["w_down"], "w_down", torch.uint8, (E, d, f // 2), device)
+        for n, shape in (("s_gate", (E, f, d // 16)), ("s_up", (E, f, d // 16)), ("s_down", (E, d, f // 16))):
+            _need(w[n].view(torch.uint8), n, torch.uint8, shape, device)
+        for n in ("t_gate", "t_up", "t_down"):
+            _need(w[n], n, torch.float32, (E,), device)
+        return MoeExpertWeights(*(w[n].data_ptr() for n in
+                                  ("w_gate", "w_up", "w_down", "s_gate", "s_up", "s_down",
+                                   "t_gate", "t_up", "t_down")))
     if wfmt == MOE_DTYPE_MXFP4:
         _need(w["w_gate"], "w_gate", torch.uint8, (E, f, d // 2), device)
         _need(w["w_up"], "w_up", torch.uint8, (E, f, d // 2), device)
@@ -131,6 +143,8 @@ def _weights(w: dict, E, d, f, wfmt, device) -> MoeExpertWeights:
 
 
 def _wfmt(w: dict) -> int:
+    if w.get("t_gate") is not None:
+        return MOE_DTYPE_NVFP4
     if "s_gate" in w and w["s_gate"] is not None:
         return MOE_DTYPE_MXFP4
     return MOE_DTYPE_F32 if w["w_gate"].dtype == torch.float32 else MOE_DTYPE_BF16
@@ -138,7 +152,7 @@ def _wfmt(w: dict) -> int:
 
 def _wshape(w: dict, wfmt: int):
     E, f, dd = w["w_gate"].shape
-    return E, (dd * 2 if wfmt == MOE_DTYPE_MXFP4 else dd), f
+    return E, (dd * 2 if wfmt in (MOE_DTYPE_MXFP4, MOE_DTYPE_NVFP4) else dd), f
 
 
 def moe_workspace_size(T, d, E, k, f, act_dtype, w_dtype) -> int:

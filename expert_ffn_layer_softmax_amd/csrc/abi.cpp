@@ -107,13 +107,14 @@ moe_status_t check_dims(const moe_dims_t* d, Dims* out) {
   if (!d) return MOE_ERR_INVALID_ARGUMENT;
   if (d->T < 0 || d->d <= 0 || d->f <= 0 || d->E <= 0 || d->k <= 0) return MOE_ERR_INVALID_ARGUMENT;
   if (d->k > d->E) return MOE_ERR_INVALID_ARGUMENT;
-  if (d->act_dtype < 0 || d->act_dtype > 2 || d->w_dtype < 0 || d->w_dtype > 2)
+  if (d->act_dtype < 0 || d->act_dtype > 3 || d->w_dtype < 0 || d->w_dtype > 3)
     return MOE_ERR_INVALID_ARGUMENT;
   if (!routing_shape_ok(d->T, d->E, d->k)) return MOE_ERR_UNSUPPORTED;
   if (d->d % 32 != 0 || d->f % 32 != 0) return MOE_ERR_UNSUPPORTED;
   const bool pair_ok = (d->act_dtype == MOE_DTYPE_F32 && d->w_dtype == MOE_DTYPE_F32) ||
                        (d->act_dtype == MOE_DTYPE_BF16 && d->w_dtype == MOE_DTYPE_BF16) ||
-                       (d->act_dtype == MOE_DTYPE_BF16 && d->w_dtype == MOE_DTYPE_MXFP4);
+                       (d->act_dtype == MOE_DTYPE_BF16 && d->w_dtype == MOE_DTYPE_MXFP4) ||
+                       (d->act_dtype == MOE_DTYPE_BF16 && d->w_dtype == MOE_DTYPE_NVFP4);
   if (!pair_ok) return MOE_ERR_UNSUPPORTED;
   *out = Dims{d->T, d->d, d->E, d->k, d->f, d->act_dtype, d->w_dtype};
   return MOE_OK;
@@ -123,12 +124,22 @@ moe_status_t check_weights(const moe_expert_weights_t* w, const Dims& dm, Weight
   if (!w || !w->w_gate || !w->w_up || !w->w_down) return MOE_ERR_INVALID_ARGUMENT;
   if (!aligned16(w->w_gate) || !aligned16(w->w_up) || !aligned16(w->w_down))
     return MOE_ERR_INVALID_ARGUMENT;
-  if (dm.wfmt == kMXFP4) {
+  if (is_fp4(dm.wfmt)) {
     if (!w->s_gate || !w->s_up || !w->s_down) return MOE_ERR_INVALID_ARGUMENT;
+    if (!aligned16(w->s_gate) || !aligned16(w->s_up) || !aligned16(w->s_down))
+      return MOE_ERR_INVALID_ARGUMENT;
   } else if (w->s_gate || w->s_up || w->s_down) {
     return MOE_ERR_INVALID_ARGUMENT;
   }
-  *out = Weights{w->w_gate, w->w_up, w->w_down, w->s_gate, w->s_up, w->s_down};
+  if (dm.wfmt == kNVFP4) {
+    if (!w->t_gate || !w->t_up || !w->t_down) return MOE_ERR_INVALID_ARGUMENT;
+    if (!aligned16(w->t_gate) || !aligned16(w->t_up) || !aligned16(w->t_down))
+      return MOE_ERR_INVALID_ARGUMENT;
+  } else if (w->t_gate || w->t_up || w->t_down) {
+    return MOE_ERR_INVALID_ARGUMENT;
+  }
+  *out = Weights{w->w_gate, w->w_up, w->w_down, w->s_gate, w->s_up, w->s_down,
+                 w->t_gate, w->t_up, w->t_down};
   return MOE_OK;
 }
 

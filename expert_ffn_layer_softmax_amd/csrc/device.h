@@ -38,6 +38,16 @@ __device__ __forceinline__ float e8m0_to_f32(uint32_t s) {
   return __uint_as_float(bits);
 }
 
+// OCP FP8 E4M3 byte -> fp32, exactly: 1 sign, 4 exponent bits (bias 7),
+// 3 mantissa bits, subnormals m * 2^-9 at exponent 0.  The NaN bytes 0x7F and
+// 0xFF are outside the supported inputs (they decode to +-480 here).
+__device__ __forceinline__ float e4m3_to_f32(uint32_t b) {
+  const uint32_t e = (b >> 3) & 15u;
+  const uint32_t m = b & 7u;
+  const float v = (e == 0u) ? (float)m * 0.001953125f : __uint_as_float(((e + 120u) << 23) | (m << 20));
+  return (b & 0x80u) ? -v : v;
+}
+
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 
 // Two E2M1 codes in byte `sel` of `w` -> fp32 pair (low nibble first), by

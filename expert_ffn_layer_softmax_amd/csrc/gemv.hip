@@ -10,8 +10,10 @@
 // "Answer quality": bf16 partial sums cost accuracy).
 //
 // Work unit: one wave64 per RPW weight rows of one active expert.  A 16-byte
-// "chunk" of a row holds 4 fp32, 8 bf16 or 32 MX-FP4 codes (exactly one
-// 32-element scale block); lane l takes chunks l, l+64, ... so each load
+// "chunk" of a row holds 4 fp32, 8 bf16 or 32 4-bit codes (one MX-FP4 scale
+// block, two NVFP4 ones; the NVFP4 matrix scale multiplies each finished row
+// sum, as in the pages' own 4-bit format: SGLang-TorchTPU on TPU v7 page,
+// "Results"); lane l takes chunks l, l+64, ... so each load
 // instruction reads 1 KiB of contiguous row.  The weight loads are issued
 // right after one scalar lookup of the slot's (expert, rows) entry, before the
 // token indices are resolved, so the index chain overlaps the weight stream.
@@ -44,6 +46,19 @@ struct WT<kMXFP4> {
   static constexpr int XB = 64;
   __host__ __device__ static size_t row_bytes(int K) { return (size_t)K / 2; }
 };
+template <>
+struct WT<kNVFP4> {
+  static constexpr int CE = 32;
+  static constexpr int XB = 64;
+  __host__ __device__ static size_t row_bytes(int K) { return (size_t)K / 2; }
+};
+
+// Block-scale bytes per weight row: one E8M0 per 32 elements (MX-FP4), one
+// E4M3 per 16 (NVFP4, two per 16-byte chunk).
+template <int WF>
+constexpr size_t scale_row_bytes(int K) {
+  return WF == kMXFP4 ? (size_t)K / 32 : (WF == kNVFP4 ? (size_t)K / 16 : 0);
+}
 
 // Activations are fp32 with fp32 weights and bf16 otherwise.
 template <int WF>
@@ -54,8 +69,19 @@ struct XChunk {
   u32x4 v[WT<WF>::XB / 16];
 };
 
-// acc + <w, x> over one chunk.  For MX-FP4 the block scale is left out: the
-// caller multiplies the block's partial sum by it (one scale per chunk).
+// acc + <codes, x> for code word j of a 4-bit chunk (elements 8j..8j+7; byte
+// b holds elements 8j+2b, 8j+2b+1) and the matching activation vector j.
+__device__ __forceinline__ float fp4_word_dot(uint32_t cw_in, const u32x4& xv, float acc) {
+  const uint32_t cw = opaque(cw_in);
+  acc = dot2_bf16(fp4x2_to_bf16x2<0>(cw), xv.x, acc);
+  acc = dot2_bf16(fp4x2_to_bf16x2<1>(cw), xv.y, acc);
+  acc = dot2_bf16(fp4x2_to_bf16x2<2>(cw), xv.z, acc);
+  acc = dot2_bf16(fp4x2_to_bf16x2<3>(cw), xv.w, acc);
+  return acc;
+}
+
+// acc + <w, x> over one chunk.  For the 4-bit formats the block scales are
+// left out: scaled_chunk applies them to the partial sums.
 template <int WF>
 __device__ __forceinline__ float dot_chunk(const u32x4& w, const XChunk<WF>& x, float acc) {
   if constexpr (WF == kF32) {
@@ -69,19 +95,30 @@ __device__ __forceinline__ float dot_chunk(const u32x4& w, const XChunk<WF>& x, 
     acc = dot2_bf16(w.z, x.v[0].z, acc);
     acc = dot2_bf16(w.w, x.v[0].w, acc);
   } else {
-    // code word j holds elements 8j..8j+7 (byte b: elements 8j+2b, 8j+2b+1);
-    // activation vector j holds the same 8 elements as 4 bf16 pairs.
-    const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const uint32_t cw = opaque(ww[j]);
-      acc = dot2_bf16(fp4x2_to_bf16x2<0>(cw), x.v[j].x, acc);
-      acc = dot2_bf16(fp4x2_to_bf16x2<1>(cw), x.v[j].y, acc);
-      acc = dot2_bf16(fp4x2_to_bf16x2<2>(cw), x.v[j].z, acc);
-      acc = dot2_bf16(fp4x2_to_bf16x2<3>(cw), x.v[j].w, acc);
-    }
+    // activation vector j holds the 8 elements of code word j as 4 bf16 pairs
+    acc = fp4_word_dot(w.x, x.v[0], acc);
+    acc = fp4_word_dot(w.y, x.v[1], acc);
+    acc = fp4_word_dot(w.z, x.v[2], acc);
+    acc = fp4_word_dot(w.w, x.v[3], acc);
   }
   return acc;
+}
+
+// acc + the chunk's contribution with its block scales: MX-FP4 scales the
+// chunk's sum by s; NVFP4 scales elements 0..15 (words 0, 1) by s and 16..31
+// (words 2, 3) by s2; other formats have no block scale.
+template <int WF>
+__device__ __forceinline__ float scaled_chunk(const u32x4& w, const XChunk<WF>& x, float s, float s2,
+                                              float acc) {
+  if constexpr (WF == kMXFP4) {
+    return fmaf(dot_chunk<WF>(w, x, 0.f), s, acc);
+  } else if constexpr (WF == kNVFP4) {
+    const float lo = fp4_word_dot(w.y, x.v[1], fp4_word_dot(w.x, x.v[0], 0.f));
+    const float hi = fp4_word_dot(w.w, x.v[3], fp4_word_dot(w.z, x.v[2], 0.f));
+    return fmaf(hi, s2, fmaf(lo, s, acc));
+  } else {
+    return dot_chunk<WF>(w, x, acc);
+  }
 }
 
 template <int WF>
@@ -94,30 +131,50 @@ __device__ __forceinline__ void store_act(void* base, size_t i, float v) {
 
 __device__ __forceinline__ float silu(float z) { return z / (1.0f + expf(-z)); }
 
+// A row's finished sum times its matrix's fp32 scale (NVFP4 only).
+template <int WF>
+__device__ __forceinline__ float matrix_scaled(float v, const float* t, int e) {
+  if constexpr (WF == kNVFP4)
+    return v * t[e];
+  else
+    return v;
+}
+
 // Weight rows of RPW consecutive outputs, one segment, in registers.
 template <int WF, int MAXC, int RPW>
 struct RowRegs {
   u32x4 w[RPW][MAXC];
-  float s[RPW][MAXC];  // MX-FP4 block scales
-  uint32_t sw[RPW];    // MX-FP4: this lane's word of 4 scale bytes, until unpack()
+  float s[RPW][MAXC];   // 4-bit block scale (NVFP4: of elements 0..15)
+  float s2[RPW][MAXC];  // NVFP4: block scale of elements 16..31
+  uint32_t sw[RPW];     // this lane's scale word(s), until unpack()
+  uint32_t sw2[RPW];    // NVFP4: second word
   bool words;
 
-  // Issue the loads of chunks c = c0 + i*64 + lane (c < cend).  MX-FP4 block
-  // scales (one byte per chunk) are fetched four to a lane with 32-bit loads
-  // issued before the weight loads; unpack() hands them to the lanes that use
-  // them with a lane shuffle (byte loads per chunk would double the load
-  // instructions of the stream).
+  // Issue the loads of chunks c = c0 + i*64 + lane (c < cend).  Block scales
+  // (MX-FP4: one byte per chunk; NVFP4: two) are fetched with 4- or 8-byte
+  // loads covering four chunks per lane, issued before the weight loads;
+  // unpack() hands them to the lanes that use them with a lane shuffle (byte
+  // loads per chunk would double the load instructions of the stream).
   __device__ __forceinline__ void load(const char* row0, size_t rb, const uint8_t* s0, size_t sb,
                                        int nrows, int c0, int cend, int lane) {
-    words = (WF == kMXFP4) && ((sb & 3) == 0) && ((c0 & 3) == 0);
-    if constexpr (WF == kMXFP4) {
+    constexpr size_t SPC = WF == kNVFP4 ? 2 : 1;  // scale bytes per chunk
+    words = is_fp4(WF) && ((sb & (4 * SPC - 1)) == 0) && ((c0 & 3) == 0);
+    if constexpr (is_fp4(WF)) {
       if (words) {
-        const int q = (c0 >> 2) + lane;  // scale word of chunks 4q .. 4q+3
+        const int q = (c0 >> 2) + lane;  // scale word(s) of chunks 4q .. 4q+3
 #pragma unroll
         for (int r = 0; r < RPW; ++r) {
-          sw[r] = 0x7f7f7f7fu;
-          if (r < nrows && 4 * q < cend && lane < MAXC * 16)
-            sw[r] = *reinterpret_cast<const uint32_t*>(s0 + r * sb + 4 * (size_t)q);
+          sw[r] = sw2[r] = 0;
+          if (r < nrows && 4 * q < cend && lane < MAXC * 16) {
+            const uint8_t* sp = s0 + r * sb + 4 * SPC * (size_t)q;
+            if constexpr (WF == kNVFP4) {
+              const uint2 v = *reinterpret_cast<const uint2*>(sp);
+              sw[r] = v.x;
+              sw2[r] = v.y;
+            } else {
+              sw[r] = *reinterpret_cast<const uint32_t*>(sp);
+            }
+          }
         }
       }
     }
@@ -130,22 +187,36 @@ struct RowRegs {
           w[r][i] = ld_stream16(row0 + r * rb + (size_t)c * 16);
           if constexpr (WF == kMXFP4) {
             if (!words) s[r][i] = e8m0_to_f32(s0[r * sb + c]);
+          } else if constexpr (WF == kNVFP4) {
+            if (!words) {
+              s[r][i] = e4m3_to_f32(s0[r * sb + 2 * (size_t)c]);
+              s2[r][i] = e4m3_to_f32(s0[r * sb + 2 * (size_t)c + 1]);
+            }
           }
         }
       }
     }
   }
-  // Scales into s[][] (MX-FP4 word path).  Every lane of the wave must call.
+  // Scales into s[][] / s2[][] (word path).  Every lane of the wave must call.
   __device__ __forceinline__ void unpack(int lane) {
-    if constexpr (WF == kMXFP4) {
+    if constexpr (is_fp4(WF)) {
       if (words) {
 #pragma unroll
         for (int r = 0; r < RPW; ++r) {
 #pragma unroll
           for (int i = 0; i < MAXC; ++i) {
             const int cl = i * kWave + lane;  // chunk relative to c0
-            const uint32_t v = __shfl(sw[r], (cl >> 2) & (kWave - 1), kWave);
-            s[r][i] = e8m0_to_f32((v >> (8 * (cl & 3))) & 0xffu);
+            const int src = (cl >> 2) & (kWave - 1);
+            const uint32_t v = __shfl(sw[r], src, kWave);
+            if constexpr (WF == kMXFP4) {
+              s[r][i] = e8m0_to_f32((v >> (8 * (cl & 3))) & 0xffu);
+            } else {
+              const uint32_t v2 = __shfl(sw2[r], src, kWave);
+              const uint32_t word = (cl & 2) ? v2 : v;
+              const uint32_t sh = 16 * (cl & 1);
+              s[r][i] = e4m3_to_f32((word >> sh) & 0xffu);
+              s2[r][i] = e4m3_to_f32((word >> (sh + 8)) & 0xffu);
+            }
           }
         }
       }
@@ -155,6 +226,15 @@ struct RowRegs {
                                            int nrows, int c0, int cend, int lane) {
     load(row0, rb, s0, sb, nrows, c0, cend, lane);
     unpack(lane);
+  }
+  // acc + chunk i of row r with its block scales
+  __device__ __forceinline__ float fma_chunk(int r, int i, const XChunk<WF>& x, float acc) const {
+    if constexpr (WF == kNVFP4)
+      return scaled_chunk<WF>(w[r][i], x, s[r][i], s2[r][i], acc);
+    else if constexpr (WF == kMXFP4)
+      return scaled_chunk<WF>(w[r][i], x, s[r][i], 0.f, acc);
+    else
+      return scaled_chunk<WF>(w[r][i], x, 0.f, 0.f, acc);
   }
 };
 
@@ -172,6 +252,8 @@ struct GateUpArgs {
   const void* wu;
   const uint8_t* sg;
   const uint8_t* su;
+  const float* tg;  // NVFP4 matrix scales [E]
+  const float* tu;
   const int* sorted_src;
   const int* slot_info;
   const int* num_active;
@@ -207,12 +289,12 @@ __global__ __launch_bounds__(256) void gemv_gate_up_kernel(GateUpArgs a) {
   const int cbeg = part * cpp;
   const int cend = min(nchunks, cbeg + cpp);
   const size_t rb = WT<WF>::row_bytes(a.d);
-  const size_t sb = (size_t)a.d / 32;
+  const size_t sb = scale_row_bytes<WF>(a.d);
   const size_t woff = (size_t)e * a.f + min(n0, a.f - 1);
   const char* gp = reinterpret_cast<const char*>(a.wg) + woff * rb;
   const char* up = reinterpret_cast<const char*>(a.wu) + woff * rb;
-  const uint8_t* sgp = (WF == kMXFP4) ? a.sg + woff * sb : nullptr;
-  const uint8_t* sup = (WF == kMXFP4) ? a.su + woff * sb : nullptr;
+  const uint8_t* sgp = is_fp4(WF) ? a.sg + woff * sb : nullptr;
+  const uint8_t* sup = is_fp4(WF) ? a.su + woff * sb : nullptr;
 
   RowRegs<WF, MAXC, RPW> G, U;
   if (!MULTISEG) {  // whole (part of the) rows, loaded once, before the token chain
@@ -246,13 +328,8 @@ __global__ __launch_bounds__(256) void gemv_gate_up_kernel(GateUpArgs a) {
         if (c < cend) {
 #pragma unroll
           for (int r = 0; r < RPW; ++r) {
-            if constexpr (WF == kMXFP4) {
-              ag[r] = fmaf(dot_chunk<WF>(G.w[r][i], xc[i], 0.f), G.s[r][i], ag[r]);
-              au[r] = fmaf(dot_chunk<WF>(U.w[r][i], xc[i], 0.f), U.s[r][i], au[r]);
-            } else {
-              ag[r] = dot_chunk<WF>(G.w[r][i], xc[i], ag[r]);
-              au[r] = dot_chunk<WF>(U.w[r][i], xc[i], au[r]);
-            }
+            ag[r] = G.fma_chunk(r, i, xc[i], ag[r]);
+            au[r] = U.fma_chunk(r, i, xc[i], au[r]);
           }
         }
       }
@@ -261,8 +338,8 @@ __global__ __launch_bounds__(256) void gemv_gate_up_kernel(GateUpArgs a) {
 #pragma unroll
       for (int r = 0; r < RPW; ++r) {
         if (r < nrows) {
-          const float gs = wave_sum(ag[r]);
-          const float us = wave_sum(au[r]);
+          const float gs = matrix_scaled<WF>(wave_sum(ag[r]), a.tg, e);
+          const float us = matrix_scaled<WF>(wave_sum(au[r]), a.tu, e);
           if (lane == 0) store_act<WF>(a.h, (size_t)(r0 + tt) * a.f + n0 + r, silu(gs) * us);
         }
       }
@@ -310,12 +387,12 @@ __global__ __launch_bounds__(256) void gemv_gate_up_t1_rows_kernel(GateUpArgs a)
   const int nrows = min(R, a.f - n0);
   const int nchunks = a.d / CE;
   const size_t rb = WT<WF>::row_bytes(a.d);
-  const size_t sb = (size_t)a.d / 32;
+  const size_t sb = scale_row_bytes<WF>(a.d);
   const size_t woff = (size_t)e * a.f + n0;
   const char* gp = reinterpret_cast<const char*>(a.wg) + woff * rb;
   const char* up = reinterpret_cast<const char*>(a.wu) + woff * rb;
-  const uint8_t* sgp = (WF == kMXFP4) ? a.sg + woff * sb : nullptr;
-  const uint8_t* sup = (WF == kMXFP4) ? a.su + woff * sb : nullptr;
+  const uint8_t* sgp = is_fp4(WF) ? a.sg + woff * sb : nullptr;
+  const uint8_t* sup = is_fp4(WF) ? a.su + woff * sb : nullptr;
 
   RowRegs<WF, MAXC, 1> G[2], U[2];
   G[0].load(gp, rb, sgp, sb, 1, 0, nchunks, lane);
@@ -344,17 +421,12 @@ __global__ __launch_bounds__(256) void gemv_gate_up_t1_rows_kernel(GateUpArgs a)
       for (int i = 0; i < MAXC; ++i) {
         const int c = i * kWave + lane;
         if (c < nchunks) {
-          if constexpr (WF == kMXFP4) {
-            ag = fmaf(dot_chunk<WF>(G[cur].w[0][i], xc[i], 0.f), G[cur].s[0][i], ag);
-            au = fmaf(dot_chunk<WF>(U[cur].w[0][i], xc[i], 0.f), U[cur].s[0][i], au);
-          } else {
-            ag = dot_chunk<WF>(G[cur].w[0][i], xc[i], ag);
-            au = dot_chunk<WF>(U[cur].w[0][i], xc[i], au);
-          }
+          ag = G[cur].fma_chunk(0, i, xc[i], ag);
+          au = U[cur].fma_chunk(0, i, xc[i], au);
         }
       }
-      const float gs = wave_sum(ag);
-      const float us = wave_sum(au);
+      const float gs = matrix_scaled<WF>(wave_sum(ag), a.tg, e);
+      const float us = matrix_scaled<WF>(wave_sum(au), a.tu, e);
       if (lane == 0) store_act<WF>(a.h, (size_t)r0 * a.f + n0 + r, silu(gs) * us);
     }
   }
@@ -364,6 +436,7 @@ struct DownArgs {
   const void* h;
   const void* wd;
   const uint8_t* sd;
+  const float* td;  // NVFP4 matrix scales [E]
   const int* slot_info;
   const int* num_active;
   float* y_sorted;
@@ -387,10 +460,10 @@ __global__ __launch_bounds__(256) void gemv_down_kernel(DownArgs a) {
   const int nrows = min(RPW, a.d - n0);
   const int nchunks = a.f / CE;
   const size_t rb = WT<WF>::row_bytes(a.f);
-  const size_t sb = (size_t)a.f / 32;
+  const size_t sb = scale_row_bytes<WF>(a.f);
   const size_t woff = (size_t)e * a.d + n0;
   const char* wp = reinterpret_cast<const char*>(a.wd) + woff * rb;
-  const uint8_t* sp = (WF == kMXFP4) ? a.sd + woff * sb : nullptr;
+  const uint8_t* sp = is_fp4(WF) ? a.sd + woff * sb : nullptr;
 
   RowRegs<WF, MAXC, RPW> W;
   if (!MULTISEG) W.load_all(wp, rb, sp, sb, nrows, 0, nchunks, lane);
@@ -417,19 +490,14 @@ __global__ __launch_bounds__(256) void gemv_down_kernel(DownArgs a) {
         const int c = c0 + i * kWave + lane;
         if (c < nchunks) {
 #pragma unroll
-          for (int r = 0; r < RPW; ++r) {
-            if constexpr (WF == kMXFP4)
-              acc[r] = fmaf(dot_chunk<WF>(W.w[r][i], hc[i], 0.f), W.s[r][i], acc[r]);
-            else
-              acc[r] = dot_chunk<WF>(W.w[r][i], hc[i], acc[r]);
-          }
+          for (int r = 0; r < RPW; ++r) acc[r] = W.fma_chunk(r, i, hc[i], acc[r]);
         }
       }
     }
 #pragma unroll
     for (int r = 0; r < RPW; ++r) {
       if (r < nrows) {
-        const float y = wave_sum(acc[r]);
+        const float y = matrix_scaled<WF>(wave_sum(acc[r]), a.td, e);
         if (lane == 0) a.y_sorted[(size_t)(r0 + tt) * a.d + n0 + r] = y;
       }
     }
@@ -440,6 +508,7 @@ struct DownCombineArgs {
   const void* h;
   const void* wd;
   const uint8_t* sd;
+  const float* td;
   const int* topk_idx;
   const float* topk_w;
   const int* dest_row;
@@ -462,11 +531,11 @@ __global__ __launch_bounds__(NTH) void gemv_down_combine_t1_kernel(DownCombineAr
   const int e = a.topk_idx[j];
   const int nchunks = a.f / CE;
   const size_t rb = WT<WF>::row_bytes(a.f);
-  const size_t sb = (size_t)a.f / 32;
+  const size_t sb = scale_row_bytes<WF>(a.f);
   const size_t woff = (size_t)e * a.d + n0;
   RowRegs<WF, MAXC, RPW> W;
   W.load_all(reinterpret_cast<const char*>(a.wd) + woff * rb, rb,
-             (WF == kMXFP4) ? a.sd + woff * sb : nullptr, sb, nrows, 0, nchunks, lane);
+             is_fp4(WF) ? a.sd + woff * sb : nullptr, sb, nrows, 0, nchunks, lane);
   const char* hr =
       reinterpret_cast<const char*>(a.h) + (size_t)a.dest_row[j] * a.f * act_bytes<WF>();
   XChunk<WF> hc[MAXC];
@@ -483,17 +552,12 @@ __global__ __launch_bounds__(NTH) void gemv_down_combine_t1_kernel(DownCombineAr
     const int c = i * kWave + lane;
     if (c < nchunks) {
 #pragma unroll
-      for (int r = 0; r < RPW; ++r) {
-        if constexpr (WF == kMXFP4)
-          acc[r] = fmaf(dot_chunk<WF>(W.w[r][i], hc[i], 0.f), W.s[r][i], acc[r]);
-        else
-          acc[r] = dot_chunk<WF>(W.w[r][i], hc[i], acc[r]);
-      }
+      for (int r = 0; r < RPW; ++r) acc[r] = W.fma_chunk(r, i, hc[i], acc[r]);
     }
   }
 #pragma unroll
   for (int r = 0; r < RPW; ++r) {
-    const float y = wave_sum(acc[r]);
+    const float y = matrix_scaled<WF>(wave_sum(acc[r]), a.td, e);
     if (lane == 0) ys[j][r] = y;
   }
   __syncthreads();
@@ -506,20 +570,20 @@ __global__ __launch_bounds__(NTH) void gemv_down_combine_t1_kernel(DownCombineAr
 }
 
 // ---------------------------------------------------------------- launch --
-int chunk_elems(int wf) { return wf == kF32 ? 4 : (wf == kBF16 ? 8 : 32); }
+int chunk_elems(int wf) { return wf == kF32 ? 4 : (wf == kBF16 ? 8 : 32); }  // 4-bit: 32
 
 // Registers per lane for one row: the smallest supported MAXC covering the
-// row (MX-FP4 capped at 4: each chunk needs 64 B of activations).
+// row (4-bit formats capped at 4: each chunk needs 64 B of activations).
 int pick_maxc(int nchunks, int wf) {
   const int need = (nchunks + kWave - 1) / kWave;
   static const int opts[] = {1, 2, 3, 4, 6, 8, 12, 16};
-  const int cap = wf == kMXFP4 ? 4 : 16;
+  const int cap = is_fp4(wf) ? 4 : 16;
   for (int o : opts)
     if (need <= o && o <= cap) return o;
   return cap;
 }
 
-// Rows walked per wave by the single-token MX-FP4 gate/up kernel.
+// Rows walked per wave by the single-token 4-bit gate/up kernel.
 constexpr int kT1Rows = 8;
 
 // Rows per wave so that a wave keeps about 12 chunks per matrix in flight.
@@ -532,10 +596,10 @@ constexpr int rpw_t1_small(int maxc) { return maxc <= 2 ? 8 : rpw_for(maxc); }
     case 2: { constexpr int MC = 2; CALL; } break;                                    \
     case 3: { constexpr int MC = 3; CALL; } break;                                    \
     case 4: { constexpr int MC = 4; CALL; } break;                                    \
-    case 6: { if constexpr (WFV != kMXFP4) { constexpr int MC = 6; CALL; } } break;   \
-    case 8: { if constexpr (WFV != kMXFP4) { constexpr int MC = 8; CALL; } } break;   \
-    case 12: { if constexpr (WFV != kMXFP4) { constexpr int MC = 12; CALL; } } break; \
-    default: { if constexpr (WFV != kMXFP4) { constexpr int MC = 16; CALL; } } break; \
+    case 6: { if constexpr (!is_fp4(WFV)) { constexpr int MC = 6; CALL; } } break;   \
+    case 8: { if constexpr (!is_fp4(WFV)) { constexpr int MC = 8; CALL; } } break;   \
+    case 12: { if constexpr (!is_fp4(WFV)) { constexpr int MC = 12; CALL; } } break; \
+    default: { if constexpr (!is_fp4(WFV)) { constexpr int MC = 16; CALL; } } break; \
   }
 
 #define MOE_MAXC12_SWITCH(WFV, MAXC, CALL)                                            \
@@ -543,17 +607,18 @@ constexpr int rpw_t1_small(int maxc) { return maxc <= 2 ? 8 : rpw_for(maxc); }
     case 1: { constexpr int MC = 1; CALL; } break;                                    \
     case 2: { constexpr int MC = 2; CALL; } break;                                    \
     case 3: { constexpr int MC = 3; CALL; } break;                                    \
-    case 4: { if constexpr (WFV != kMXFP4) { constexpr int MC = 4; CALL; } } break;   \
-    case 6: { if constexpr (WFV != kMXFP4) { constexpr int MC = 6; CALL; } } break;   \
-    case 8: { if constexpr (WFV != kMXFP4) { constexpr int MC = 8; CALL; } } break;   \
-    default: { if constexpr (WFV != kMXFP4) { constexpr int MC = 12; CALL; } } break; \
+    case 4: { if constexpr (!is_fp4(WFV)) { constexpr int MC = 4; CALL; } } break;   \
+    case 6: { if constexpr (!is_fp4(WFV)) { constexpr int MC = 6; CALL; } } break;   \
+    case 8: { if constexpr (!is_fp4(WFV)) { constexpr int MC = 8; CALL; } } break;   \
+    default: { if constexpr (!is_fp4(WFV)) { constexpr int MC = 12; CALL; } } break; \
   }
 
-#define MOE_WF_SWITCH(WFV, CALL)                          \
-  switch (WFV) {                                          \
-    case kF32: { constexpr int WF = kF32; CALL; } break;   \
-    case kBF16: { constexpr int WF = kBF16; CALL; } break; \
-    default: { constexpr int WF = kMXFP4; CALL; } break;   \
+#define MOE_WF_SWITCH(WFV, CALL)                             \
+  switch (WFV) {                                             \
+    case kF32: { constexpr int WF = kF32; CALL; } break;      \
+    case kBF16: { constexpr int WF = kBF16; CALL; } break;    \
+    case kMXFP4: { constexpr int WF = kMXFP4; CALL; } break;  \
+    default: { constexpr int WF = kNVFP4; CALL; } break;      \
   }
 
 #define MOE_SEG_SWITCH(MULTI, CALL)                 \
@@ -565,13 +630,13 @@ constexpr int rpw_t1_small(int maxc) { return maxc <= 2 ? 8 : rpw_for(maxc); }
 hipError_t launch_gemv_gate_up(const Dims& dm, const void* x, const Plan& p, const Weights& w,
                                void* h, hipStream_t s) {
   LaunchTimer tm("gemv_gate_up", s);
-  GateUpArgs a{x, w.wg, w.wu, w.sg, w.su, p.sorted_src, p.slot_info, p.num_active, h,
-               dm.d, dm.f, dm.k};
+  GateUpArgs a{x, w.wg, w.wu, w.sg, w.su, w.tg, w.tu, p.sorted_src, p.slot_info, p.num_active,
+               h, dm.d, dm.f, dm.k};
   const long long max_active = dm.Tk() < dm.E ? dm.Tk() : dm.E;
   const int nchunks = dm.d / chunk_elems(dm.wfmt);
   const int maxc = pick_maxc(nchunks, dm.wfmt);
   const bool multi = nchunks > maxc * kWave;
-  if (!multi && dm.wfmt != kMXFP4 && maxc >= 8) {
+  if (!multi && !is_fp4(dm.wfmt) && maxc >= 8) {
     // long rows: two waves per row, each streaming half of it
     const int maxc2 = pick_maxc((nchunks + 1) / 2, dm.wfmt);
     const dim3 grid((unsigned)(max_active * ((dm.f + 1) / 2))), block(256);
@@ -586,15 +651,22 @@ hipError_t launch_gemv_gate_up(const Dims& dm, const void* x, const Plan& p, con
     }
     return hipGetLastError();
   }
-  if (dm.T == 1 && dm.wfmt == kMXFP4 && !multi) {
+  if (dm.T == 1 && is_fp4(dm.wfmt) && !multi) {
     // short rows: each wave walks kT1Rows rows with the next row in flight
     const dim3 grid((unsigned)(max_active * ((dm.f + 4 * kT1Rows - 1) / (4 * kT1Rows)))), block(256);
-    switch (maxc) {
-      case 1: gemv_gate_up_t1_rows_kernel<kMXFP4, 1, kT1Rows><<<grid, block, 0, s>>>(a); break;
-      case 2: gemv_gate_up_t1_rows_kernel<kMXFP4, 2, kT1Rows><<<grid, block, 0, s>>>(a); break;
-      case 3: gemv_gate_up_t1_rows_kernel<kMXFP4, 3, kT1Rows><<<grid, block, 0, s>>>(a); break;
-      default: gemv_gate_up_t1_rows_kernel<kMXFP4, 4, kT1Rows><<<grid, block, 0, s>>>(a); break;
+#define MOE_T1ROWS(WFV)                                                                          \
+  switch (maxc) {                                                                                \
+    case 1: gemv_gate_up_t1_rows_kernel<WFV, 1, kT1Rows><<<grid, block, 0, s>>>(a); break;       \
+    case 2: gemv_gate_up_t1_rows_kernel<WFV, 2, kT1Rows><<<grid, block, 0, s>>>(a); break;       \
+    case 3: gemv_gate_up_t1_rows_kernel<WFV, 3, kT1Rows><<<grid, block, 0, s>>>(a); break;       \
+    default: gemv_gate_up_t1_rows_kernel<WFV, 4, kT1Rows><<<grid, block, 0, s>>>(a); break;      \
+  }
+    if (dm.wfmt == kMXFP4) {
+      MOE_T1ROWS(kMXFP4)
+    } else {
+      MOE_T1ROWS(kNVFP4)
     }
+#undef MOE_T1ROWS
     return hipGetLastError();
   }
   const int rpw = rpw_for(maxc);
@@ -607,7 +679,7 @@ hipError_t launch_gemv_gate_up(const Dims& dm, const void* x, const Plan& p, con
 hipError_t launch_gemv_down(const Dims& dm, const void* h, const Plan& p, const Weights& w,
                             float* y_sorted, hipStream_t s) {
   LaunchTimer tm("gemv_down", s);
-  DownArgs a{h, w.wd, w.sd, p.slot_info, p.num_active, y_sorted, dm.d, dm.f};
+  DownArgs a{h, w.wd, w.sd, w.td, p.slot_info, p.num_active, y_sorted, dm.d, dm.f};
   const long long max_active = dm.Tk() < dm.E ? dm.Tk() : dm.E;
   const int nchunks = dm.f / chunk_elems(dm.wfmt);
   const int maxc = pick_maxc(nchunks, dm.wfmt);
@@ -624,7 +696,7 @@ bool gemv_down_combine_t1_ok(const Dims& dm) {
   // enough that the weight registers fit without spilling
   const int nchunks = dm.f / chunk_elems(dm.wfmt);
   const int maxc = pick_maxc(nchunks, dm.wfmt);
-  const int limit = dm.wfmt == kMXFP4 ? 3 : 12;
+  const int limit = is_fp4(dm.wfmt) ? 3 : 12;
   return dm.T == 1 && dm.k <= 16 && nchunks <= maxc * kWave && maxc <= limit;
 }
 
@@ -632,7 +704,7 @@ hipError_t launch_gemv_down_combine_t1(const Dims& dm, const void* h, const Plan
                                        const int* topk_idx, const float* topk_w,
                                        const Weights& w, void* out, hipStream_t s) {
   LaunchTimer tm("gemv_down_combine_t1", s);
-  DownCombineArgs a{h, w.wd, w.sd, topk_idx, topk_w, p.dest_row, out, dm.d, dm.f, dm.k};
+  DownCombineArgs a{h, w.wd, w.sd, w.td, topk_idx, topk_w, p.dest_row, out, dm.d, dm.f, dm.k};
   const int maxc = pick_maxc(dm.f / chunk_elems(dm.wfmt), dm.wfmt);
   const dim3 block(64 * dm.k);
   if (dm.k <= 8) {  // 512-thread blocks: up to 256 registers, twice the short rows per wave

@@ -59,8 +59,10 @@ struct GGArgs {
   const int* sorted_src;  // gate/up: row r reads x[sorted_src[r] / k]
   const void* w0;         // gate/up: W_gate; down: W_down   ([E][N][K] or codes)
   const void* w1;         // gate/up: W_up
-  const uint8_t* s0;      // MX-FP4 scales of w0 / w1
+  const uint8_t* s0;      // 4-bit block scales of w0 / w1
   const uint8_t* s1;
+  const float* t0;        // NVFP4 matrix scales [E] of w0 / w1
+  const float* t1;
   const int* mtiles;
   const int* num_mtiles;
   void* out;              // gate/up: h bf16 [T*k][N]; down: y_sorted fp32 [T*k][N]
@@ -501,7 +503,7 @@ __global__ __launch_bounds__(kThreads) void gg_dma_kernel(GGArgs a) {
   }
 }
 
-// ---- MX-FP4 weights, cache-line groups of codes in LDS.
+// ---- 4-bit weights (MX-FP4 or NVFP4), cache-line groups of codes in LDS.
 //
 // A weight row's codes for one K-step are 32 bytes, a quarter of a 128-byte
 // line; fetched step by step, a line is needed again three steps later, by
@@ -511,8 +513,11 @@ __global__ __launch_bounds__(kThreads) void gg_dma_kernel(GGArgs a) {
 // weight rows x 128 bytes (whole lines, 8 lanes per line), a group of 256
 // weight rows x 4 steps is 32 KB, and three group buffers let a group be
 // issued two groups ahead of its use, one instruction per wave per step.  The
-// block scales of a group (8 bytes per weight row) arrive with one 4-byte
-// DMA per lane at the group's first step.  The activation tile and the
+// block scales of a group (MX-FP4: 8 E8M0 bytes per weight row; NVFP4: 16
+// E4M3 bytes) arrive with one or two 4-byte DMAs per lane at the group's first
+// step, and the NVFP4 matrix scale multiplies the accumulators in the
+// epilogue (E2M1 x E4M3 is exact in bf16, and is formed in fp32: the scaled
+// convert only takes powers of two).  The activation tile and the
 // 2 x 4 wave grid are those of gg_dma_kernel (64 rows x two 32-column
 // operands per wave, wave-local SwiGLU); codes are converted to bf16 (scale
 // applied by the instruction) just before their MFMAs.
@@ -524,26 +529,81 @@ __global__ __launch_bounds__(kThreads) void gg_dma_kernel(GGArgs a) {
 constexpr int kGroupSteps = 4;
 constexpr int kGroupBufs = 3;
 constexpr int kCodesGroup = BN * 128;                 // 32 KB: 256 weight rows x one line
-constexpr int kScalesGroup = BN * 8;                  // 2 KB
 constexpr int kMx4A = 3;                              // activation stages
-constexpr int kMx4Lds = kMx4A * kStageA + kGroupBufs * (kCodesGroup + kScalesGroup);
 constexpr int kCodeDmaPerStep = kCodesGroup / (kWave * 16) / kWaves / kGroupSteps;  // 1
 static_assert(kCodeDmaPerStep == 1, "one code DMA per wave per step");
-static_assert(kScalesGroup == kWaves * kWave * 4, "one scale DMA per wave per group");
+
+// Scale bytes per weight row per group, and the group's scale DMAs per wave.
+template <int WF>
+struct GroupScales {
+  static constexpr int kBytesPerRow = WF == kNVFP4 ? 16 : 8;
+  static constexpr int kBytes = BN * kBytesPerRow;
+  static constexpr int kDmas = kBytes / (kWaves * kWave * 4);
+  static constexpr int kLds = kMx4A * kStageA + kGroupBufs * (kCodesGroup + kBytes);
+  static_assert(kDmas * kWaves * kWave * 4 == kBytes, "whole scale DMAs");
+};
+
+// A lane's 4-bit operand for one K-step: its 32-element block of codes per
+// matrix and the scales of the block's halves (equal for MX-FP4).
+struct Fp4Regs {
+  u32x4 v[2];
+  float lo[2], hi[2];
+};
+
+// Two E2M1 codes (byte SEL of w) times an NVFP4 block scale, as a packed bf16
+// pair.  The gfx950 scaled convert applies only the exponent of its fp32
+// scale (checked on the device: scale 1.5 multiplies by 1), which suits the
+// E8M0 scales of MX-FP4 but not E4M3, so the product is formed in fp32.  It
+// has at most 6 significant bits (E2M1: 2, E4M3: 4), so the upper half of its
+// fp32 bits is the exact bf16 value.
+template <int SEL>
+__device__ __forceinline__ uint32_t fp4x2_times(uint32_t w, float sc) {
+  auto f = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, SEL);
+  const uint32_t lo = __float_as_uint(f[0] * sc);
+  const uint32_t hi = __float_as_uint(f[1] * sc);
+  return __builtin_amdgcn_perm(hi, lo, 0x07060302u);  // {hi[31:16], lo[31:16]}
+}
+
+// bf16 fragment for substep s of matrix m: code word s holds elements
+// 8s..8s+7, so words 0 and 1 take the first half's scale.
+template <int WF>
+__device__ __forceinline__ bf16x8_t fp4_frag(const Fp4Regs& b, int m, int s) {
+  const uint32_t w = b.v[m][s];
+  const float sc = s < 2 ? b.lo[m] : b.hi[m];
+  u32x4 r;
+  if constexpr (WF == kNVFP4) {
+    r.x = fp4x2_times<0>(w, sc);
+    r.y = fp4x2_times<1>(w, sc);
+    r.z = fp4x2_times<2>(w, sc);
+    r.w = fp4x2_times<3>(w, sc);
+  } else {  // E8M0: a power of two, applied by the instruction
+    r.x = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, sc, 0));
+    r.y = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, sc, 1));
+    r.z = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, sc, 2));
+    r.w = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, sc, 3));
+  }
+  return __builtin_bit_cast(bf16x8_t, r);
+}
 
 // MFMAs of one K-step for the VM valid row sub-tiles of this wave.  `cb` and
 // `sb` are the group's code and scale buffers, p the step's place in it.
-template <int VM>
+template <int WF, int VM>
 __device__ __forceinline__ void mx4_step(const char* st, const char* cb, const char* sb, int p,
                                          const int* aoff, const int* brow, int half,
                                          f32x16_t (&acc)[2][2]) {
   if constexpr (VM > 0) {
-    BRegs<kMXFP4> b;
+    Fp4Regs b;
 #pragma unroll
     for (int m = 0; m < 2; ++m) {
       const int u = 2 * p + half;  // the lane's 32-element block inside the line
       b.v[m] = *reinterpret_cast<const u32x4*>(cb + brow[m] * 128 + ((u ^ (brow[m] & 7)) << 4));
-      b.s[m] = static_cast<uint8_t>(sb[brow[m] * 8 + u]);
+      if constexpr (WF == kNVFP4) {
+        const uint8_t* q = reinterpret_cast<const uint8_t*>(sb) + brow[m] * 16 + 2 * u;
+        b.lo[m] = e4m3_to_f32(q[0]);
+        b.hi[m] = e4m3_to_f32(q[1]);
+      } else {
+        b.lo[m] = b.hi[m] = e8m0_to_f32(static_cast<uint8_t>(sb[brow[m] * 8 + u]));
+      }
     }
     bf16x8_t af[2][2];
 #pragma unroll
@@ -555,8 +615,8 @@ __device__ __forceinline__ void mx4_step(const char* st, const char* cb, const c
         for (int mi = 0; mi < VM; ++mi)
           af[(s + 1) & 1][mi] = *reinterpret_cast<const bf16x8_t*>(st + aoff[4 * mi + s + 1]);
       }
-      const bf16x8_t b0 = b_frag<kMXFP4>(b, 0, s);
-      const bf16x8_t b1 = b_frag<kMXFP4>(b, 1, s);
+      const bf16x8_t b0 = fp4_frag<WF>(b, 0, s);
+      const bf16x8_t b1 = fp4_frag<WF>(b, 1, s);
 #pragma unroll
       for (int mi = 0; mi < VM; ++mi) {
         acc[0][mi] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[s & 1][mi], b0, acc[0][mi], 0, 0, 0);
@@ -566,9 +626,10 @@ __device__ __forceinline__ void mx4_step(const char* st, const char* cb, const c
   }
 }
 
-template <bool GATEUP>
+template <int WF, bool GATEUP>
 __global__ __launch_bounds__(kThreads) void gg_mx_group_kernel(GGArgs a) {
-  __shared__ __align__(1024) char lds[kMx4Lds];
+  using GS = GroupScales<WF>;
+  __shared__ __align__(1024) char lds[GS::kLds];
   char* const lds_a = lds;
   char* const lds_c = lds + kMx4A * kStageA;
   char* const lds_s = lds_c + kGroupBufs * kCodesGroup;
@@ -613,7 +674,7 @@ __global__ __launch_bounds__(kThreads) void gg_mx_group_kernel(GGArgs a) {
     }
     col = min(col, a.N - 1);
     code = reinterpret_cast<const char*>(w) + ((size_t)e * a.N + col) * (a.K / 2);
-    scale = sc + ((size_t)e * a.N + col) * (a.K / 32);
+    scale = sc + ((size_t)e * a.N + col) * ((size_t)a.K / 256 * GS::kBytesPerRow);
   };
 
   // ---- activation DMA sources (see gg_dma_kernel)
@@ -641,14 +702,17 @@ __global__ __launch_bounds__(kThreads) void gg_mx_group_kernel(GGArgs a) {
     wrow(r, code, scale);
     csrc[p] = code + ((slot16 ^ (r & 7)) << 4);
   }
-  // ---- scale DMA source: dword lane of wave w covers weight row (64 w +
-  // lane) / 2, bytes 4 ((64 w + lane) % 2) .. +3 of the group's 8
-  const uint8_t* ssrc;
-  {
-    const int d = kWave * wave + lane;
+  // ---- scale DMA sources: dword d = 64 (kDmas w + i) + lane of the group
+  // covers weight row d / W, bytes 4 (d % W) .. +3 of the row's group bytes
+  // (W = words per row)
+  constexpr int W = GS::kBytesPerRow / 4;
+  const uint8_t* ssrc[GS::kDmas];
+#pragma unroll
+  for (int i = 0; i < GS::kDmas; ++i) {
+    const int d = kWave * (GS::kDmas * wave + i) + lane;
     const char* code;
-    wrow(d >> 1, code, ssrc);
-    ssrc += 4 * (d & 1);
+    wrow(d / W, code, ssrc[i]);
+    ssrc[i] += 4 * (d % W);
   }
   const int nk = a.K / BK;
   const int ng = nk / kGroupSteps;
@@ -661,8 +725,11 @@ __global__ __launch_bounds__(kThreads) void gg_mx_group_kernel(GGArgs a) {
     dma16<0>(csrc[p] + (size_t)min(g, ng - 1) * 128, d);
   };
   auto issue_scales = [&](int g) {
-    char* d = lds_s + (g % kGroupBufs) * kScalesGroup + wave * kWave * 4;
-    __builtin_amdgcn_global_load_lds(ssrc + (size_t)min(g, ng - 1) * 8, (lds_void_t*)d, 4, 0, 0);
+    char* d = lds_s + (g % kGroupBufs) * GS::kBytes + GS::kDmas * wave * kWave * 4;
+    const size_t go = (size_t)min(g, ng - 1) * GS::kBytesPerRow;
+#pragma unroll
+    for (int i = 0; i < GS::kDmas; ++i)
+      __builtin_amdgcn_global_load_lds(ssrc[i] + go, (lds_void_t*)(d + i * kWave * 4), 4, 0, 0);
   };
   auto issue_a = [&](int kk) {
     char* d = adst + (kk % kMx4A) * kStageA;
@@ -703,14 +770,15 @@ __global__ __launch_bounds__(kThreads) void gg_mx_group_kernel(GGArgs a) {
     constexpr int VM = decltype(vm_c)::value;
     for (int g = 0; g < ng; ++g) {
       const char* cb = lds_c + (g % kGroupBufs) * kCodesGroup;
-      const char* sb = lds_s + (g % kGroupBufs) * kScalesGroup;
+      const char* sb = lds_s + (g % kGroupBufs) * GS::kBytes;
 #pragma unroll
       for (int p = 0; p < kGroupSteps; ++p) {
         const int kk = kGroupSteps * g + p;
         // loads younger than activation stage kk: those of step kk-1 (three,
-        // four after a group's first step); at step 0 only stage 1's two
+        // three plus the scale DMAs after a group's first step); at step 0
+        // only stage 1's two
         if (p == 1)
-          wait_and_barrier<4>();
+          wait_and_barrier<3 + GS::kDmas>();
         else if (p == 0)
           wait_and_barrier<2>();
         else
@@ -719,7 +787,7 @@ __global__ __launch_bounds__(kThreads) void gg_mx_group_kernel(GGArgs a) {
         if (p == 0) issue_scales(g + 2);
         asm volatile("" ::: "memory");  // activation DMAs are the step's youngest loads
         issue_a(kk + 2);
-        mx4_step<VM>(lds_a + (kk % kMx4A) * kStageA, cb, sb, p, aoff, brow, half, acc);
+        mx4_step<WF, VM>(lds_a + (kk % kMx4A) * kStageA, cb, sb, p, aoff, brow, half, acc);
       }
     }
   };
@@ -732,7 +800,16 @@ __global__ __launch_bounds__(kThreads) void gg_mx_group_kernel(GGArgs a) {
   // the clamped loads past the end must land before the block's LDS is released
   __builtin_amdgcn_s_waitcnt(0);
 
-  // ---- epilogue (as gg_dma_kernel)
+  // ---- epilogue (as gg_dma_kernel, after the NVFP4 matrix scales)
+  if constexpr (WF == kNVFP4) {
+    const float t0 = a.t0[e];
+    const float t1 = GATEUP ? a.t1[e] : t0;
+#pragma unroll
+    for (int mi = 0; mi < 2; ++mi) {
+      acc[0][mi] *= t0;
+      acc[1][mi] *= t1;
+    }
+  }
 #pragma unroll
   for (int mi = 0; mi < 2; ++mi) {
     if (mi < vm) {
@@ -764,14 +841,15 @@ __global__ __launch_bounds__(kThreads) void gg_mx_group_kernel(GGArgs a) {
 // K-steps of loads in flight (register budget of two waves per SIMD).
 constexpr int kDepthDirect = 2;  // gg_direct_b_kernel, MX-FP4 weights
 
-// MX-FP4 GEMMs whose K (d for gate/up, f for down) holds whole code groups
-// use gg_mx_group_kernel; others fall back to gg_direct_b_kernel.
+// 4-bit GEMMs whose K (d for gate/up, f for down) holds whole code groups
+// use gg_mx_group_kernel; other MX-FP4 GEMMs fall back to gg_direct_b_kernel
+// (NVFP4 layers with such K take the GEMV path).
 bool mx_grouped(int K) { return K % (kGroupSteps * BK) == 0; }
 
 // Output columns per tile: gate/up counts columns of each of W_gate, W_up.
 int tile_cols(const Dims& dm, bool gateup) {
   const int K = gateup ? dm.d : dm.f;
-  const int base = (dm.wfmt == kMXFP4 && !mx_grouped(K)) ? 256 : 128;
+  const int base = (dm.wfmt == kMXFP4 && !mx_grouped(K)) ? 256 : 128;  // direct-B: 256
   return gateup ? base : 2 * base;
 }
 
@@ -779,8 +857,10 @@ template <bool GATEUP>
 hipError_t launch_gg(const Dims& dm, const GGArgs& a, hipStream_t s) {
   const size_t max_tiles = grouped_gemm_max_mtiles(dm) * (size_t)a.ntiles;
   const dim3 grid((unsigned)((max_tiles + kXcds - 1) / kXcds * kXcds)), block(kThreads);
-  if (dm.wfmt == kMXFP4 && mx_grouped(a.K))
-    gg_mx_group_kernel<GATEUP><<<grid, block, 0, s>>>(a);
+  if (dm.wfmt == kNVFP4)
+    gg_mx_group_kernel<kNVFP4, GATEUP><<<grid, block, 0, s>>>(a);
+  else if (dm.wfmt == kMXFP4 && mx_grouped(a.K))
+    gg_mx_group_kernel<kMXFP4, GATEUP><<<grid, block, 0, s>>>(a);
   else if (dm.wfmt == kMXFP4)
     gg_direct_b_kernel<kMXFP4, GATEUP, kDepthDirect><<<grid, block, 0, s>>>(a);
   else
@@ -791,8 +871,9 @@ hipError_t launch_gg(const Dims& dm, const GGArgs& a, hipStream_t s) {
 }  // namespace
 
 bool grouped_gemm_ok(const Dims& dm) {
-  return dm.act == kBF16 && (dm.wfmt == kBF16 || dm.wfmt == kMXFP4) && dm.T >= kGemmMinT &&
-         dm.d % BK == 0 && dm.f % BK == 0;
+  if (dm.act != kBF16 || dm.T < kGemmMinT) return false;
+  if (dm.wfmt == kNVFP4) return mx_grouped(dm.d) && mx_grouped(dm.f);
+  return (dm.wfmt == kBF16 || dm.wfmt == kMXFP4) && dm.d % BK == 0 && dm.f % BK == 0;
 }
 
 size_t grouped_gemm_max_mtiles(const Dims& dm) {
@@ -805,7 +886,7 @@ hipError_t launch_gg_gate_up(const Dims& dm, const void* x, const Plan& p, const
                              void* h, hipStream_t s) {
   LaunchTimer tm("gg_gate_up", s);
   const int tc = tile_cols(dm, true);
-  GGArgs a{x, p.sorted_src, w.wg, w.wu, w.sg, w.su, p.mtiles, p.num_mtiles, h,
+  GGArgs a{x, p.sorted_src, w.wg, w.wu, w.sg, w.su, w.tg, w.tu, p.mtiles, p.num_mtiles, h,
            dm.d, dm.f, dm.k, (dm.f + tc - 1) / tc};
   return launch_gg<true>(dm, a, s);
 }
@@ -814,7 +895,7 @@ hipError_t launch_gg_down(const Dims& dm, const void* h, const Plan& p, const We
                           float* y_sorted, hipStream_t s) {
   LaunchTimer tm("gg_down", s);
   const int tc = tile_cols(dm, false);
-  GGArgs a{h, nullptr, w.wd, nullptr, w.sd, nullptr, p.mtiles, p.num_mtiles, y_sorted,
+  GGArgs a{h, nullptr, w.wd, nullptr, w.sd, nullptr, w.td, nullptr, p.mtiles, p.num_mtiles, y_sorted,
            dm.f, dm.d, dm.k, (dm.d + tc - 1) / tc};
   return launch_gg<false>(dm, a, s);
 }

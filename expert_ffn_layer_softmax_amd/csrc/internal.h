@@ -9,7 +9,12 @@
 namespace moe {
 
 // Storage formats, numbered as moe_dtype_t.
-enum Fmt : int { kF32 = 0, kBF16 = 1, kMXFP4 = 2 };
+enum Fmt : int { kF32 = 0, kBF16 = 1, kMXFP4 = 2, kNVFP4 = 3 };
+
+// The two 4-bit weight formats share codes and kernels; they differ in the
+// block scales (E8M0 per 32 elements vs E4M3 per 16 plus an fp32 scale per
+// matrix).
+constexpr bool is_fp4(int wf) { return wf == kMXFP4 || wf == kNVFP4; }
 
 // Rows per m-tile of the grouped MFMA GEMMs; the tile list in the workspace
 // is sized for this value.  Each m-tile entry holds kMtileInts ints:
@@ -35,7 +40,8 @@ struct Dims {
 
 struct Weights {
   const void *wg, *wu, *wd;
-  const uint8_t *sg, *su, *sd;
+  const uint8_t *sg, *su, *sd;  // 4-bit block scales
+  const float *tg, *tu, *td;    // NVFP4 matrix scales [E]
 };
 
 // Workspace layout (byte offsets, each 256-aligned).

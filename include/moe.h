@@ -2,7 +2,8 @@
  * moe.h -- C ABI of a gfx950 (MI355X) library for the forward pass of one
  * Mixture-of-Experts decoder layer: router softmax and top-k selection,
  * grouping of (token, slot) pairs by expert, a grouped SwiGLU expert FFN over
- * bf16 or MX-FP4 weights with fp32 accumulation, and the weighted combine.
+ * bf16, MX-FP4 or NVFP4 weights with fp32 accumulation, and the weighted
+ * combine.
  *
  * The layer is the one the Muse Spark pages describe: every decoder layer is
  * a Mixture-of-Experts layer that sends each token to 8 of its 256 experts
@@ -37,13 +38,22 @@
  *                      per byte, element 2i in the low nibble; E8M0 scales
  *                      uint8 [E][f][d/32] / [E][d][f/32], one per 32
  *                      consecutive elements along the reduction dimension.
+ *    NVFP4 weights:    the same codes; OCP FP8 E4M3 scales uint8 [E][f][d/16]
+ *                      / [E][d][f/16], one per 16 consecutive elements along
+ *                      the reduction dimension; fp32 scales t_gate, t_up,
+ *                      t_down [E], one per weight matrix.  A weight is
+ *                      E2M1(code) * E4M3(scale) * t (the 4-bit expert format
+ *                      the pages run: SGLang-TorchTPU on TPU v7 page,
+ *                      "Results").  E4M3 NaN bytes (0x7F, 0xFF) are outside
+ *                      the domain.
  *    topk_idx, topk_w  [T][k]          int32 / fp32
  *    y_sorted          [T*k][d]        fp32
  *    out               [T][d]          act dtype
  *
  * Supported shapes: 1 <= E <= 1024, 1 <= k <= min(E, 64), d and f positive
  * multiples of 32, T*k < 2^31.  Supported (act, weight) dtype pairs:
- * (F32, F32), (BF16, BF16), (BF16, MXFP4); others give MOE_ERR_UNSUPPORTED.
+ * (F32, F32), (BF16, BF16), (BF16, MXFP4), (BF16, NVFP4); others give
+ * MOE_ERR_UNSUPPORTED.
  */
 #ifndef MOE_MI355X_H_
 #define MOE_MI355X_H_
@@ -63,7 +73,12 @@ typedef enum {
   MOE_ERR_DEVICE = 4               /* a HIP call failed                     */
 } moe_status_t;
 
-typedef enum { MOE_DTYPE_F32 = 0, MOE_DTYPE_BF16 = 1, MOE_DTYPE_MXFP4 = 2 } moe_dtype_t;
+typedef enum {
+  MOE_DTYPE_F32 = 0,
+  MOE_DTYPE_BF16 = 1,
+  MOE_DTYPE_MXFP4 = 2,
+  MOE_DTYPE_NVFP4 = 3
+} moe_dtype_t;
 
 /* Layer shape.  T tokens of hidden size d, E experts of FFN width f, each
  * token routed to k experts.  act_dtype / w_dtype hold moe_dtype_t values. */
@@ -74,7 +89,9 @@ typedef struct {
 } moe_dims_t;
 
 /* Stacked expert weights (device pointers, layouts above).  s_* are the
- * MX-FP4 scale arrays and must be NULL for other weight dtypes. */
+ * block-scale arrays of the 4-bit dtypes (E8M0 for MX-FP4, E4M3 for NVFP4)
+ * and t_* the NVFP4 per-matrix fp32 scales; each must be NULL for the dtypes
+ * that do not use it. */
 typedef struct {
   const void* w_gate;
   const void* w_up;
@@ -82,6 +99,9 @@ typedef struct {
   const uint8_t* s_gate;
   const uint8_t* s_up;
   const uint8_t* s_down;
+  const float* t_gate;
+  const float* t_up;
+  const float* t_down;
 } moe_expert_weights_t;
 
 typedef void* moe_stream_t; /* a hipStream_t */

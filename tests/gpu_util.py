@@ -37,6 +37,11 @@ def to_host_act(t: torch.Tensor) -> np.ndarray:
 def expert_getter(w: dict, wfmt: str):
     """Oracle-side expert decoder over device weights (one D2H copy per call)."""
     def get(e):
+        if wfmt == "nvfp4":
+            return tuple(oracle.decode_nvfp4(w["w_" + n][e].cpu().numpy(),
+                                             w["s_" + n][e].view(torch.uint8).cpu().numpy(),
+                                             float(w["t_" + n][e]))
+                         for n in ("gate", "up", "down"))
         if wfmt == "mxfp4":
             return tuple(oracle.decode_mxfp4(w["w_" + n][e].cpu().numpy(), w["s_" + n][e].cpu().numpy())
                          for n in ("gate", "up", "down"))

@@ -63,6 +63,9 @@ def test_workspace_size_validation(m):
     assert _ws(m, _dims(m, act=1, w=0))[0] == UNSUPPORTED
     assert _ws(m, _dims(m, act=2, w=2))[0] == UNSUPPORTED   # MX-FP4 activations
     assert _ws(m, _dims(m, act=5))[0] == INVALID
+    assert _ws(m, _dims(m, act=1, w=3))[0] == OK            # NVFP4 weights
+    assert _ws(m, _dims(m, act=3, w=3))[0] == UNSUPPORTED   # NVFP4 activations
+    assert _ws(m, _dims(m, act=1, w=4))[0] == INVALID
     assert m.lib.moe_workspace_size(None, None) == INVALID
 
 
@@ -97,8 +100,8 @@ def test_permute_validation(m):
     assert L.moe_permute(FAKE, 3, 1025, 2, FAKE, FAKE, FAKE, FAKE, None) == UNSUPPORTED
 
 
-def _w(m, mx=False, bad=None):
-    vals = [FAKE.value] * 3 + ([FAKE.value] * 3 if mx else [None] * 3)
+def _w(m, mx=False, bad=None, t=False):
+    vals = [FAKE.value] * 3 + ([FAKE.value] * 3 if mx else [None] * 3) + ([FAKE.value] * 3 if t else [None] * 3)
     if bad is not None:
         vals[bad[0]] = bad[1]
     return m._lib.MoeExpertWeights(*vals)
@@ -118,6 +121,16 @@ def test_layer_forward_validation(m):
     assert L.moe_layer_forward(*args(dims, _w(m), ws=ctypes.c_void_p(0x10010))) == INVALID
     assert L.moe_layer_forward(*args(_dims(m, d=40), _w(m))) == UNSUPPORTED
     assert L.moe_layer_forward(*args(_dims(m, T=0), _w(m))) == OK
+    # NVFP4: block scales and fp32 matrix scales both required; matrix scales
+    # only with NVFP4
+    nvd = _dims(m, w=3)
+    nvn = _ws(m, nvd)[1]
+    assert L.moe_layer_forward(*args(nvd, _w(m, mx=True), wsb=nvn)) == INVALID       # no t_*
+    assert L.moe_layer_forward(*args(nvd, _w(m, t=True), wsb=nvn)) == INVALID        # no s_*
+    assert L.moe_layer_forward(*args(nvd, _w(m, mx=True, t=True, bad=(7, MISALIGNED.value)),
+                                     wsb=nvn)) == INVALID
+    assert L.moe_layer_forward(*args(mxd, _w(m, mx=True, t=True), wsb=_ws(m, mxd)[1])) == INVALID
+    assert L.moe_layer_forward(*args(dims, _w(m, t=True))) == INVALID
     assert L.moe_layer_forward(None, None, None, None, None, None, None, None, None, 0, None) == INVALID
 
 

@@ -29,7 +29,7 @@ def _gpu():
 
 
 def _tol(wl):
-    return MXFP4_TOL if wl.wfmt == "mxfp4" else ACT_TOL[wl.act]
+    return MXFP4_TOL if wl.wfmt in ("mxfp4", "nvfp4") else ACT_TOL[wl.act]
 
 
 # --------------------------------------------------------------------- route
@@ -114,6 +114,17 @@ SMALL = [
     ("gg_mx_ntail", 90, 640, 6, 2, 256, "bf16", "mxfp4"),      # down N=640: partial n-tile
     ("gg_mx_oddk", 80, 320, 6, 2, 192, "bf16", "mxfp4"),       # K % 128 != 0 on both GEMMs
     ("gg_mx_gtail", 150, 512, 6, 2, 320, "bf16", "mxfp4"),     # gate/up N=320: partial n-tile
+    # NVFP4: 16-element E4M3 blocks and fp32 matrix scales
+    ("nv_t1", 1, 256, 16, 4, 96, "bf16", "nvfp4"),
+    ("nv_t5", 5, 512, 32, 8, 160, "bf16", "nvfp4"),
+    ("nv_t16", 16, 1024, 64, 8, 352, "bf16", "nvfp4"),
+    ("nv_t40", 40, 256, 8, 2, 128, "bf16", "nvfp4"),
+    ("nv_segd", 1, 33792, 2, 1, 32, "bf16", "nvfp4"),
+    ("nv_t1_bigf", 1, 64, 4, 2, 8192, "bf16", "nvfp4"),
+    ("nv_oddk_t100", 100, 320, 6, 2, 192, "bf16", "nvfp4"),     # K % 256 != 0: GEMV at any T
+    ("gg_nv_t100", 100, 256, 8, 4, 256, "bf16", "nvfp4"),
+    ("gg_nv_hot", 700, 512, 5, 2, 512, "bf16", "nvfp4"),
+    ("gg_nv_tails", 150, 768, 6, 2, 512, "bf16", "nvfp4"),      # partial n-tiles on both GEMMs
 ]
 
 
@@ -175,7 +186,7 @@ def test_determinism_and_t0():
     assert r["out"].shape == (0, 256)
 
 
-@pytest.mark.parametrize("wfmt,k", [("bf16", 8), ("mxfp4", 8), ("f32", 4), ("bf16", 16)])
+@pytest.mark.parametrize("wfmt,k", [("bf16", 8), ("mxfp4", 8), ("nvfp4", 8), ("f32", 4), ("bf16", 16)])
 def test_single_token_fused_path_equals_stagewise(wfmt, k):
     """The single-token layer (fused down+combine) is bit-identical to
     route -> permute -> expert_ffn -> combine called one by one."""
@@ -196,7 +207,8 @@ def test_single_token_fused_path_equals_stagewise(wfmt, k):
 
 
 # ------------------------------------------------------------ HIP graphs
-@pytest.mark.parametrize("T,wfmt", [(1, "bf16"), (16, "bf16"), (100, "bf16"), (100, "mxfp4")])
+@pytest.mark.parametrize("T,wfmt", [(1, "bf16"), (16, "bf16"), (100, "bf16"), (100, "mxfp4"),
+                                    (100, "nvfp4")])
 def test_hip_graph_replay(T, wfmt):
     """A captured layer replays to the eager result, bit for bit, after eager
     calls with other routing have rewritten the same workspace and outputs."""
@@ -233,7 +245,7 @@ def test_hip_graph_replay(T, wfmt):
 
 
 # --------------------------------------------------- individual entry points
-@pytest.mark.parametrize("wfmt,T", [("bf16", 7), ("bf16", 64), ("mxfp4", 23), ("f32", 9)])
+@pytest.mark.parametrize("wfmt,T", [("bf16", 7), ("bf16", 64), ("mxfp4", 23), ("nvfp4", 64), ("f32", 9)])
 def test_stagewise_entry_points(wfmt, T):
     from expert_ffn_layer_softmax_amd import moe_combine, moe_expert_ffn, moe_permute, moe_route
     act = "f32" if wfmt == "f32" else "bf16"
@@ -302,7 +314,7 @@ def test_verify_bf16_full(full_bf16_weights):
     assert err <= 5e-3
 
 
-@pytest.mark.parametrize("name", ["prefill_bf16", "prefill_mxfp4"])
+@pytest.mark.parametrize("name", ["prefill_bf16", "prefill_mxfp4", "prefill_nvfp4"])
 def test_prefill_full_sampled(name, full_bf16_weights):
     """T=4096 with skewed load: routing checked in full; outputs on sampled
     tokens (each token's output depends only on its own row and logits)."""
@@ -327,15 +339,16 @@ def test_prefill_full_sampled(name, full_bf16_weights):
     got = to_host_act(res["out"])[S]
     err = rel_l2(got, ref["out"])
     log(f"  sampled tokens {S.tolist()}: rel_l2={err:.3e}")
-    assert err <= (MXFP4_TOL if wl.wfmt == "mxfp4" else 5e-3)
-    if wl.wfmt == "mxfp4":
+    assert err <= (MXFP4_TOL if wl.wfmt in ("mxfp4", "nvfp4") else 5e-3)
+    if wl.wfmt != "bf16":
         del w
         torch.cuda.empty_cache()
 
 
-def test_decode_mxfp4_full():
-    wl = WORKLOADS["decode_mxfp4"]
-    log("generating full MX-FP4 expert weights (7.06 GB)")
+@pytest.mark.parametrize("name", ["decode_mxfp4", "decode_nvfp4"])
+def test_decode_fp4_full(name):
+    wl = WORKLOADS[name]
+    log(f"generating full {wl.wfmt} expert weights")
     w = gen_expert_weights(wl, "cuda")
     for s in (0, 9):
         x, w, w_r, logits = make_inputs(wl, weights=w, logit_set=s)
