@@ -18,6 +18,8 @@ from .moe_oracle import (  # noqa: F401
     layer,
     permute,
     route,
+    quantize_mxfp8,
+    round_e4m3,
     router_logits,
     swiglu_expert,
 )

@@ -202,15 +202,57 @@ def _silu(z: np.ndarray) -> np.ndarray:
         return z / (1.0 + np.exp(-z))
 
 
-def swiglu_expert(xs: np.ndarray, wg: np.ndarray, wu: np.ndarray, wd: np.ndarray) -> np.ndarray:
-    """One expert applied to rows ``xs[n, d]``; ``wg, wu: [f][d]``, ``wd: [d][f]``."""
+# ----------------------------------------------------------------------------
+# FP8 activations (the pages run the experts with FP8 compute: SGLang-TorchTPU
+# on TPU v7 page, "Results").  Reading: OCP MX-style FP8, i.e. E4M3 elements
+# with one E8M0 scale per 32 consecutive elements along the reduction
+# dimension, applied to the two activation operands of the expert FFN (x before
+# the gate/up products, h before the down product).
+# ----------------------------------------------------------------------------
+
+def round_e4m3(v: np.ndarray) -> np.ndarray:
+    """Nearest OCP FP8 E4M3 value (ties to even mantissa), saturating at +-448.
+    Normal values 2**e * (1 + m/8) for e >= -6, subnormals m * 2**-9."""
+    v = np.asarray(v, dtype=np.float64)
+    a = np.abs(v)
+    e = np.floor(np.log2(np.where(a > 0, a, 1.0)))
+    e = np.maximum(e, -6.0)                      # below 2**-6 the spacing stays 2**-9
+    quantum = np.ldexp(1.0, (e - 3).astype(np.int64))
+    q = np.round(a / quantum) * quantum          # numpy rounds half to even
+    q = np.minimum(q, 448.0)
+    return np.where(v < 0, -q, q)
+
+
+def quantize_mxfp8(v: np.ndarray) -> np.ndarray:
+    """The values an MXFP8 encoding of ``v[..., K]`` (K % 32 == 0) decodes to.
+    Per 32-element block: shared exponent s = floor(log2 amax) - 8 (E4M3's
+    largest exponent), clamped to the E8M0 range [-126, 127]; elements are
+    v / 2**s rounded to E4M3 (saturating at +-448); an all-zero block stays 0."""
+    v = np.asarray(v, dtype=np.float64)
+    K = v.shape[-1]
+    assert K % 32 == 0, "MXFP8 rows must hold whole 32-element blocks"
+    b = v.reshape(*v.shape[:-1], K // 32, 32)
+    amax = np.abs(b).max(axis=-1)
+    s = np.floor(np.log2(np.where(amax > 0, amax, 1.0))) - 8
+    s = np.clip(s, -126, 127)
+    scale = np.ldexp(1.0, s.astype(np.int64))[..., None]
+    return (round_e4m3(b / scale) * scale).reshape(v.shape)
+
+
+def swiglu_expert(xs: np.ndarray, wg: np.ndarray, wu: np.ndarray, wd: np.ndarray,
+                  act_quant=None) -> np.ndarray:
+    """One expert applied to rows ``xs[n, d]``; ``wg, wu: [f][d]``, ``wd: [d][f]``.
+    ``act_quant`` (e.g. ``quantize_mxfp8``) is applied to the rows and to h
+    before the products that read them."""
+    q = (lambda a: a) if act_quant is None else act_quant
+    xs = q(xs)
     g = xs @ wg.T
     u = xs @ wu.T
-    h = _silu(g) * u
+    h = q(_silu(g) * u)
     return h @ wd.T
 
 
-def expert_ffn(x, offsets, sorted_src, k, get_expert):
+def expert_ffn(x, offsets, sorted_src, k, get_expert, act_quant=None):
     """``y_sorted[r] = FFN_e(x[sorted_src[r] // k])`` for r in expert e's segment.
 
     ``get_expert(e)`` returns the fp64 ``(w_gate[e], w_up[e], w_down[e])``; it
@@ -228,7 +270,7 @@ def expert_ffn(x, offsets, sorted_src, k, get_expert):
             continue
         wg, wu, wd = get_expert(e)
         tok = sorted_src[r0:r1] // k
-        y[r0:r1] = swiglu_expert(x[tok], wg, wu, wd)
+        y[r0:r1] = swiglu_expert(x[tok], wg, wu, wd, act_quant)
     return y
 
 
@@ -243,9 +285,10 @@ def combine(y_sorted, dest_row, w):
     return out
 
 
-def layer(x, logits, k, get_expert, E=None, w_r=None):
+def layer(x, logits, k, get_expert, E=None, w_r=None, act_quant=None):
     """Whole layer.  If ``w_r`` is given the logits are computed from it
     (``logits`` is then ignored); otherwise ``logits`` are used as given.
+    ``act_quant`` quantises the expert FFN's activation operands (FP8 mode).
     Returns a dict with every intermediate."""
     x = np.asarray(x, dtype=np.float64)
     if w_r is not None:
@@ -254,7 +297,7 @@ def layer(x, logits, k, get_expert, E=None, w_r=None):
     E = logits.shape[1] if E is None else E
     idx, w = route(logits, k)
     counts, offsets, sorted_src, dest_row = permute(idx, E)
-    y = expert_ffn(x, offsets, sorted_src, k, get_expert)
+    y = expert_ffn(x, offsets, sorted_src, k, get_expert, act_quant)
     out = combine(y, dest_row, w)
     return dict(logits=logits, idx=idx, w=w, counts=counts, offsets=offsets,
                 sorted_src=sorted_src, dest_row=dest_row, y_sorted=y, out=out)

@@ -1,4 +1,5 @@
-"""Pins for the oracle's input decoders: bf16, E8M0, MX-FP4 (E2M1), E4M3 and NVFP4.
+"""Pins for the oracle's number formats: bf16, E8M0, MX-FP4 (E2M1), E4M3, NVFP4
+and the MXFP8 activation quantiser.
 
 bf16, E8M0 and E4M3 are checked against torch's own dtype conversions; E2M1 against
 the format's bit-field definition (sign, two exponent bits with bias 1, one
@@ -9,7 +10,8 @@ import numpy as np
 import pytest
 import torch
 
-from oracle import E2M1_VALUES, decode_bf16, decode_e4m3, decode_e8m0, decode_mxfp4, decode_nvfp4
+from oracle import (E2M1_VALUES, decode_bf16, decode_e4m3, decode_e8m0, decode_mxfp4, decode_nvfp4,
+                    quantize_mxfp8, round_e4m3)
 from synth import quantize_mxfp4, quantize_nvfp4
 
 
@@ -167,3 +169,49 @@ def test_nvfp4_products_exact_in_bf16(rng):
     deq = decode_nvfp4(codes.numpy(), scales.numpy(), 1.0)
     as_bf16 = torch.tensor(deq).to(torch.bfloat16).to(torch.float64).numpy()
     np.testing.assert_array_equal(deq, as_bf16)
+
+
+# ----------------------------------------------------------------- MXFP8
+# FP8 activations (the pages' "FP8 compute"): E4M3 elements, one E8M0 scale
+# per 32 elements along the reduction dimension.
+
+def test_round_e4m3_matches_torch_cast(rng):
+    v = rng.normal(size=20000) * 10.0 ** rng.integers(-5, 3, size=20000)
+    v = np.concatenate([v, [2.375, -2.375, 2.0 ** -10, 1.5 * 2.0 ** -10, 448.0, 460.0, 464.0, -470.0, 0.0]])
+    ref = torch.tensor(v).clamp(-448, 448).to(torch.float8_e4m3fn).to(torch.float64).numpy()
+    np.testing.assert_array_equal(round_e4m3(v), ref)
+
+
+def test_mxfp8_block_scale_and_grid(rng):
+    v = rng.normal(size=(6, 128)) * 0.3
+    q = quantize_mxfp8(v)
+    b = v.reshape(6, 4, 32)
+    qb = q.reshape(6, 4, 32)
+    amax = np.abs(b).max(-1)
+    s = np.floor(np.log2(amax)) - 8
+    scaled = qb / np.ldexp(1.0, s.astype(int))[..., None]
+    # every value is an E4M3 value times the block's power of two
+    e4m3 = decode_e4m3(np.arange(256, dtype=np.uint8))
+    assert np.isin(scaled, e4m3[~np.isnan(e4m3)]).all()
+    # amax / 2**s lies in [256, 512): at most one rounding step plus saturation
+    assert np.all(amax / np.ldexp(1.0, s.astype(int)) >= 256)
+    err = np.abs(q - v)
+    big = np.abs(b).reshape(v.shape) >= np.repeat(np.ldexp(1.0, (s - 6).astype(int)), 32, -1) * 1.0
+    assert np.all(err[big] <= np.abs(v)[big] * 2.0 ** -4 + 1e-300)   # half an E4M3 step, normal range
+
+
+def test_mxfp8_fixed_points_and_zero_block():
+    v = np.zeros((1, 64))
+    v[0, :32] = [2.0 ** (i % 9) * (1 + (i % 8) / 8) for i in range(32)]   # on the grid
+    np.testing.assert_array_equal(quantize_mxfp8(v), v)
+    assert np.all(quantize_mxfp8(v)[0, 32:] == 0.0)
+
+
+def test_swiglu_with_act_quant_reduces_on_grid_inputs(rng):
+    from oracle import swiglu_expert
+    xs = quantize_mxfp8(rng.normal(size=(3, 64)))
+    wg, wu, wd = (rng.normal(size=s) for s in ((32, 64), (32, 64), (64, 32)))
+    g = xs @ wg.T
+    h = (g / (1 + np.exp(-g))) * (xs @ wu.T)
+    np.testing.assert_allclose(swiglu_expert(xs, wg, wu, wd, quantize_mxfp8),
+                               quantize_mxfp8(h) @ wd.T, rtol=0, atol=0)
