@@ -26,6 +26,7 @@ sys.path.insert(0, ROOT)
 METRIC = "MoE-layer tokens/s; decode HBM GB/s and prefill MFMA TFLOP/s as % of peak"
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
+FP8_PEAK_TFLOPS = 5000.0       # MI355X dense fp8 MFMA (the FP8 x FP4 scaled MFMA runs at this rate)
 
 
 def _parse():
@@ -44,6 +45,8 @@ def _parse():
     p.add_argument("--layers", type=int, default=1,
                    help="chain this many layers per step, each with its own weights (out of one "
                         "layer is x of the next); tokens/s counts each token once per step")
+    p.add_argument("--fp8", action="store_true",
+                   help="FP8 activations (MXFP8) on the scaled MFMA; MX-FP4 workloads only")
     p.add_argument("--graph", action="store_true",
                    help="replay each step from a captured HIP graph (one graph per logit-set "
                         "offset, rotated) instead of launching it")
@@ -95,7 +98,7 @@ def _traffic(kernel: str, workload: str, digest: str):
     return rec.get("bytes_per_launch")
 
 
-def cpu_baseline(wl, x, w, logit_sets, budget_s: float):
+def cpu_baseline(wl, x, w, logit_sets, budget_s: float, fp8: bool = False):
     """The oracle, as it stands, on the host: one token per logit set until the
     budget is spent.  Expert weights are copied to host memory untimed; decoding
     them to fp64 is part of the oracle's timed work."""
@@ -140,7 +143,7 @@ def cpu_baseline(wl, x, w, logit_sets, budget_s: float):
 
         t0 = time.perf_counter()
         xh = oracle.decode_bf16(xh_raw) if wl.act == "bf16" else xh_raw.astype(np.float64)
-        oracle.layer(xh, lg, wl.k, get, E=wl.E)
+        oracle.layer(xh, lg, wl.k, get, E=wl.E, act_quant=oracle.quantize_mxfp8 if fp8 else None)
         spent += time.perf_counter() - t0
         done_tokens += T
         sets_used += 1
@@ -176,13 +179,14 @@ def measure(wl, ws_list, args, with_cpu: bool):
     topk_idx = torch.empty(wl.T, k, dtype=torch.int32, device=dev)
     topk_w = torch.empty(wl.T, k, dtype=torch.float32, device=dev)
     res = moe_layer_forward(x, ws_list[0], k, logits=sets[0], topk_idx=topk_idx, topk_w=topk_w,
-                            out=acts[1])
+                            out=acts[1], fp8=args.fp8)
     ws = res["workspace"]
 
     # Steps call the C entry point directly with pre-marshalled arguments, so
     # host-side Python work does not pace the GPU.
     wfmt = L._wfmt(ws_list[0])
-    dims = L._dims(wl.T, wl.d, wl.E, k, wl.f, L._ACT[x.dtype], wfmt)
+    dims = L._dims(wl.T, wl.d, wl.E, k, wl.f, L._ACT[x.dtype], wfmt,
+                   L.MOE_FLAG_FP8_ACTIVATIONS if args.fp8 else 0)
     wts = [L._weights(w, wl.E, wl.d, wl.f, wfmt, dev) for w in ws_list]
     lptr = [ctypes.c_void_p(sets[i].data_ptr()) for i in range(nsets)]
     aptr = [ctypes.c_void_p(t.data_ptr()) for t in acts]
@@ -265,8 +269,9 @@ def measure(wl, ws_list, args, with_cpu: bool):
     # weights read once, x read, h written; 2 FLOPs per MAC over T*k rows
     k_bytes = mean_uniq * eb["gate_up"] + wl.T * wl.d * act_b + wl.T * k * wl.f * act_b
     k_flops = 4.0 * wl.T * k * wl.d * wl.f
-    if k_flops / k_bytes > RIDGE_FLOP_PER_BYTE:
-        bound, unit, peak = "mfma", "TFLOP/s", BF16_PEAK_TFLOPS
+    mfma_peak = FP8_PEAK_TFLOPS if args.fp8 else BF16_PEAK_TFLOPS
+    if k_flops / k_bytes > mfma_peak * 1e12 / (HBM_PEAK_GBS * 1e9):
+        bound, unit, peak = "mfma", "TFLOP/s", mfma_peak
         achieved = k_flops / (kernel_us * 1e-6) / 1e12
     else:
         bound, unit, peak = "hbm", "GB/s", HBM_PEAK_GBS
@@ -274,7 +279,7 @@ def measure(wl, ws_list, args, with_cpu: bool):
     layer_bytes = (mean_uniq * eb["total"] + 2 * wl.T * wl.d * act_b + wl.T * wl.E * 4 + wl.T * k * 8)
     layer_flops = 6.0 * wl.T * k * wl.d * wl.f
     step_bytes, step_flops = nl * layer_bytes, nl * layer_flops
-    t_floor = max(step_bytes / (HBM_PEAK_GBS * 1e9), step_flops / (BF16_PEAK_TFLOPS * 1e12))
+    t_floor = max(step_bytes / (HBM_PEAK_GBS * 1e9), step_flops / (mfma_peak * 1e12))
     digest = _source_digest(srcs)
     traffic = _traffic(kname, wl.name, digest) if nl == 1 else None
     breakdown = {}
@@ -289,11 +294,13 @@ def measure(wl, ws_list, args, with_cpu: bool):
         cfg["layers"] = nl
     if graphs:
         cfg["hip_graph"] = True
+    if args.fp8:
+        cfg["activations"] = "mxfp8"
     rec = {
         "metric": METRIC, "value": round(tokens_per_s, 2), "unit": "tokens/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 5),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-        "dtype": "bf16" if wl.act == "bf16" else "f32", "data": "synthetic",
+        "dtype": "fp8" if args.fp8 else ("bf16" if wl.act == "bf16" else "f32"), "data": "synthetic",
         "config": cfg,
         "roofline": {"bound": bound, "kernel": kname, "achieved": round(achieved, 1),
                      "peak": peak, "unit": unit, "frac": round(achieved / peak, 4),
@@ -302,13 +309,13 @@ def measure(wl, ws_list, args, with_cpu: bool):
                      "algorithmic_flops_per_launch": k_flops},
         "step": {"algorithmic_bytes": int(step_bytes), "algorithmic_flops": step_flops,
                  "hbm_frac": round(step_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
-                 "mfma_frac": round(step_flops / (ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4),
+                 "mfma_frac": round(step_flops / (ms * 1e-3) / 1e12 / mfma_peak, 4),
                  "attainable_frac": round(t_floor / (ms * 1e-3), 4),
                  "kernel_us": breakdown},
     }
     if with_cpu:
         print("[bench] CPU oracle baseline", file=sys.stderr, flush=True)
-        rec["cpu_baseline"] = cpu_baseline(wl, x, ws_list[0], sets, args.cpu_seconds)
+        rec["cpu_baseline"] = cpu_baseline(wl, x, ws_list[0], sets, args.cpu_seconds, args.fp8)
     else:
         rec["cpu_baseline"] = None
     return rec

@@ -32,7 +32,7 @@ lib = ctypes.CDLL(LIB_PATH, mode=ctypes.RTLD_GLOBAL)
 class MoeDims(ctypes.Structure):
     _fields_ = [("T", ctypes.c_int32), ("d", ctypes.c_int32), ("E", ctypes.c_int32),
                 ("k", ctypes.c_int32), ("f", ctypes.c_int32),
-                ("act_dtype", ctypes.c_int32), ("w_dtype", ctypes.c_int32)]
+                ("act_dtype", ctypes.c_int32), ("w_dtype", ctypes.c_int32), ("flags", ctypes.c_int32)]
 
 
 class MoeExpertWeights(ctypes.Structure):
@@ -109,8 +109,11 @@ def _need(t, name, dtype=None, shape=None, device=None):
 _ACT = {torch.float32: MOE_DTYPE_F32, torch.bfloat16: MOE_DTYPE_BF16}
 
 
-def _dims(T, d, E, k, f, act, wfmt) -> MoeDims:
-    return MoeDims(T, d, E, k, f, act, wfmt)
+MOE_FLAG_FP8_ACTIVATIONS = 1
+
+
+def _dims(T, d, E, k, f, act, wfmt, flags=0) -> MoeDims:
+    return MoeDims(T, d, E, k, f, act, wfmt, flags)
 
 
 def _weights(w: dict, E, d, f, wfmt, device) -> MoeExpertWeights:
@@ -155,9 +158,9 @@ def _wshape(w: dict, wfmt: int):
     return E, (dd * 2 if wfmt in (MOE_DTYPE_MXFP4, MOE_DTYPE_NVFP4) else dd), f
 
 
-def moe_workspace_size(T, d, E, k, f, act_dtype, w_dtype) -> int:
+def moe_workspace_size(T, d, E, k, f, act_dtype, w_dtype, flags=0) -> int:
     out = _sz(0)
-    _check(lib.moe_workspace_size(ctypes.byref(_dims(T, d, E, k, f, act_dtype, w_dtype)),
+    _check(lib.moe_workspace_size(ctypes.byref(_dims(T, d, E, k, f, act_dtype, w_dtype, flags)),
                                   ctypes.byref(out)), "moe_workspace_size")
     return out.value
 
@@ -202,7 +205,9 @@ def _workspace(dims: MoeDims, device, workspace):
     return workspace
 
 
-def moe_expert_ffn(x, offsets, sorted_src, k, weights: dict, y_sorted=None, workspace=None):
+def moe_expert_ffn(x, offsets, sorted_src, k, weights: dict, y_sorted=None, workspace=None, fp8=False):
+    """Grouped SwiGLU expert FFN.  ``fp8=True`` sets MOE_FLAG_FP8_ACTIVATIONS
+    (MXFP8 activations on the scaled MFMA; MX-FP4 weights)."""
     _need(x, "x")
     if x.dtype not in _ACT:
         raise TypeError("x must be float32 or bfloat16")
@@ -212,7 +217,7 @@ def moe_expert_ffn(x, offsets, sorted_src, k, weights: dict, y_sorted=None, work
     dev = x.device
     _need(offsets, "offsets", torch.int32, (E + 1,), dev)
     _need(sorted_src, "sorted_src", torch.int32, (T * k,), dev)
-    dims = _dims(T, d, E, k, f, _ACT[x.dtype], wfmt)
+    dims = _dims(T, d, E, k, f, _ACT[x.dtype], wfmt, MOE_FLAG_FP8_ACTIVATIONS if fp8 else 0)
     w = _weights(weights, E, d, f, wfmt, dev)
     if y_sorted is None:
         y_sorted = torch.empty(T * k, d, dtype=torch.float32, device=dev)
@@ -242,9 +247,11 @@ def moe_combine(y_sorted, dest_row, topk_w, out_dtype, out=None):
 
 
 def moe_layer_forward(x, weights: dict, k, logits=None, w_router=None, topk_idx=None, topk_w=None,
-                      out=None, workspace=None):
+                      out=None, workspace=None, fp8=False):
     """Whole layer.  Give ``w_router`` to compute the logits in-path (they are
-    written to ``logits``, allocated if None), or ``logits`` to route by them."""
+    written to ``logits``, allocated if None), or ``logits`` to route by them.
+    ``fp8=True`` sets MOE_FLAG_FP8_ACTIVATIONS (MXFP8 activations on the scaled
+    MFMA; MX-FP4 weights)."""
     _need(x, "x")
     if x.dtype not in _ACT:
         raise TypeError("x must be float32 or bfloat16")
@@ -265,7 +272,7 @@ def moe_layer_forward(x, weights: dict, k, logits=None, w_router=None, topk_idx=
     _need(topk_idx, "topk_idx", torch.int32, (T, k), dev)
     _need(topk_w, "topk_w", torch.float32, (T, k), dev)
     _need(out, "out", x.dtype, (T, d), dev)
-    dims = _dims(T, d, E, k, f, _ACT[x.dtype], wfmt)
+    dims = _dims(T, d, E, k, f, _ACT[x.dtype], wfmt, MOE_FLAG_FP8_ACTIVATIONS if fp8 else 0)
     w = _weights(weights, E, d, f, wfmt, dev)
     ws = _workspace(dims, dev, workspace)
     _check(lib.moe_layer_forward(ctypes.byref(dims), _ptr(x), _ptr(w_router), _ptr(logits),

@@ -69,8 +69,13 @@ WsLayout ws_layout(const Dims& dm) {
   L.slot_info = o;   o = align_up(o + E * 16);
   L.mtiles = o;      o = align_up(o + max_mtiles * kMtileInts * 4);
   L.num_mtiles = o;  o = align_up(o + 4);
-  L.h = o;           o = align_up(o + Tk * (size_t)dm.f * act);
+  L.h = o;           o = align_up(o + (dm.fp8 ? 0 : Tk * (size_t)dm.f * act));
   L.y_sorted = o;    o = align_up(o + Tk * (size_t)dm.d * 4);
+  const size_t T = (size_t)dm.T;
+  L.xq = o;          o = align_up(o + (dm.fp8 ? T * dm.d : 0));
+  L.xs = o;          o = align_up(o + (dm.fp8 ? T * dm.d / 32 : 0));
+  L.hq = o;          o = align_up(o + (dm.fp8 ? Tk * dm.f : 0));
+  L.hs = o;          o = align_up(o + (dm.fp8 ? Tk * dm.f / 32 : 0));
   L.total = o;
   return L;
 }
@@ -116,7 +121,11 @@ moe_status_t check_dims(const moe_dims_t* d, Dims* out) {
                        (d->act_dtype == MOE_DTYPE_BF16 && d->w_dtype == MOE_DTYPE_MXFP4) ||
                        (d->act_dtype == MOE_DTYPE_BF16 && d->w_dtype == MOE_DTYPE_NVFP4);
   if (!pair_ok) return MOE_ERR_UNSUPPORTED;
-  *out = Dims{d->T, d->d, d->E, d->k, d->f, d->act_dtype, d->w_dtype};
+  if (d->flags & ~MOE_FLAG_FP8_ACTIVATIONS) return MOE_ERR_INVALID_ARGUMENT;
+  Dims dm{d->T, d->d, d->E, d->k, d->f, d->act_dtype, d->w_dtype};
+  dm.fp8 = (d->flags & MOE_FLAG_FP8_ACTIVATIONS) != 0;
+  if (dm.fp8 && !fp8_path_ok(dm)) return MOE_ERR_UNSUPPORTED;
+  *out = dm;
   return MOE_OK;
 }
 
@@ -145,7 +154,18 @@ moe_status_t check_weights(const moe_expert_weights_t* w, const Dims& dm, Weight
 
 // Expert FFN on a prepared plan (offsets, sorted_src, active list).
 hipError_t run_expert_ffn(const Dims& dm, const void* x, const Plan& p, const Weights& w,
-                          void* h, float* y_sorted, hipStream_t s) {
+                          char* ws, const WsLayout& L, float* y_sorted, hipStream_t s) {
+  if (dm.fp8) {
+    uint8_t* xq = reinterpret_cast<uint8_t*>(ws + L.xq);
+    uint8_t* xs = reinterpret_cast<uint8_t*>(ws + L.xs);
+    uint8_t* hq = reinterpret_cast<uint8_t*>(ws + L.hq);
+    uint8_t* hs = reinterpret_cast<uint8_t*>(ws + L.hs);
+    hipError_t e = launch_quantize_mxfp8(x, dm.T, dm.d, xq, xs, s);
+    if (e == hipSuccess) e = launch_gg_f8_gate_up(dm, xq, xs, p, w, hq, hs, s);
+    if (e == hipSuccess) e = launch_gg_f8_down(dm, hq, hs, p, w, y_sorted, s);
+    return e;
+  }
+  void* h = ws + L.h;
   if (grouped_gemm_ok(dm)) {
     hipError_t e = launch_gg_gate_up(dm, x, p, w, h, s);
     if (e != hipSuccess) return e;
@@ -219,7 +239,7 @@ moe_status_t moe_expert_ffn(const moe_dims_t* dims, const void* x, const int32_t
   p.sorted_src = const_cast<int*>(sorted_src);
   hipError_t e = launch_plan_from_offsets(offsets, dm.E, p, s);
   if (e == hipSuccess)
-    e = run_expert_ffn(dm, x, p, w, static_cast<char*>(workspace) + L.h, y_sorted, s);
+    e = run_expert_ffn(dm, x, p, w, static_cast<char*>(workspace), L, y_sorted, s);
   return device_status(e);
 }
 
@@ -260,7 +280,7 @@ moe_status_t moe_layer_forward(const moe_dims_t* dims, const void* x, const void
 
   hipError_t e = hipSuccess;
   if (w_router) e = launch_router_logits(x, w_router, logits, dm.T, dm.d, dm.E, dm.act, s);
-  if (gemv_down_combine_t1_ok(dm)) {
+  if (!dm.fp8 && gemv_down_combine_t1_ok(dm)) {
     // single token: one-wave route+plan, gate/up GEMV, down GEMV + combine
     if (e == hipSuccess) e = launch_route_plan_t1(logits, dm.E, dm.k, topk_idx, topk_w, p, s);
     if (e == hipSuccess) e = launch_gemv_gate_up(dm, x, p, w, h, s);
@@ -275,7 +295,7 @@ moe_status_t moe_layer_forward(const moe_dims_t* dims, const void* x, const void
     if (e == hipSuccess) e = launch_route_topk(logits, dm.T, dm.E, dm.k, topk_idx, topk_w, s);
     if (e == hipSuccess) e = launch_permute(topk_idx, dm.T, dm.E, dm.k, p, true, s);
   }
-  if (e == hipSuccess) e = run_expert_ffn(dm, x, p, w, h, y_sorted, s);
+  if (e == hipSuccess) e = run_expert_ffn(dm, x, p, w, ws, L, y_sorted, s);
   if (e == hipSuccess) e = launch_combine(dm, y_sorted, p.dest_row, topk_w, out, s);
   return device_status(e);
 }

@@ -63,6 +63,8 @@ struct GGArgs {
   const uint8_t* s1;
   const float* t0;        // NVFP4 matrix scales [E] of w0 / w1
   const float* t1;
+  const uint8_t* a_scale; // FP8 activations: E8M0 scales [rows][K/32] of a_src
+  void* out_scale;        // FP8 gate/up: E8M0 scales [T*k][N/32] of the fp8 h in out
   const int* mtiles;
   const int* num_mtiles;
   void* out;              // gate/up: h bf16 [T*k][N]; down: y_sorted fp32 [T*k][N]
@@ -838,6 +840,328 @@ __global__ __launch_bounds__(kThreads) void gg_mx_group_kernel(GGArgs a) {
   }
 }
 
+// ---- FP8 activations x MX-FP4 weights on the scaled MFMA.
+//
+// The pages run the experts with FP8 compute and 4-bit weights
+// (SGLang-TorchTPU on TPU v7 page, "Results").  Here the activation operand
+// (x for gate/up, h for down) is MXFP8, E4M3 values with one E8M0 scale per
+// 32 elements, and the weights MX-FP4; v_mfma_scale_f32_32x32x64_f8f6f4 takes
+// both with their block scales, so no code is converted in registers and one
+// instruction covers K = 64.  Operand layout of that instruction, checked on
+// the device: a weight lane (column c = lane % 32, half h = lane / 32) holds
+// the 32 codes of K-block h, low nibble first, and supplies that block's scale;
+// an activation lane (row lane % 32, half h) holds K [16h, 16h+16) and
+// [32+16h, 32+16h+16) and supplies the scale of K-block h of its row.
+//
+// Tile, wave grid, code groups, weight scales, tile order and waits are those
+// of gg_mx_group_kernel.  The activation stage is 128 rows x 64 fp8 bytes (one
+// DMA instruction per wave, 16 rows of 4 units); the activation scales of a
+// group (8 bytes per row) come with one 32-lane 4-byte DMA per wave at the
+// group's first step.  The gate/up epilogue writes h as MXFP8: each wave's 32
+// columns are one block, whose maximum it takes across the 32 lanes of a half.
+constexpr int kF8A = 3;                                   // activation stages
+constexpr int kStageA8 = BM * 64;                         // 8 KB
+constexpr int kAScalesGroup = BM * 8;                     // 1 KB
+constexpr int kF8Lds = kF8A * kStageA8 + kGroupBufs * (kCodesGroup + BN * 8 + kAScalesGroup);
+
+// 16-byte unit u of 64-byte activation row r lives at unit u ^ g8(r): a
+// fragment read (16 consecutive rows, one unit) then touches distinct bank
+// groups in 8- and 16-lane groups (checked on the CPU).
+__device__ __forceinline__ int a8_off(int row, int unit) {
+  const int g = ((row >> 2) & 1) | ((((row >> 1) ^ (row >> 3)) & 1) << 1);
+  return row * 64 + ((unit ^ g) << 4);
+}
+
+typedef int i32x8_t __attribute__((ext_vector_type(8)));
+
+template <int VM>
+__device__ __forceinline__ void f8_step(const char* st, const char* cb, const char* sb, const char* ab,
+                                        int p, const int* arow, const int* brow, int half,
+                                        f32x16_t (&acc)[2][2]) {
+  if constexpr (VM > 0) {
+    i32x8_t bv[2];
+    int bs[2];
+#pragma unroll
+    for (int m = 0; m < 2; ++m) {
+      const int u = 2 * p + half;  // the lane's 32-element block inside the line
+      const u32x4 c = *reinterpret_cast<const u32x4*>(cb + brow[m] * 128 + ((u ^ (brow[m] & 7)) << 4));
+      bv[m] = i32x8_t{(int)c.x, (int)c.y, (int)c.z, (int)c.w, 0, 0, 0, 0};
+      bs[m] = static_cast<uint8_t>(sb[brow[m] * 8 + u]);
+    }
+#pragma unroll
+    for (int mi = 0; mi < VM; ++mi) {
+      const u32x4 lo = *reinterpret_cast<const u32x4*>(st + a8_off(arow[mi], half));
+      const u32x4 hi = *reinterpret_cast<const u32x4*>(st + a8_off(arow[mi], 2 + half));
+      const i32x8_t av{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+      const int as = static_cast<uint8_t>(ab[arow[mi] * 8 + 2 * p + half]);
+#pragma unroll
+      for (int m = 0; m < 2; ++m)
+        acc[m][mi] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av, bv[m], acc[m][mi], 0, 4, 0, as,
+                                                                     0, bs[m]);
+    }
+  }
+}
+
+// OCP FP8 E4M3 byte of v (already divided by its block scale): round to
+// nearest even, saturating at +-448 (the convert itself would give NaN).
+__device__ __forceinline__ uint32_t e4m3_byte(float v) {
+  v = fminf(fmaxf(v, -448.0f), 448.0f);
+  return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(v, v, 0, false) & 0xffu;
+}
+
+// E8M0 byte of a block whose largest magnitude is amax: 2^(floor(log2 amax)
+// - 8), the MX rule for E4M3 elements, kept in [1, 254].
+__device__ __forceinline__ uint32_t mxfp8_scale_byte(float amax) {
+  const int ef = (int)((__float_as_uint(amax) >> 23) & 0xffu);
+  return (uint32_t)min(max(ef - 8, 1), 254);
+}
+
+template <bool GATEUP>
+__global__ __launch_bounds__(kThreads) void gg_f8f4_kernel(GGArgs a) {
+  __shared__ __align__(1024) char lds[kF8Lds];
+  char* const lds_a = lds;
+  char* const lds_c = lds + kF8A * kStageA8;
+  char* const lds_s = lds_c + kGroupBufs * kCodesGroup;
+  char* const lds_as = lds_s + kGroupBufs * BN * 8;
+  const int tid = threadIdx.x;
+  const int lane = lane_id();
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave >> 2;
+  const int wn = wave & 3;
+  const int half = lane >> 5;
+  const int cl = lane & 31;
+
+  // ---- tile (as in the other kernels)
+  const int num_tiles = *a.num_mtiles * a.ntiles;
+  const int per_xcd = (num_tiles + kXcds - 1) / kXcds;
+  const int slot = blockIdx.x / kXcds;
+  if (slot >= per_xcd) return;
+  const int L = (blockIdx.x % kXcds) * per_xcd + slot;
+  if (L >= num_tiles) return;
+  const int* eq = a.mtiles + kMtileInts * (L / a.ntiles);
+  const int e = eq[0];
+  const int first_mt = eq[3];
+  const int nmt = eq[4];
+  const int local = L - first_mt * a.ntiles;
+  const int ntile = local / nmt;
+  const int* em = a.mtiles + kMtileInts * (first_mt + (local - ntile * nmt));
+  const int row0 = em[1];
+  const int nrows = em[2];
+  const int nbase = ntile * (GATEUP ? BN / 2 : BN);
+  const int nk = a.K / BK;
+  const int ng = nk / kGroupSteps;
+
+  // weight row r of the tile (0..255) -> its codes and scales
+  auto wrow = [&](int r, const char*& code, const uint8_t*& scale) {
+    const void* w = a.w0;
+    const uint8_t* sc = a.s0;
+    int col;
+    if (GATEUP) {
+      const bool up = r >= BN / 2;
+      w = up ? a.w1 : a.w0;
+      sc = up ? a.s1 : a.s0;
+      col = nbase + (up ? r - BN / 2 : r);
+    } else {
+      col = nbase + r;
+    }
+    col = min(col, a.N - 1);
+    code = reinterpret_cast<const char*>(w) + ((size_t)e * a.N + col) * (a.K / 2);
+    scale = sc + ((size_t)e * a.N + col) * (a.K / 32);
+  };
+  // activation row r of the tile (0..127) -> source row index
+  auto arow_src = [&](int r) -> size_t {
+    const int src = row0 + min(r, nrows - 1);
+    return GATEUP ? (size_t)(a.sorted_src[src] / a.k) : (size_t)src;
+  };
+
+  // ---- activation DMA: wave w fills rows 16w .. 16w+15; lane -> row
+  // 16w + lane/4, slot lane%4 <- global unit slot ^ g8(row)
+  const char* asrc;
+  {
+    const int r = 16 * wave + (lane >> 2);
+    const int g = ((r >> 2) & 1) | ((((r >> 1) ^ (r >> 3)) & 1) << 1);
+    asrc = reinterpret_cast<const char*>(a.a_src) + arow_src(r) * (size_t)a.K + (((lane & 3) ^ g) << 4);
+  }
+  char* const adst = lds_a + 16 * wave * 64;
+  // ---- activation scale DMA: lanes 0..31 of wave w fill rows 16w + lane/2,
+  // word lane%2 of the row's 8 group bytes
+  const uint8_t* assrc = a.a_scale + arow_src(16 * wave + ((lane & 31) >> 1)) * (size_t)(a.K / 32) +
+                         4 * (lane & 1);
+  // ---- code and weight-scale DMA sources (as gg_mx_group_kernel)
+  const int slot16 = lane & 7;
+  const char* csrc[kGroupSteps];
+#pragma unroll
+  for (int p = 0; p < kGroupSteps; ++p) {
+    const int r = 32 * wave + 8 * p + (lane >> 3);
+    const char* code;
+    const uint8_t* scale;
+    wrow(r, code, scale);
+    csrc[p] = code + ((slot16 ^ (r & 7)) << 4);
+  }
+  const uint8_t* ssrc;
+  {
+    const int d = kWave * wave + lane;
+    const char* code;
+    wrow(d >> 1, code, ssrc);
+    ssrc += 4 * (d & 1);
+  }
+
+  auto issue_codes = [&](int g, int p) {
+    char* d = lds_c + (g % kGroupBufs) * kCodesGroup + (32 * wave + 8 * p) * 128;
+    dma16<0>(csrc[p] + (size_t)min(g, ng - 1) * 128, d);
+  };
+  auto issue_scales = [&](int g) {  // weight and activation scales of group g
+    const int gs = min(g, ng - 1);
+    char* d = lds_s + (g % kGroupBufs) * (BN * 8) + wave * kWave * 4;
+    __builtin_amdgcn_global_load_lds(ssrc + (size_t)gs * 8, (lds_void_t*)d, 4, 0, 0);
+    char* da = lds_as + (g % kGroupBufs) * kAScalesGroup + 16 * wave * 8;
+    if (lane < 32) __builtin_amdgcn_global_load_lds(assrc + (size_t)gs * 8, (lds_void_t*)da, 4, 0, 0);
+  };
+  auto issue_a = [&](int kk) {
+    dma16<kAuxA>(asrc + (size_t)min(kk, nk - 1) * 64, adst + (kk % kF8A) * kStageA8);
+  };
+
+  int arow[2], brow[2];
+#pragma unroll
+  for (int mi = 0; mi < 2; ++mi) arow[mi] = 64 * wm + 32 * mi + cl;
+#pragma unroll
+  for (int m = 0; m < 2; ++m) brow[m] = GATEUP ? (m * (BN / 2) + 32 * wn + cl) : (64 * wn + 32 * m + cl);
+
+  f32x16_t acc[2][2];
+#pragma unroll
+  for (int m = 0; m < 2; ++m)
+#pragma unroll
+    for (int mi = 0; mi < 2; ++mi) acc[m][mi] = f32x16_t{};
+
+  const int vm = min(max((nrows + 31) / 32 - 2 * wm, 0), 2);
+
+  // ---- prologue: groups 0 and 1, then activation steps 0 and 1 (youngest)
+#pragma unroll
+  for (int g = 0; g < 2; ++g) {
+#pragma unroll
+    for (int p = 0; p < kGroupSteps; ++p) issue_codes(g, p);
+    issue_scales(g);
+  }
+  asm volatile("" ::: "memory");
+  issue_a(0);
+  issue_a(1);
+
+  // Loads per step: one code DMA, at a group's first step the weight- and
+  // activation-scale DMAs, then the activation DMA (youngest).  Younger than
+  // activation stage kk: the loads of step kk-1 (two, four after a group's
+  // first step); at step 0 only stage 1's one.
+  auto main_loop = [&](auto vm_c) {
+    constexpr int VM = decltype(vm_c)::value;
+    for (int g = 0; g < ng; ++g) {
+      const char* cb = lds_c + (g % kGroupBufs) * kCodesGroup;
+      const char* sb = lds_s + (g % kGroupBufs) * (BN * 8);
+      const char* ab = lds_as + (g % kGroupBufs) * kAScalesGroup;
+#pragma unroll
+      for (int p = 0; p < kGroupSteps; ++p) {
+        const int kk = kGroupSteps * g + p;
+        if (p == 1)
+          wait_and_barrier<4>();
+        else if (p == 0)
+          wait_and_barrier<1>();
+        else
+          wait_and_barrier<2>();
+        issue_codes(g + 2, p);
+        if (p == 0) issue_scales(g + 2);
+        asm volatile("" ::: "memory");
+        issue_a(kk + 2);
+        f8_step<VM>(lds_a + (kk % kF8A) * kStageA8, cb, sb, ab, p, arow, brow, half, acc);
+      }
+    }
+  };
+  if (vm == 2)
+    main_loop(std::integral_constant<int, 2>{});
+  else if (vm == 1)
+    main_loop(std::integral_constant<int, 1>{});
+  else
+    main_loop(std::integral_constant<int, 0>{});
+  __builtin_amdgcn_s_waitcnt(0);
+
+  // ---- epilogue
+  if (GATEUP) {
+    // h = silu(g) * u as MXFP8: the wave's 32 columns are one scale block
+    const int col = nbase + 32 * wn + cl;
+    uint8_t* hq = reinterpret_cast<uint8_t*>(a.out);
+    uint8_t* hs = reinterpret_cast<uint8_t*>(a.out_scale);
+#pragma unroll
+    for (int mi = 0; mi < 2; ++mi) {
+      if (mi < vm) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int row = 64 * wm + 32 * mi + 8 * (i >> 2) + 4 * half + (i & 3);
+          const float g = acc[0][mi][i];
+          const float h = g / (1.0f + expf(-g)) * acc[1][mi][i];
+          float amax = fabsf(h);
+#pragma unroll
+          for (int o = 1; o < 32; o <<= 1) amax = fmaxf(amax, __shfl_xor(amax, o, kWave));
+          const uint32_t sbyte = mxfp8_scale_byte(amax);
+          const float inv = __uint_as_float((254u - sbyte) << 23);  // 2^(127 - sbyte)
+          if (row < nrows) {
+            const size_t r = (size_t)(row0 + row);
+            hq[r * a.N + col] = (uint8_t)e4m3_byte(h * inv);
+            if (cl == 0) hs[r * (a.N / 32) + col / 32] = (uint8_t)sbyte;
+          }
+        }
+      }
+    }
+  } else {
+#pragma unroll
+    for (int mi = 0; mi < 2; ++mi) {
+      if (mi < vm) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int row = 64 * wm + 32 * mi + 8 * (i >> 2) + 4 * half + (i & 3);
+          if (row < nrows) {
+            const size_t orow = (size_t)(row0 + row) * a.N;
+#pragma unroll
+            for (int m = 0; m < 2; ++m) {
+              const int col = nbase + 64 * wn + 32 * m + cl;
+              reinterpret_cast<float*>(a.out)[orow + col] = acc[m][mi][i];
+            }
+          }
+        }
+      }
+    }
+  }
+}
+
+// x [T][K] bf16 -> MXFP8: one thread per 32-element block.
+__global__ __launch_bounds__(256) void quantize_mxfp8_kernel(const uint16_t* __restrict__ x, long long nblocks,
+                                                             uint8_t* __restrict__ q, uint8_t* __restrict__ qs) {
+  const long long b = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+  if (b >= nblocks) return;
+  const u32x4* src = reinterpret_cast<const u32x4*>(x + 32 * b);
+  float v[32];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const u32x4 w = src[j];
+    const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      v[8 * j + 2 * t] = __uint_as_float(ww[t] << 16);
+      v[8 * j + 2 * t + 1] = __uint_as_float(ww[t] & 0xffff0000u);
+    }
+  }
+  float amax = 0.f;
+#pragma unroll
+  for (int j = 0; j < 32; ++j) amax = fmaxf(amax, fabsf(v[j]));
+  const uint32_t sbyte = mxfp8_scale_byte(amax);
+  const float inv = __uint_as_float((254u - sbyte) << 23);
+  uint32_t out[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j)
+    out[j] = e4m3_byte(v[4 * j] * inv) | (e4m3_byte(v[4 * j + 1] * inv) << 8) |
+             (e4m3_byte(v[4 * j + 2] * inv) << 16) | (e4m3_byte(v[4 * j + 3] * inv) << 24);
+  u32x4* dst = reinterpret_cast<u32x4*>(q + 32 * b);
+  dst[0] = u32x4{out[0], out[1], out[2], out[3]};
+  dst[1] = u32x4{out[4], out[5], out[6], out[7]};
+  qs[b] = (uint8_t)sbyte;
+}
+
 // K-steps of loads in flight (register budget of two waves per SIMD).
 constexpr int kDepthDirect = 2;  // gg_direct_b_kernel, MX-FP4 weights
 
@@ -886,7 +1210,7 @@ hipError_t launch_gg_gate_up(const Dims& dm, const void* x, const Plan& p, const
                              void* h, hipStream_t s) {
   LaunchTimer tm("gg_gate_up", s);
   const int tc = tile_cols(dm, true);
-  GGArgs a{x, p.sorted_src, w.wg, w.wu, w.sg, w.su, w.tg, w.tu, p.mtiles, p.num_mtiles, h,
+  GGArgs a{x, p.sorted_src, w.wg, w.wu, w.sg, w.su, w.tg, w.tu, nullptr, nullptr, p.mtiles, p.num_mtiles, h,
            dm.d, dm.f, dm.k, (dm.f + tc - 1) / tc};
   return launch_gg<true>(dm, a, s);
 }
@@ -895,9 +1219,46 @@ hipError_t launch_gg_down(const Dims& dm, const void* h, const Plan& p, const We
                           float* y_sorted, hipStream_t s) {
   LaunchTimer tm("gg_down", s);
   const int tc = tile_cols(dm, false);
-  GGArgs a{h, nullptr, w.wd, nullptr, w.sd, nullptr, w.td, nullptr, p.mtiles, p.num_mtiles, y_sorted,
+  GGArgs a{h, nullptr, w.wd, nullptr, w.sd, nullptr, w.td, nullptr, nullptr, nullptr, p.mtiles, p.num_mtiles,
+           y_sorted,
            dm.f, dm.d, dm.k, (dm.d + tc - 1) / tc};
   return launch_gg<false>(dm, a, s);
+}
+
+bool fp8_path_ok(const Dims& dm) {
+  return dm.act == kBF16 && dm.wfmt == kMXFP4 && mx_grouped(dm.d) && mx_grouped(dm.f);
+}
+
+hipError_t launch_quantize_mxfp8(const void* x, long long rows, int K, uint8_t* q, uint8_t* qs,
+                                 hipStream_t s) {
+  LaunchTimer tm("quantize_mxfp8", s);
+  const long long nb = rows * (K / 32);
+  if (nb == 0) return hipSuccess;
+  const dim3 grid((unsigned)((nb + 255) / 256)), block(256);
+  quantize_mxfp8_kernel<<<grid, block, 0, s>>>(reinterpret_cast<const uint16_t*>(x), nb, q, qs);
+  return hipGetLastError();
+}
+
+hipError_t launch_gg_f8_gate_up(const Dims& dm, const uint8_t* xq, const uint8_t* xs, const Plan& p,
+                                const Weights& w, uint8_t* hq, uint8_t* hs, hipStream_t s) {
+  LaunchTimer tm("gg_gate_up", s);
+  GGArgs a{xq, p.sorted_src, w.wg, w.wu, w.sg, w.su, nullptr, nullptr, xs, hs, p.mtiles, p.num_mtiles,
+           hq, dm.d, dm.f, dm.k, dm.f / (BN / 2)};
+  const size_t max_tiles = grouped_gemm_max_mtiles(dm) * (size_t)a.ntiles;
+  const dim3 grid((unsigned)((max_tiles + kXcds - 1) / kXcds * kXcds)), block(kThreads);
+  gg_f8f4_kernel<true><<<grid, block, 0, s>>>(a);
+  return hipGetLastError();
+}
+
+hipError_t launch_gg_f8_down(const Dims& dm, const uint8_t* hq, const uint8_t* hs, const Plan& p,
+                             const Weights& w, float* y_sorted, hipStream_t s) {
+  LaunchTimer tm("gg_down", s);
+  GGArgs a{hq, nullptr, w.wd, nullptr, w.sd, nullptr, nullptr, nullptr, hs, nullptr, p.mtiles,
+           p.num_mtiles, y_sorted, dm.f, dm.d, dm.k, dm.d / BN};
+  const size_t max_tiles = grouped_gemm_max_mtiles(dm) * (size_t)a.ntiles;
+  const dim3 grid((unsigned)((max_tiles + kXcds - 1) / kXcds * kXcds)), block(kThreads);
+  gg_f8f4_kernel<false><<<grid, block, 0, s>>>(a);
+  return hipGetLastError();
 }
 
 }  // namespace moe

@@ -35,6 +35,7 @@ constexpr int kGemmMinT = 48;
 
 struct Dims {
   int T, d, E, k, f, act, wfmt;
+  bool fp8 = false;  // MXFP8 activations on the scaled MFMA
   long long Tk() const { return (long long)T * k; }
 };
 
@@ -47,7 +48,9 @@ struct Weights {
 // Workspace layout (byte offsets, each 256-aligned).
 struct WsLayout {
   size_t counts, offsets, sorted_src, dest_row, active, num_active, slot_info, mtiles, num_mtiles;
-  size_t h, y_sorted, total;
+  size_t h, y_sorted;
+  size_t xq, xs, hq, hs;  // FP8 activations: x and h as MXFP8 (values, E8M0 scales)
+  size_t total;
 };
 WsLayout ws_layout(const Dims& dm);
 
@@ -103,6 +106,14 @@ bool grouped_gemm_ok(const Dims& dm);
 size_t grouped_gemm_max_mtiles(const Dims& dm);
 hipError_t launch_gg_gate_up(const Dims& dm, const void* x, const Plan& p, const Weights& w,
                              void* h, hipStream_t s);
+// FP8 activations (MXFP8) x MX-FP4 weights on the scaled MFMA.
+bool fp8_path_ok(const Dims& dm);
+hipError_t launch_quantize_mxfp8(const void* x, long long rows, int K, uint8_t* q, uint8_t* qs,
+                                 hipStream_t s);
+hipError_t launch_gg_f8_gate_up(const Dims& dm, const uint8_t* xq, const uint8_t* xs, const Plan& p,
+                                const Weights& w, uint8_t* hq, uint8_t* hs, hipStream_t s);
+hipError_t launch_gg_f8_down(const Dims& dm, const uint8_t* hq, const uint8_t* hs, const Plan& p,
+                             const Weights& w, float* y_sorted, hipStream_t s);
 hipError_t launch_gg_down(const Dims& dm, const void* h, const Plan& p, const Weights& w,
                           float* y_sorted, hipStream_t s);
 hipError_t launch_combine(const Dims& dm, const float* y_sorted, const int* dest_row,

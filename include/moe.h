@@ -80,12 +80,29 @@ typedef enum {
   MOE_DTYPE_NVFP4 = 3
 } moe_dtype_t;
 
+/* Compute options (moe_dims_t.flags).
+ *  MOE_FLAG_FP8_ACTIVATIONS: run the expert products with FP8 activations,
+ *    the pages' production precision ("FP8 compute" with 4-bit expert
+ *    weights: SGLang-TorchTPU on TPU v7 page, "Results").  x and h are
+ *    quantised to MXFP8 (OCP FP8 E4M3 values, one E8M0 scale per 32
+ *    elements along the reduction dimension: scale 2^(floor(log2 amax) - 8),
+ *    elements rounded to nearest even and saturated at +-448) and multiplied
+ *    with MX-FP4 weights on the gfx950 scaled MFMA.  Requires act BF16,
+ *    weights MXFP4, d and f multiples of 256 (else MOE_ERR_UNSUPPORTED); x, out
+ *    and every other buffer keep their layouts.  Applies at every T (the
+ *    grouped MFMA path is then used for decode too).  Results are defined
+ *    with the quantised activations; they differ from the bf16 path by the
+ *    FP8 rounding (about 2-4 % relative). */
+enum { MOE_FLAG_FP8_ACTIVATIONS = 1 };
+
 /* Layer shape.  T tokens of hidden size d, E experts of FFN width f, each
- * token routed to k experts.  act_dtype / w_dtype hold moe_dtype_t values. */
+ * token routed to k experts.  act_dtype / w_dtype hold moe_dtype_t values;
+ * flags holds MOE_FLAG_* bits (0 for the default bf16/fp32 compute). */
 typedef struct {
   int32_t T, d, E, k, f;
   int32_t act_dtype;
   int32_t w_dtype;
+  int32_t flags;
 } moe_dims_t;
 
 /* Stacked expert weights (device pointers, layouts above).  s_* are the

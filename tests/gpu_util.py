@@ -76,12 +76,14 @@ def check_routing(res, logits_host, k, E):
     return idx, w
 
 
-def run_layer_and_oracle(wl: Workload, x, w, w_r, logits, k=None, sample=None):
+def run_layer_and_oracle(wl: Workload, x, w, w_r, logits, k=None, sample=None, fp8=False):
     """Run moe_layer_forward on the device and the oracle on the same bytes.
-    ``sample``: token indices to check (the layer is per-token independent)."""
+    ``sample``: token indices to check (the layer is per-token independent).
+    ``fp8``: FP8-activation mode on both sides (the oracle quantises x and h
+    to MXFP8 with its own code)."""
     from expert_ffn_layer_softmax_amd import moe_layer_forward
     k = wl.k if k is None else k
-    res = moe_layer_forward(x, w, k, logits=logits, w_router=w_r)
+    res = moe_layer_forward(x, w, k, logits=logits, w_router=w_r, fp8=fp8)
     torch.cuda.synchronize()
     lg = res["logits"].cpu().numpy()
     xh = to_host_act(x)
@@ -90,6 +92,7 @@ def run_layer_and_oracle(wl: Workload, x, w, w_r, logits, k=None, sample=None):
         assert rel_l2(lg.astype(np.float64), ref_logits) <= 1e-5
     check_routing(res, lg, k, wl.E)
     S = np.arange(wl.T) if sample is None else np.asarray(sample)
-    ref = oracle.layer(xh[S], lg[S], k, expert_getter(w, wl.wfmt), E=wl.E)
+    ref = oracle.layer(xh[S], lg[S], k, expert_getter(w, wl.wfmt), E=wl.E,
+                       act_quant=oracle.quantize_mxfp8 if fp8 else None)
     got = to_host_act(res["out"])[S]
     return got, ref, res

@@ -39,8 +39,8 @@ def test_python_binding_names_match_abi(m):
         assert callable(getattr(m, n))
 
 
-def _dims(m, T=4, d=64, E=8, k=2, f=32, act=1, w=1):
-    return m._lib.MoeDims(T, d, E, k, f, act, w)
+def _dims(m, T=4, d=64, E=8, k=2, f=32, act=1, w=1, flags=0):
+    return m._lib.MoeDims(T, d, E, k, f, act, w, flags)
 
 
 def _ws(m, dims):
@@ -66,6 +66,17 @@ def test_workspace_size_validation(m):
     assert _ws(m, _dims(m, act=1, w=3))[0] == OK            # NVFP4 weights
     assert _ws(m, _dims(m, act=3, w=3))[0] == UNSUPPORTED   # NVFP4 activations
     assert _ws(m, _dims(m, act=1, w=4))[0] == INVALID
+    # FP8 activations: MX-FP4 weights, bf16 activations, d and f multiples of 256
+    assert _ws(m, _dims(m, d=256, f=512, w=2, flags=1))[0] == OK
+    assert _ws(m, _dims(m, d=256, f=512, w=2, flags=2))[0] == INVALID
+    assert _ws(m, _dims(m, d=256, f=512, w=1, flags=1))[0] == UNSUPPORTED   # bf16 weights
+    assert _ws(m, _dims(m, d=256, f=512, w=3, flags=1))[0] == UNSUPPORTED   # NVFP4 weights
+    assert _ws(m, _dims(m, d=320, f=512, w=2, flags=1))[0] == UNSUPPORTED   # d % 256
+    # the FP8 workspace holds the MXFP8 activations instead of the bf16 h
+    T, k, d, f = 64, 8, 256, 512
+    w8 = _ws(m, _dims(m, T=T, d=d, E=16, k=k, f=f, w=2, flags=1))[1]
+    w16 = _ws(m, _dims(m, T=T, d=d, E=16, k=k, f=f, w=2))[1]
+    assert w8 - w16 >= T * d + T * d // 32 + T * k * f // 32 - T * k * f - 4 * 256
     assert m.lib.moe_workspace_size(None, None) == INVALID
 
 

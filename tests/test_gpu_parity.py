@@ -206,20 +206,54 @@ def test_single_token_fused_path_equals_stagewise(wfmt, k):
                        staged.view(torch.int16) if act == "bf16" else staged.view(torch.int32))
 
 
+# ------------------------------------------------- FP8 activations (MXFP8)
+# Both sides quantise x and h to MXFP8; they differ by fp32 vs fp64
+# accumulation and, rarely, an FP8 rounding decision that the accumulation
+# difference moves across a boundary, so the bf16 tolerance applies.
+FP8_CASES = [
+    # name, T, d, E, k, f
+    ("fp8_t1", 1, 256, 16, 4, 256),
+    ("fp8_t16", 16, 512, 32, 8, 256),
+    ("fp8_t100", 100, 256, 8, 4, 512),
+    ("fp8_hot", 700, 512, 5, 2, 512),       # several m-tiles per expert
+    ("fp8_tails", 150, 768, 6, 2, 256),     # 3 down n-tiles, ragged m-tiles
+]
+
+
+@pytest.mark.parametrize("case", FP8_CASES, ids=[c[0] for c in FP8_CASES])
+def test_layer_fp8_activations(case):
+    name, T, d, E, k, f = case
+    log(f"fp8 layer {name}")
+    wl = Workload(name, T=T, d=d, E=E, k=k, f=f, act="bf16", wfmt="mxfp4",
+                  seed=zlib.crc32(name.encode()) % 100000,
+                  x_std=1.0, wg_std=d ** -0.5, wu_std=d ** -0.5, wd_std=f ** -0.5)
+    x, w, w_r, logits = make_inputs(wl)
+    got, ref, _ = run_layer_and_oracle(wl, x, w, w_r, logits, fp8=True)
+    err = rel_l2(got, ref["out"])
+    # the FP8 rounding is real: the bf16-activation result differs by about 2-4 %
+    plain = oracle.layer(to_host_act(x), logits.cpu().numpy(), k, expert_getter(w, "mxfp4"), E=E)
+    sep = rel_l2(plain["out"], ref["out"])
+    log(f"  rel_l2={err:.3e} (bf16-activation reference differs by {sep:.3e})")
+    assert err <= 5e-3
+    assert sep > 5e-3
+
+
 # ------------------------------------------------------------ HIP graphs
 @pytest.mark.parametrize("T,wfmt", [(1, "bf16"), (16, "bf16"), (100, "bf16"), (100, "mxfp4"),
-                                    (100, "nvfp4")])
+                                    (100, "nvfp4"), (100, "mxfp4_fp8")])
 def test_hip_graph_replay(T, wfmt):
     """A captured layer replays to the eager result, bit for bit, after eager
     calls with other routing have rewritten the same workspace and outputs."""
     from expert_ffn_layer_softmax_amd import moe_layer_forward
     log(f"graph T={T} {wfmt}")
+    fp8 = wfmt.endswith("_fp8")
+    wfmt = wfmt[:-4] if fp8 else wfmt
     k = 8
     wl = Workload("graph", T=T, d=512, E=32, k=k, f=256, act="bf16", wfmt=wfmt, seed=71 + T,
                   x_std=1.0, wg_std=512 ** -0.5, wu_std=512 ** -0.5, wd_std=256 ** -0.5)
     x, w, _, logits = make_inputs(wl)
     other_logits = torch.randn(T, wl.E, generator=torch.Generator().manual_seed(T)).cuda()
-    eager = moe_layer_forward(x, w, k, logits=logits)
+    eager = moe_layer_forward(x, w, k, logits=logits, fp8=fp8)
     ref_out, ref_idx = eager["out"].clone(), eager["topk_idx"].clone()
     ws = eager["workspace"]
     out = torch.empty_like(ref_out)
@@ -228,15 +262,15 @@ def test_hip_graph_replay(T, wfmt):
     side = torch.cuda.Stream()
     side.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(side):
-        moe_layer_forward(x, w, k, logits=logits, topk_idx=idx, topk_w=tw, out=out, workspace=ws)
+        moe_layer_forward(x, w, k, logits=logits, topk_idx=idx, topk_w=tw, out=out, workspace=ws, fp8=fp8)
     torch.cuda.current_stream().wait_stream(side)
     torch.cuda.synchronize()
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g):
-        moe_layer_forward(x, w, k, logits=logits, topk_idx=idx, topk_w=tw, out=out, workspace=ws)
+        moe_layer_forward(x, w, k, logits=logits, topk_idx=idx, topk_w=tw, out=out, workspace=ws, fp8=fp8)
     torch.cuda.synchronize()
     for _ in range(3):
-        moe_layer_forward(x, w, k, logits=other_logits, topk_idx=idx, topk_w=tw, out=out, workspace=ws)
+        moe_layer_forward(x, w, k, logits=other_logits, topk_idx=idx, topk_w=tw, out=out, workspace=ws, fp8=fp8)
         torch.cuda.synchronize()
         g.replay()
         torch.cuda.synchronize()
@@ -314,16 +348,17 @@ def test_verify_bf16_full(full_bf16_weights):
     assert err <= 5e-3
 
 
-@pytest.mark.parametrize("name", ["prefill_bf16", "prefill_mxfp4", "prefill_nvfp4"])
+@pytest.mark.parametrize("name", ["prefill_bf16", "prefill_mxfp4", "prefill_nvfp4", "prefill_mxfp4_fp8"])
 def test_prefill_full_sampled(name, full_bf16_weights):
     """T=4096 with skewed load: routing checked in full; outputs on sampled
     tokens (each token's output depends only on its own row and logits)."""
-    wl = WORKLOADS[name]
+    fp8 = name.endswith("_fp8")
+    wl = WORKLOADS[name[:-4] if fp8 else name]
     log(f"{name} full (T=4096), sampled tokens")
     w = full_bf16_weights if wl.wfmt == "bf16" else gen_expert_weights(wl, "cuda")
     x, w, w_r, logits = make_inputs(wl, weights=w)
     from expert_ffn_layer_softmax_amd import moe_layer_forward
-    res = moe_layer_forward(x, w, wl.k, logits=logits)
+    res = moe_layer_forward(x, w, wl.k, logits=logits, fp8=fp8)
     torch.cuda.synchronize()
     lg = res["logits"].cpu().numpy()
     check_routing(res, lg, wl.k, wl.E)
@@ -335,11 +370,12 @@ def test_prefill_full_sampled(name, full_bf16_weights):
     hot_tokens = np.nonzero((res["topk_idx"].cpu().numpy() == hot).any(1))[0]
     S = np.unique(np.concatenate([rng.choice(wl.T, 4, replace=False), hot_tokens[-2:]]))
     xh = to_host_act(x)
-    ref = oracle.layer(xh[S], lg[S], wl.k, expert_getter(w, wl.wfmt), E=wl.E)
+    ref = oracle.layer(xh[S], lg[S], wl.k, expert_getter(w, wl.wfmt), E=wl.E,
+                       act_quant=oracle.quantize_mxfp8 if fp8 else None)
     got = to_host_act(res["out"])[S]
     err = rel_l2(got, ref["out"])
     log(f"  sampled tokens {S.tolist()}: rel_l2={err:.3e}")
-    assert err <= (MXFP4_TOL if wl.wfmt in ("mxfp4", "nvfp4") else 5e-3)
+    assert err <= (MXFP4_TOL if wl.wfmt in ("mxfp4", "nvfp4") and not fp8 else 5e-3)
     if wl.wfmt != "bf16":
         del w
         torch.cuda.empty_cache()
