@@ -82,7 +82,6 @@ DOMINANT = {
     "prefill": ("gg_gate_up", ["expert_ffn_layer_softmax_amd/csrc/grouped_gemm.hip",
                                "expert_ffn_layer_softmax_amd/csrc/device.h"]),
 }
-RIDGE_FLOP_PER_BYTE = BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9)
 
 
 def _traffic(kernel: str, workload: str, digest: str):
