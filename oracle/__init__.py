@@ -7,6 +7,7 @@ baseline leg of ``bench.py`` use it.  It shares no code with the HIP library.
 
 from .moe_oracle import (  # noqa: F401
     E2M1_VALUES,
+    EXPERT_NORM_EPS,
     combine,
     decode_bf16,
     decode_e4m3,

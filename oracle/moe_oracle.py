@@ -274,21 +274,35 @@ def expert_ffn(x, offsets, sorted_src, k, get_expert, act_quant=None):
     return y
 
 
-def combine(y_sorted, dest_row, w):
-    """``out[t] = sum_j w[t, j] * y_sorted[dest_row[t*k + j]]`` (fp64, no rounding)."""
+# Per-expert output normalisation, the second reading of "per-expert outputs
+# are normalised, then combined" (TensorSharp Muse Spark report, "Performance"
+# section; the pages give no formula).  Reading taken: each selected expert's
+# output row is divided by its root mean square over d, with EXPERT_NORM_EPS
+# inside the root (the plain parameter-free RMS normalisation), before the
+# weighted sum.  It makes the combine nonlinear in the expert outputs.
+EXPERT_NORM_EPS = 1e-6
+
+
+def combine(y_sorted, dest_row, w, expert_norm: bool = False):
+    """``out[t] = sum_j w[t, j] * n(y_sorted[dest_row[t*k + j]])`` (fp64, no
+    rounding); n is the identity, or the RMS normalisation if ``expert_norm``."""
     w = np.asarray(w, dtype=np.float64)
     T, k = w.shape
     dest = np.asarray(dest_row).reshape(T, k)
     out = np.zeros((T, y_sorted.shape[1]), dtype=np.float64)
     for j in range(k):
-        out += w[:, j:j + 1] * y_sorted[dest[:, j]]
+        rows = y_sorted[dest[:, j]]
+        if expert_norm:
+            rows = rows / np.sqrt(np.mean(rows * rows, axis=1, keepdims=True) + EXPERT_NORM_EPS)
+        out += w[:, j:j + 1] * rows
     return out
 
 
-def layer(x, logits, k, get_expert, E=None, w_r=None, act_quant=None):
+def layer(x, logits, k, get_expert, E=None, w_r=None, act_quant=None, expert_norm=False):
     """Whole layer.  If ``w_r`` is given the logits are computed from it
     (``logits`` is then ignored); otherwise ``logits`` are used as given.
-    ``act_quant`` quantises the expert FFN's activation operands (FP8 mode).
+    ``act_quant`` quantises the expert FFN's activation operands (FP8 mode);
+    ``expert_norm`` RMS-normalises each expert output before the combine.
     Returns a dict with every intermediate."""
     x = np.asarray(x, dtype=np.float64)
     if w_r is not None:
@@ -298,7 +312,7 @@ def layer(x, logits, k, get_expert, E=None, w_r=None, act_quant=None):
     idx, w = route(logits, k)
     counts, offsets, sorted_src, dest_row = permute(idx, E)
     y = expert_ffn(x, offsets, sorted_src, k, get_expert, act_quant)
-    out = combine(y, dest_row, w)
+    out = combine(y, dest_row, w, expert_norm)
     return dict(logits=logits, idx=idx, w=w, counts=counts, offsets=offsets,
                 sorted_src=sorted_src, dest_row=dest_row, y_sorted=y, out=out)
 

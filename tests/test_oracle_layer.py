@@ -152,3 +152,25 @@ def test_expert_getter_only_called_for_routed_experts(rng):
         return wg[e], wu[e], wd[e]
     res = layer(x, rng.normal(size=(T, E)).astype(np.float32), k, get)
     assert sorted(seen) == sorted(set(res["idx"].ravel().tolist()))
+
+
+# ------------------------------------------------- per-expert normalisation
+def test_expert_norm_scale_invariance_and_unit_rms(rng):
+    """With per-expert RMS normalisation the output does not change when an
+    expert's output row is scaled by c > 0 (eps aside), and each normalised
+    row has unit RMS; without it the combine is linear in the rows."""
+    from oracle import EXPERT_NORM_EPS, combine
+    T, k, d = 3, 4, 64
+    y = rng.normal(size=(T * k, d)) * 10.0
+    dest = rng.permutation(T * k)
+    w = rng.dirichlet(np.ones(k), size=T)
+    base = combine(y, dest, w, expert_norm=True)
+    y2 = y.copy()
+    y2[dest[5]] *= 7.0
+    np.testing.assert_allclose(combine(y2, dest, w, expert_norm=True), base, rtol=0, atol=1e-7)
+    assert not np.allclose(combine(y2, dest, w), combine(y, dest, w))
+    # one slot with weight 1: the output is that row over its RMS
+    one = combine(y[:1], np.array([0]), np.ones((1, 1)), expert_norm=True)
+    rms = np.sqrt(np.mean(one ** 2))
+    assert abs(rms - 1.0) < EXPERT_NORM_EPS
+    np.testing.assert_allclose(one[0] * np.linalg.norm(y[0]) / np.sqrt(d), y[0], rtol=1e-8)
