@@ -47,6 +47,9 @@ def _parse():
                         "layer is x of the next); tokens/s counts each token once per step")
     p.add_argument("--fp8", action="store_true",
                    help="FP8 activations (MXFP8) on the scaled MFMA; MX-FP4 workloads only")
+    p.add_argument("--expert-norm", action="store_true",
+                   help="RMS-normalise each expert's output row before the combine "
+                        "(MOE_FLAG_EXPERT_NORM)")
     p.add_argument("--graph", action="store_true",
                    help="replay each step from a captured HIP graph (one graph per logit-set "
                         "offset, rotated) instead of launching it")
@@ -97,7 +100,8 @@ def _traffic(kernel: str, workload: str, digest: str):
     return rec.get("bytes_per_launch")
 
 
-def cpu_baseline(wl, x, w, logit_sets, budget_s: float, fp8: bool = False):
+def cpu_baseline(wl, x, w, logit_sets, budget_s: float, fp8: bool = False,
+                 expert_norm: bool = False):
     """The oracle, as it stands, on the host: one token per logit set until the
     budget is spent.  Expert weights are copied to host memory untimed; decoding
     them to fp64 is part of the oracle's timed work."""
@@ -142,7 +146,8 @@ def cpu_baseline(wl, x, w, logit_sets, budget_s: float, fp8: bool = False):
 
         t0 = time.perf_counter()
         xh = oracle.decode_bf16(xh_raw) if wl.act == "bf16" else xh_raw.astype(np.float64)
-        oracle.layer(xh, lg, wl.k, get, E=wl.E, act_quant=oracle.quantize_mxfp8 if fp8 else None)
+        oracle.layer(xh, lg, wl.k, get, E=wl.E, act_quant=oracle.quantize_mxfp8 if fp8 else None,
+                     expert_norm=expert_norm)
         spent += time.perf_counter() - t0
         done_tokens += T
         sets_used += 1
@@ -178,14 +183,14 @@ def measure(wl, ws_list, args, with_cpu: bool):
     topk_idx = torch.empty(wl.T, k, dtype=torch.int32, device=dev)
     topk_w = torch.empty(wl.T, k, dtype=torch.float32, device=dev)
     res = moe_layer_forward(x, ws_list[0], k, logits=sets[0], topk_idx=topk_idx, topk_w=topk_w,
-                            out=acts[1], fp8=args.fp8)
+                            out=acts[1], fp8=args.fp8, expert_norm=args.expert_norm)
     ws = res["workspace"]
 
     # Steps call the C entry point directly with pre-marshalled arguments, so
     # host-side Python work does not pace the GPU.
     wfmt = L._wfmt(ws_list[0])
     dims = L._dims(wl.T, wl.d, wl.E, k, wl.f, L._ACT[x.dtype], wfmt,
-                   L.MOE_FLAG_FP8_ACTIVATIONS if args.fp8 else 0)
+                   L._flags(args.fp8, args.expert_norm))
     wts = [L._weights(w, wl.E, wl.d, wl.f, wfmt, dev) for w in ws_list]
     lptr = [ctypes.c_void_p(sets[i].data_ptr()) for i in range(nsets)]
     aptr = [ctypes.c_void_p(t.data_ptr()) for t in acts]
@@ -295,6 +300,8 @@ def measure(wl, ws_list, args, with_cpu: bool):
         cfg["hip_graph"] = True
     if args.fp8:
         cfg["activations"] = "mxfp8"
+    if args.expert_norm:
+        cfg["expert_norm"] = "rms"
     rec = {
         "metric": METRIC, "value": round(tokens_per_s, 2), "unit": "tokens/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 5),
@@ -314,7 +321,8 @@ def measure(wl, ws_list, args, with_cpu: bool):
     }
     if with_cpu:
         print("[bench] CPU oracle baseline", file=sys.stderr, flush=True)
-        rec["cpu_baseline"] = cpu_baseline(wl, x, ws_list[0], sets, args.cpu_seconds, args.fp8)
+        rec["cpu_baseline"] = cpu_baseline(wl, x, ws_list[0], sets, args.cpu_seconds, args.fp8,
+                                           args.expert_norm)
     else:
         rec["cpu_baseline"] = None
     return rec

@@ -13,6 +13,7 @@ from ._lib import (  # noqa: F401
     MOE_DTYPE_F32,
     MOE_DTYPE_MXFP4,
     MOE_DTYPE_NVFP4,
+    MOE_FLAG_EXPERT_NORM,
     MOE_FLAG_FP8_ACTIVATIONS,
     MoeError,
     lib,

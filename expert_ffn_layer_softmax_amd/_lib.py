@@ -110,6 +110,7 @@ _ACT = {torch.float32: MOE_DTYPE_F32, torch.bfloat16: MOE_DTYPE_BF16}
 
 
 MOE_FLAG_FP8_ACTIVATIONS = 1
+MOE_FLAG_EXPERT_NORM = 2
 
 
 def _dims(T, d, E, k, f, act, wfmt, flags=0) -> MoeDims:
@@ -217,7 +218,7 @@ def moe_expert_ffn(x, offsets, sorted_src, k, weights: dict, y_sorted=None, work
     dev = x.device
     _need(offsets, "offsets", torch.int32, (E + 1,), dev)
     _need(sorted_src, "sorted_src", torch.int32, (T * k,), dev)
-    dims = _dims(T, d, E, k, f, _ACT[x.dtype], wfmt, MOE_FLAG_FP8_ACTIVATIONS if fp8 else 0)
+    dims = _dims(T, d, E, k, f, _ACT[x.dtype], wfmt, _flags(fp8))
     w = _weights(weights, E, d, f, wfmt, dev)
     if y_sorted is None:
         y_sorted = torch.empty(T * k, d, dtype=torch.float32, device=dev)
@@ -229,7 +230,11 @@ def moe_expert_ffn(x, offsets, sorted_src, k, weights: dict, y_sorted=None, work
     return y_sorted
 
 
-def moe_combine(y_sorted, dest_row, topk_w, out_dtype, out=None):
+def _flags(fp8=False, expert_norm=False):
+    return (MOE_FLAG_FP8_ACTIVATIONS if fp8 else 0) | (MOE_FLAG_EXPERT_NORM if expert_norm else 0)
+
+
+def moe_combine(y_sorted, dest_row, topk_w, out_dtype, out=None, expert_norm=False):
     _need(y_sorted, "y_sorted", torch.float32)
     T, k = topk_w.shape
     d = y_sorted.shape[1]
@@ -240,18 +245,20 @@ def moe_combine(y_sorted, dest_row, topk_w, out_dtype, out=None):
         out = torch.empty(T, d, dtype=out_dtype, device=dev)
     _need(out, "out", out_dtype, (T, d), dev)
     dims = _dims(T, d, max(k, 1), k, 32, _ACT[out_dtype],
-                 MOE_DTYPE_F32 if out_dtype == torch.float32 else MOE_DTYPE_BF16)
+                 MOE_DTYPE_F32 if out_dtype == torch.float32 else MOE_DTYPE_BF16,
+                 _flags(expert_norm=expert_norm))
     _check(lib.moe_combine(ctypes.byref(dims), _ptr(y_sorted), _ptr(dest_row), _ptr(topk_w),
                            _ptr(out), _stream(y_sorted)), "moe_combine")
     return out
 
 
 def moe_layer_forward(x, weights: dict, k, logits=None, w_router=None, topk_idx=None, topk_w=None,
-                      out=None, workspace=None, fp8=False):
+                      out=None, workspace=None, fp8=False, expert_norm=False):
     """Whole layer.  Give ``w_router`` to compute the logits in-path (they are
     written to ``logits``, allocated if None), or ``logits`` to route by them.
     ``fp8=True`` sets MOE_FLAG_FP8_ACTIVATIONS (MXFP8 activations on the scaled
-    MFMA; MX-FP4 weights)."""
+    MFMA; MX-FP4 weights); ``expert_norm=True`` sets MOE_FLAG_EXPERT_NORM
+    (each expert's output row RMS-normalised before the combine)."""
     _need(x, "x")
     if x.dtype not in _ACT:
         raise TypeError("x must be float32 or bfloat16")
@@ -272,7 +279,7 @@ def moe_layer_forward(x, weights: dict, k, logits=None, w_router=None, topk_idx=
     _need(topk_idx, "topk_idx", torch.int32, (T, k), dev)
     _need(topk_w, "topk_w", torch.float32, (T, k), dev)
     _need(out, "out", x.dtype, (T, d), dev)
-    dims = _dims(T, d, E, k, f, _ACT[x.dtype], wfmt, MOE_FLAG_FP8_ACTIVATIONS if fp8 else 0)
+    dims = _dims(T, d, E, k, f, _ACT[x.dtype], wfmt, _flags(fp8, expert_norm))
     w = _weights(weights, E, d, f, wfmt, dev)
     ws = _workspace(dims, dev, workspace)
     _check(lib.moe_layer_forward(ctypes.byref(dims), _ptr(x), _ptr(w_router), _ptr(logits),

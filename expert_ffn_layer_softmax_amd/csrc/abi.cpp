@@ -121,9 +121,10 @@ moe_status_t check_dims(const moe_dims_t* d, Dims* out) {
                        (d->act_dtype == MOE_DTYPE_BF16 && d->w_dtype == MOE_DTYPE_MXFP4) ||
                        (d->act_dtype == MOE_DTYPE_BF16 && d->w_dtype == MOE_DTYPE_NVFP4);
   if (!pair_ok) return MOE_ERR_UNSUPPORTED;
-  if (d->flags & ~MOE_FLAG_FP8_ACTIVATIONS) return MOE_ERR_INVALID_ARGUMENT;
+  if (d->flags & ~(MOE_FLAG_FP8_ACTIVATIONS | MOE_FLAG_EXPERT_NORM)) return MOE_ERR_INVALID_ARGUMENT;
   Dims dm{d->T, d->d, d->E, d->k, d->f, d->act_dtype, d->w_dtype};
   dm.fp8 = (d->flags & MOE_FLAG_FP8_ACTIVATIONS) != 0;
+  dm.expert_norm = (d->flags & MOE_FLAG_EXPERT_NORM) != 0;
   if (dm.fp8 && !fp8_path_ok(dm)) return MOE_ERR_UNSUPPORTED;
   *out = dm;
   return MOE_OK;
@@ -280,7 +281,7 @@ moe_status_t moe_layer_forward(const moe_dims_t* dims, const void* x, const void
 
   hipError_t e = hipSuccess;
   if (w_router) e = launch_router_logits(x, w_router, logits, dm.T, dm.d, dm.E, dm.act, s);
-  if (!dm.fp8 && gemv_down_combine_t1_ok(dm)) {
+  if (!dm.fp8 && !dm.expert_norm && gemv_down_combine_t1_ok(dm)) {
     // single token: one-wave route+plan, gate/up GEMV, down GEMV + combine
     if (e == hipSuccess) e = launch_route_plan_t1(logits, dm.E, dm.k, topk_idx, topk_w, p, s);
     if (e == hipSuccess) e = launch_gemv_gate_up(dm, x, p, w, h, s);

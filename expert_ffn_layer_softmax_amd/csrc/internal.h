@@ -35,7 +35,8 @@ constexpr int kGemmMinT = 48;
 
 struct Dims {
   int T, d, E, k, f, act, wfmt;
-  bool fp8 = false;  // MXFP8 activations on the scaled MFMA
+  bool fp8 = false;          // MXFP8 activations on the scaled MFMA
+  bool expert_norm = false;  // RMS-normalise each expert output before the combine
   long long Tk() const { return (long long)T * k; }
 };
 

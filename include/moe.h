@@ -93,7 +93,17 @@ typedef enum {
  *    grouped MFMA path is then used for decode too).  Results are defined
  *    with the quantised activations; they differ from the bf16 path by the
  *    FP8 rounding (about 2-4 % relative). */
-enum { MOE_FLAG_FP8_ACTIVATIONS = 1 };
+/*  MOE_FLAG_EXPERT_NORM: divide each selected expert's output row by its
+ *    root mean square over d, sqrt(mean(y^2) + 1e-6), before the weighted
+ *    sum.  The report that describes the combine (TensorSharp Muse Spark
+ *    report, "Performance" section) says the per-expert outputs are
+ *    normalised before they are combined but gives no formula; the default
+ *    reads that as the routing-weight normalisation, this flag as an RMS
+ *    normalisation of each expert's output row.  It makes the combine
+ *    nonlinear in the expert outputs.  Honoured by moe_combine and
+ *    moe_layer_forward (which then skips the fused single-token down+combine
+ *    kernel); other entry points ignore it. */
+enum { MOE_FLAG_FP8_ACTIVATIONS = 1, MOE_FLAG_EXPERT_NORM = 2 };
 
 /* Layer shape.  T tokens of hidden size d, E experts of FFN width f, each
  * token routed to k experts.  act_dtype / w_dtype hold moe_dtype_t values;
@@ -170,15 +180,17 @@ moe_status_t moe_expert_ffn(const moe_dims_t* dims, const void* x, const int32_t
  * experts' normalised outputs are combined):
  *   out[t] = sum_{j<k} topk_w[t][j] * y_sorted[dest_row[t*k + j]]
  * summed in fp32 in slot order and rounded once to the act dtype (bf16:
- * round to nearest even). */
+ * round to nearest even).  With MOE_FLAG_EXPERT_NORM each row is first
+ * divided by r = sqrt(sum_i y_i^2 / d + 1e-6), the sum of squares taken in
+ * fp32. */
 moe_status_t moe_combine(const moe_dims_t* dims, const float* y_sorted, const int32_t* dest_row,
                          const float* topk_w, void* out, moe_stream_t stream);
 
 /* The whole layer: [router logits] -> route -> permute -> expert FFN ->
  * combine.  If w_router is non-NULL, logits[T][E] = x . w_router^T (fp32
  * accumulation) is written to `logits`; otherwise `logits` is read as input.
- * topk_idx / topk_w receive the routing.  For T == 1 (k <= 16) the down
- * projection is fused with the combine; the per-token sum keeps slot order
+ * topk_idx / topk_w receive the routing.  For T == 1 (k <= 16, no
+ * MOE_FLAG_* set) the down projection is fused with the combine; the per-token sum keeps slot order
  * and the combine's arithmetic, so the result equals the stage-wise path bit
  * for bit.
  * workspace must hold moe_workspace_size(dims) bytes. */

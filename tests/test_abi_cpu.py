@@ -68,7 +68,11 @@ def test_workspace_size_validation(m):
     assert _ws(m, _dims(m, act=1, w=4))[0] == INVALID
     # FP8 activations: MX-FP4 weights, bf16 activations, d and f multiples of 256
     assert _ws(m, _dims(m, d=256, f=512, w=2, flags=1))[0] == OK
-    assert _ws(m, _dims(m, d=256, f=512, w=2, flags=2))[0] == INVALID
+    assert _ws(m, _dims(m, d=256, f=512, w=2, flags=4))[0] == INVALID   # unknown bit
+    # RMS-normalised combine: any supported pair, alone or with FP8 activations
+    assert _ws(m, _dims(m, flags=2))[0] == OK
+    assert _ws(m, _dims(m, d=256, f=512, w=2, flags=3))[0] == OK
+    assert _ws(m, _dims(m, flags=2))[1] == _ws(m, _dims(m))[1]
     assert _ws(m, _dims(m, d=256, f=512, w=1, flags=1))[0] == UNSUPPORTED   # bf16 weights
     assert _ws(m, _dims(m, d=256, f=512, w=3, flags=1))[0] == UNSUPPORTED   # NVFP4 weights
     assert _ws(m, _dims(m, d=320, f=512, w=2, flags=1))[0] == UNSUPPORTED   # d % 256

@@ -238,6 +238,87 @@ def test_layer_fp8_activations(case):
     assert sep > 5e-3
 
 
+# ------------------------------------------- RMS-normalised expert outputs
+# MOE_FLAG_EXPERT_NORM on every path: the fused single-token kernel is
+# bypassed, the GEMV and grouped-GEMM paths feed the normalising combine.
+NORM_CASES = [
+    # name, T, d, E, k, f, act, wfmt, fp8
+    ("norm_t1_bf16", 1, 512, 32, 8, 160, "bf16", "bf16", False),
+    ("norm_t1_f32", 1, 128, 8, 3, 64, "f32", "f32", False),
+    ("norm_t16_mx", 16, 512, 32, 8, 256, "bf16", "mxfp4", False),
+    ("norm_t40_nv", 40, 256, 8, 2, 128, "bf16", "nvfp4", False),
+    ("norm_gg_bf16", 300, 512, 16, 4, 384, "bf16", "bf16", False),
+    ("norm_gg_mx_k20", 90, 640, 32, 20, 256, "bf16", "mxfp4", False),   # 5 slots per wave
+    ("norm_fp8", 100, 256, 8, 4, 512, "bf16", "mxfp4", True),
+]
+
+
+@pytest.mark.parametrize("case", NORM_CASES, ids=[c[0] for c in NORM_CASES])
+def test_layer_expert_norm(case):
+    from expert_ffn_layer_softmax_amd import moe_layer_forward
+    name, T, d, E, k, f, act, wfmt, fp8 = case
+    log(f"expert-norm layer {name}")
+    wl = Workload(name, T=T, d=d, E=E, k=k, f=f, act=act, wfmt=wfmt,
+                  seed=zlib.crc32(name.encode()) % 100000,
+                  x_std=1.0, wg_std=d ** -0.5, wu_std=d ** -0.5, wd_std=f ** -0.5)
+    x, w, _, logits = make_inputs(wl)
+    res = moe_layer_forward(x, w, k, logits=logits, fp8=fp8, expert_norm=True)
+    torch.cuda.synchronize()
+    lg = logits.cpu().numpy()
+    check_routing(res, lg, k, E)
+    aq = oracle.quantize_mxfp8 if fp8 else None
+    get = expert_getter(w, wfmt)
+    ref = oracle.layer(to_host_act(x), lg, k, get, E=E, act_quant=aq, expert_norm=True)
+    plain = oracle.layer(to_host_act(x), lg, k, get, E=E, act_quant=aq)
+    err = rel_l2(to_host_act(res["out"]), ref["out"])
+    sep = rel_l2(plain["out"], ref["out"])
+    log(f"  rel_l2={err:.3e} (unnormalised reference differs by {sep:.3e})")
+    assert err <= (1e-5 if act == "f32" else 5e-3 if wfmt == "bf16" or fp8 else _tol(wl))
+    assert sep > 0.1
+
+
+@pytest.mark.parametrize("act,d,k,T", [("f32", 64, 1, 37), ("f32", 320, 6, 37), ("bf16", 6144, 8, 37),
+                                       ("bf16", 1024, 64, 37), ("f32", 704, 5, 300),
+                                       ("bf16", 6144, 8, 260), ("bf16", 1024, 12, 300),
+                                       ("f32", 8448, 4, 20), ("f32", 8448, 4, 256),
+                                       ("bf16", 64, 1, 400)])
+def test_combine_expert_norm_entry_point(act, d, k, T):
+    """moe_combine with the flag on the device's own y_sorted, against the
+    oracle's fp64 combine within the fp32 error bound of the norm and sum.
+    Cases cover the register-resident kernel (T >= 256, k <= 8, d <= 8192;
+    256 and 1024 threads) and the two-pass kernel (T < 256, or k > 8, or
+    d > 8192; 1024 and 256 threads)."""
+    from expert_ffn_layer_softmax_amd import moe_combine, moe_permute, moe_route
+    E = max(k, 8)
+    g = torch.Generator().manual_seed(d + k + T)
+    logits = torch.randn(T, E, generator=g).cuda()
+    idx, tw = moe_route(logits, k)
+    _, _, _, dest_row = moe_permute(idx, E)
+    # rows of very different scales (the norm removes them) and one zero row
+    scale = torch.exp2(torch.randint(-20, 20, (T * k, 1), generator=g).float())
+    y = torch.randn(T * k, d, generator=g) * scale
+    y[3] = 0.0
+    y = y.cuda()
+    dt = torch.float32 if act == "f32" else torch.bfloat16
+    out = moe_combine(y, dest_row, tw, dt, expert_norm=True)
+    torch.cuda.synchronize()
+    yh = y.cpu().numpy().astype(np.float64)
+    rd = dest_row.cpu().numpy()
+    twh = tw.cpu().numpy().astype(np.float64)
+    rout = oracle.combine(yh, rd, twh, expert_norm=True)
+    got = to_host_act(out)
+    # per-row weight w/r: sum of squares of at most d/64 sequential terms per
+    # lane, a 6-level wave tree and at most 16 wave partials (all terms >= 0),
+    # a root and a division; then the fp32 sum of k products, and for bf16 one
+    # rounding
+    mag = oracle.combine(np.abs(yh), rd, np.abs(twh), expert_norm=True)
+    u = 2.0 ** -24
+    bound = ((k + 1) + (d / 64 + 6 + 16) / 2 + 3) * u * mag + 1e-30
+    if act == "bf16":
+        bound = bound + 2.0 ** -8 * np.abs(rout)
+    assert np.all(np.abs(got - rout) <= bound), float(np.max(np.abs(got - rout) / bound))
+
+
 # ------------------------------------------------------------ HIP graphs
 @pytest.mark.parametrize("T,wfmt", [(1, "bf16"), (16, "bf16"), (100, "bf16"), (100, "mxfp4"),
                                     (100, "nvfp4"), (100, "mxfp4_fp8")])

@@ -174,3 +174,16 @@ def test_expert_norm_scale_invariance_and_unit_rms(rng):
     rms = np.sqrt(np.mean(one ** 2))
     assert abs(rms - 1.0) < EXPERT_NORM_EPS
     np.testing.assert_allclose(one[0] * np.linalg.norm(y[0]) / np.sqrt(d), y[0], rtol=1e-8)
+
+
+def test_expert_norm_eps_inside_the_root_and_zero_rows():
+    """A constant row of value c with c^2 equal to eps maps to 1/sqrt(2)
+    (eps inside the square root: c / sqrt(c^2 + eps)); a zero row stays zero."""
+    from oracle import EXPERT_NORM_EPS, combine
+    d = 96
+    c = np.sqrt(EXPERT_NORM_EPS)
+    y = np.stack([np.full(d, c), np.zeros(d), np.full(d, -3.0)])
+    out = combine(y, np.array([0, 1, 2]), np.array([[1.0], [1.0], [0.5]]), expert_norm=True)
+    np.testing.assert_allclose(out[0], np.full(d, 2 ** -0.5), rtol=1e-12)
+    assert np.all(out[1] == 0.0)
+    np.testing.assert_allclose(out[2], np.full(d, -0.5 * 3.0 / np.sqrt(9.0 + EXPERT_NORM_EPS)), rtol=1e-12)
