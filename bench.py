@@ -50,6 +50,10 @@ def _parse():
     p.add_argument("--expert-norm", action="store_true",
                    help="RMS-normalise each expert's output row before the combine "
                         "(MOE_FLAG_EXPERT_NORM)")
+    p.add_argument("--share", choices=["ep8", "tp8"], default=None,
+                   help="time one GPU's share of the layer split over 8 GPUs: ep8 = 1/8 of the "
+                        "experts with the T*k/8 rows dispatched to them (k=1 locally), tp8 = every "
+                        "expert with f/8 (rounded up to a multiple of 64); tokens/s counts the whole layer's tokens")
     p.add_argument("--graph", action="store_true",
                    help="replay each step from a captured HIP graph (one graph per logit-set "
                         "offset, rotated) instead of launching it")
@@ -250,7 +254,7 @@ def measure(wl, ws_list, args, with_cpu: bool):
     torch.cuda.synchronize()
     el = time.perf_counter() - t0
     ms = el * 1e3 / args.steps
-    tokens_per_s = wl.T * args.steps / el
+    tokens_per_s = getattr(args, "job_tokens", wl.T) * args.steps / el
 
     # per-kernel HIP-event durations on the launch stream (separate pass of
     # launched steps; graph replays carry no events)
@@ -341,6 +345,21 @@ def main():
 
     base = WORKLOADS[args.workload]
     assert not base.router, "bench workloads route by pre-drawn logits"
+    if args.share:
+        # One GPU's share at G = 8.  Expert parallelism: E/8 local experts
+        # receive T*k/8 (token, expert) rows, each for one local expert.
+        # Tensor parallelism over f: every expert, f/8 of its width.
+        args.job_tokens = base.T
+        if args.share == "ep8":
+            base = dataclasses.replace(base, E=base.E // 8, k=1, T=max(1, base.T * base.k // 8),
+                                       name=f"{base.name}_ep8_share")
+        else:
+            # f/8 rounded up to the grouped GEMMs' 64-wide K step: the extra
+            # rows are zero weights in a real shard (exact), here random
+            fs = -(-base.f // 8 // 64) * 64
+            base = dataclasses.replace(base, f=fs, name=f"{base.name}_tp8_share")
+        if args.T is not None or args.sweep:
+            raise SystemExit("--share takes the workload's own T")
     if args.layers < 1:
         raise SystemExit("--layers must be >= 1")
     dev = torch.device("cuda:0")
@@ -356,7 +375,10 @@ def main():
     wl = base
     if args.T is not None:
         wl = dataclasses.replace(base, T=args.T, name=f"{base.name}_T{args.T}")
-    rec = measure(wl, ws_list, args, with_cpu=not args.no_cpu and args.layers == 1)
+    rec = measure(wl, ws_list, args, with_cpu=not args.no_cpu and args.layers == 1 and not args.share)
+    if args.share:
+        rec["config"]["share"] = args.share
+        rec["config"]["job_tokens"] = args.job_tokens
     print(json.dumps(rec), flush=True)
 
 
