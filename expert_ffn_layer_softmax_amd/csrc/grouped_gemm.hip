@@ -329,10 +329,12 @@ __device__ __forceinline__ void wait_and_barrier() {
 }
 
 // MFMAs of one K-step on LDS stage `st` for the VM valid row sub-tiles
-// (of two) of this wave; fragments are read one substep ahead.
-template <int VM>
+// (of two) of this wave; fragments are read one substep ahead.  A lane of
+// half h feeds K units 4h + s of the step (s = substep); in a TAIL step only
+// the first 32 K exist, so the half-1 lanes feed zeros.
+template <int VM, bool TAIL = false>
 __device__ __forceinline__ void dma_step(const char* st, const int* aoff, const int* boff,
-                                         f32x16_t (&acc)[2][2]) {
+                                         f32x16_t (&acc)[2][2], int half = 0) {
   if constexpr (VM > 0) {
     const char* abuf = st;
     const char* bbuf = st + kStageA;
@@ -343,6 +345,14 @@ __device__ __forceinline__ void dma_step(const char* st, const int* aoff, const 
         a2[mi] = *reinterpret_cast<const bf16x8_t*>(abuf + aoff[4 * mi + s]);
 #pragma unroll
       for (int m = 0; m < 2; ++m) b2[m] = *reinterpret_cast<const bf16x8_t*>(bbuf + boff[4 * m + s]);
+      if constexpr (TAIL) {
+        if (half) {
+#pragma unroll
+          for (int mi = 0; mi < VM; ++mi) a2[mi] = bf16x8_t{};
+#pragma unroll
+          for (int m = 0; m < 2; ++m) b2[m] = bf16x8_t{};
+        }
+      }
     };
     rd(0, af[0], bf[0]);
 #pragma unroll
@@ -391,7 +401,14 @@ __global__ __launch_bounds__(kThreads) void gg_dma_kernel(GGArgs a) {
   // share; lane -> (row, slot), global unit slot ^ f(row).
   const size_t rb = (size_t)a.K * 2;
   const int slot16 = lane & 7;
+  // K % 64 == 32: after the nk full steps a tail step holds 32 K; a lane
+  // whose 16-byte unit lies in the missing half re-reads unit - 4 of its row
+  // (in bounds; fed to the MFMAs as zeros).  The tail is loaded after the
+  // main loop, which stays that of the K % 64 == 0 case.
+  const int nk = a.K / BK;
+  const bool ktail = (a.K % BK) != 0;
   const char* asrc[kDmaA];
+  int ahi = 0, bhi = 0;  // bit j: the lane's unit of DMA j is in the upper half of the step
 #pragma unroll
   for (int j = 0; j < kDmaA; ++j) {
     const int r = (kDmaA * 8) * wave + 8 * j + (lane >> 3);
@@ -399,6 +416,7 @@ __global__ __launch_bounds__(kThreads) void gg_dma_kernel(GGArgs a) {
     const int src = row0 + min(r, nrows - 1);
     asrc[j] = reinterpret_cast<const char*>(a.a_src) +
               (GATEUP ? (size_t)(a.sorted_src[src] / a.k) : (size_t)src) * rb + ((slot16 ^ f) << 4);
+    ahi |= ((slot16 ^ f) >= 4 ? 1 : 0) << j;
   }
   const char* bsrc[kDmaB];
 #pragma unroll
@@ -416,6 +434,7 @@ __global__ __launch_bounds__(kThreads) void gg_dma_kernel(GGArgs a) {
     }
     col = min(col, a.N - 1);
     bsrc[j] = reinterpret_cast<const char*>(w) + ((size_t)e * a.N + col) * rb + ((slot16 ^ f) << 4);
+    bhi |= ((slot16 ^ f) >= 4 ? 1 : 0) << j;
   }
   char* const adst = lds + (kDmaA * 8) * wave * (BK * 2);
   char* const bdst = lds + kStageA + (kDmaB * 8) * wave * (BK * 2);
@@ -426,6 +445,16 @@ __global__ __launch_bounds__(kThreads) void gg_dma_kernel(GGArgs a) {
     for (int j = 0; j < kDmaA; ++j) dma16<kAuxA>(asrc[j] + go, adst + so + j * 8 * (BK * 2));
 #pragma unroll
     for (int j = 0; j < kDmaB; ++j) dma16<kAuxB>(bsrc[j] + go, bdst + so + j * 8 * (BK * 2));
+  };
+  auto issue_tail = [&](int stage) {
+    const size_t go = (size_t)nk * (BK * 2);
+    const int so = stage * kStageBytes;
+#pragma unroll
+    for (int j = 0; j < kDmaA; ++j)
+      dma16<kAuxA>(asrc[j] + go - ((ahi >> j) & 1) * BK, adst + so + j * 8 * (BK * 2));
+#pragma unroll
+    for (int j = 0; j < kDmaB; ++j)
+      dma16<kAuxB>(bsrc[j] + go - ((bhi >> j) & 1) * BK, bdst + so + j * 8 * (BK * 2));
   };
 
   // ---- fragment offsets inside a stage: [sub-tile or matrix][substep]
@@ -449,9 +478,8 @@ __global__ __launch_bounds__(kThreads) void gg_dma_kernel(GGArgs a) {
 
   // valid 32-row sub-tiles of this wave's 64 rows (block-uniform per wave)
   const int vm = min(max((nrows + 31) / 32 - 2 * wm, 0), 2);
-  const int nk = a.K / BK;
 
-  issue(0, 0);
+  if (nk > 0) issue(0, 0);
   if (nk > 1) issue(1, 1);
   // The loop is instantiated per sub-tile count so the accumulators keep
   // fixed registers.
@@ -466,6 +494,13 @@ __global__ __launch_bounds__(kThreads) void gg_dma_kernel(GGArgs a) {
       if (kk + 2 < nk) issue(kk + 2, stage == 0 ? 2 : stage - 1);
       dma_step<VM>(lds + stage * kStageBytes, aoff, boff, acc);
       stage = stage == kStages - 1 ? 0 : stage + 1;
+    }
+    if (ktail) {
+      // stage `stage` was last read at step nk - 3, before every wave passed
+      // the barrier of step nk - 2
+      issue_tail(stage);
+      wait_and_barrier<0>();
+      dma_step<VM, true>(lds + stage * kStageBytes, aoff, boff, acc, half);
     }
   };
   if (vm == 2)
@@ -1197,7 +1232,8 @@ hipError_t launch_gg(const Dims& dm, const GGArgs& a, hipStream_t s) {
 bool grouped_gemm_ok(const Dims& dm) {
   if (dm.act != kBF16 || dm.T < kGemmMinT) return false;
   if (dm.wfmt == kNVFP4) return mx_grouped(dm.d) && mx_grouped(dm.f);
-  return (dm.wfmt == kBF16 || dm.wfmt == kMXFP4) && dm.d % BK == 0 && dm.f % BK == 0;
+  if (dm.wfmt == kBF16) return true;  // d, f multiples of 32: a K tail of 32 is handled
+  return dm.wfmt == kMXFP4 && dm.d % BK == 0 && dm.f % BK == 0;
 }
 
 size_t grouped_gemm_max_mtiles(const Dims& dm) {

@@ -109,6 +109,8 @@ SMALL = [
     ("gg_bf16_hot", 600, 384, 4, 2, 256, "bf16", "bf16"),      # ~300 rows/expert: 3 m-tiles
     ("gg_bf16_ntail", 64, 640, 6, 3, 128, "bf16", "bf16"),     # down N=640: partial n-tile
     ("gg_bf16_oddk", 70, 320, 6, 2, 192, "bf16", "bf16"),      # odd K-step counts
+    ("gg_bf16_ktail", 120, 352, 8, 2, 352, "bf16", "bf16"),    # K % 64 == 32 on both GEMMs
+    ("gg_bf16_ktail_t48", 48, 160, 4, 2, 96, "bf16", "bf16"),  # 2.5 and 1.5 K-steps
     ("gg_mx_t100", 100, 256, 8, 4, 256, "bf16", "mxfp4"),
     ("gg_mx_hot", 700, 512, 5, 2, 384, "bf16", "mxfp4"),
     ("gg_mx_ntail", 90, 640, 6, 2, 256, "bf16", "mxfp4"),      # down N=640: partial n-tile
@@ -460,6 +462,33 @@ def test_prefill_full_sampled(name, full_bf16_weights):
     if wl.wfmt != "bf16":
         del w
         torch.cuda.empty_cache()
+
+
+def test_prefill_tp8_shard_width_sampled():
+    """One GPU's tensor-parallel share at G = 8: f = 2816/8 = 352, a K tail of
+    32 in the down projection and a 96-column n-tile in gate/up, at T=4096."""
+    base = WORKLOADS["prefill_bf16"]
+    wl = Workload("prefill_bf16_f352", T=base.T, d=base.d, E=base.E, k=base.k, f=352, act="bf16",
+                  wfmt="bf16", seed=base.seed + 11, logit_sets=1, bias_std=base.bias_std,
+                  x_std=1.0, wg_std=base.d ** -0.5, wu_std=base.d ** -0.5, wd_std=352 ** -0.5)
+    log("prefill bf16 f=352 (T=4096), sampled tokens")
+    x, w, _, logits = make_inputs(wl)
+    from expert_ffn_layer_softmax_amd import moe_layer_forward, moe_timing_query, moe_timing_start, \
+        moe_timing_stop
+    moe_timing_start()
+    res = moe_layer_forward(x, w, wl.k, logits=logits)
+    torch.cuda.synchronize()
+    moe_timing_stop()
+    assert moe_timing_query("gg_down")[0] == 1, "the grouped GEMM path must take f = 352"
+    lg = res["logits"].cpu().numpy()
+    check_routing(res, lg, wl.k, wl.E)
+    S = np.random.default_rng(3).choice(wl.T, 6, replace=False)
+    ref = oracle.layer(to_host_act(x)[S], lg[S], wl.k, expert_getter(w, "bf16"), E=wl.E)
+    err = rel_l2(to_host_act(res["out"])[S], ref["out"])
+    log(f"  sampled tokens {sorted(S.tolist())}: rel_l2={err:.3e}")
+    assert err <= 5e-3
+    del w
+    torch.cuda.empty_cache()
 
 
 @pytest.mark.parametrize("name", ["decode_mxfp4", "decode_nvfp4"])
