@@ -53,7 +53,7 @@ def _parse():
     p.add_argument("--share", choices=["ep8", "tp8"], default=None,
                    help="time one GPU's share of the layer split over 8 GPUs: ep8 = 1/8 of the "
                         "experts with the T*k/8 rows dispatched to them (k=1 locally), tp8 = every "
-                        "expert with f/8 (rounded up to a multiple of 64); tokens/s counts the whole layer's tokens")
+                        "expert with f/8; tokens/s counts the whole layer's tokens")
     p.add_argument("--graph", action="store_true",
                    help="replay each step from a captured HIP graph (one graph per logit-set "
                         "offset, rotated) instead of launching it")
@@ -354,10 +354,7 @@ def main():
             base = dataclasses.replace(base, E=base.E // 8, k=1, T=max(1, base.T * base.k // 8),
                                        name=f"{base.name}_ep8_share")
         else:
-            # f/8 rounded up to the grouped GEMMs' 64-wide K step: the extra
-            # rows are zero weights in a real shard (exact), here random
-            fs = -(-base.f // 8 // 64) * 64
-            base = dataclasses.replace(base, f=fs, name=f"{base.name}_tp8_share")
+            base = dataclasses.replace(base, f=base.f // 8, name=f"{base.name}_tp8_share")
         if args.T is not None or args.sweep:
             raise SystemExit("--share takes the workload's own T")
     if args.layers < 1:

@@ -31,7 +31,8 @@
 // gg_direct_b_kernel (MX-FP4 weights, other K): each wave owns all 128 rows
 // and two 32-column weight operands that stream from memory into a register
 // ring; the activation rows go through a register ring into double-buffered
-// LDS.
+// LDS.  K % 64 == 32 adds one tail step after the loop (both GEMM kernels
+// for bf16 and MX-FP4 take it).
 //
 // Tile order: logical tiles run expert by expert, n-tile by n-tile, m-tile
 // by m-tile, and each XCD (blockIdx % 8 under round-robin dispatch) takes a
@@ -194,12 +195,34 @@ __global__ __launch_bounds__(kThreads) void gg_direct_b_kernel(GGArgs a) {
             (GATEUP ? (size_t)(a.sorted_src[src] / a.k) : (size_t)src) * a_rb + unit * 16;
   }
 
+  // K % 64 == 32: step nk is a tail of 32 K.  Its A units 4..7 and the
+  // half-1 lanes' weight block lie past the row: they re-read the step's
+  // first half (in bounds), and the half-1 lanes feed zeros to its MFMAs.
   const int nk = a.K / BK;
+  const int ns = (a.K + BK - 1) / BK;  // steps, the tail included
+  const int aback = unit >= 4 ? 64 : 0;
   u32x4 aring[D][kAPieces];
   BRegs<WF> bring[D];
   auto load_a = [&](u32x4* r, int kk) {
+    const size_t off = (size_t)kk * (BK * 2) - (kk == nk ? aback : 0);
 #pragma unroll
-    for (int i = 0; i < kAPieces; ++i) r[i] = ld16(ap[i] + (size_t)kk * (BK * 2));
+    for (int i = 0; i < kAPieces; ++i) r[i] = ld16(ap[i] + off);
+  };
+  auto load_b_step = [&](BRegs<WF>& b, int kk) {
+    if (kk < nk) {
+      load_b<WF>(b, p0, p1, q0, q1, kk);
+    } else if constexpr (WF == kBF16) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        b.v[0][q] = ld16(p0 + (size_t)nk * (BK * 2) - half * 64 + 16 * q);
+        b.v[1][q] = ld16(p1 + (size_t)nk * (BK * 2) - half * 64 + 16 * q);
+      }
+    } else {
+      b.v[0] = ld16(p0 + (size_t)nk * (BK / 2) - half * 16);
+      b.v[1] = ld16(p1 + (size_t)nk * (BK / 2) - half * 16);
+      b.s[0] = q0[2 * nk - half];
+      b.s[1] = q1[2 * nk - half];
+    }
   };
   auto store_a = [&](const u32x4* r, int buf) {
 #pragma unroll
@@ -213,43 +236,51 @@ __global__ __launch_bounds__(kThreads) void gg_direct_b_kernel(GGArgs a) {
 #pragma unroll
     for (int mi = 0; mi < 4; ++mi) acc[m][mi] = f32x16_t{};
 
+  auto mfma_step = [&](const char* abuf, const BRegs<WF>& b, bool zero_lane) {
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      bf16x8_t af[4];
+#pragma unroll
+      for (int mi = 0; mi < 4; ++mi)
+        af[mi] = *reinterpret_cast<const bf16x8_t*>(abuf + t_off(32 * mi + cl, half * 4 + s));
+      bf16x8_t b0 = b_frag<WF>(b, 0, s);
+      bf16x8_t b1 = b_frag<WF>(b, 1, s);
+      if (zero_lane) {
+        b0 = bf16x8_t{};
+        b1 = bf16x8_t{};
+#pragma unroll
+        for (int mi = 0; mi < 4; ++mi) af[mi] = bf16x8_t{};
+      }
+#pragma unroll
+      for (int mi = 0; mi < 4; ++mi) {
+        acc[0][mi] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[mi], b0, acc[0][mi], 0, 0, 0);
+        acc[1][mi] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[mi], b1, acc[1][mi], 0, 0, 0);
+      }
+    }
+  };
+
   // ---- prologue: steps 0..D-1 in flight, step 0 into LDS
+  const int klast = ns - 1;
 #pragma unroll
   for (int j = 0; j < D; ++j) {
-    load_a(aring[j], min(j, nk - 1));
-    load_b<WF>(bring[j], p0, p1, q0, q1, min(j, nk - 1));
+    load_a(aring[j], min(j, klast));
+    load_b_step(bring[j], min(j, klast));
   }
   store_a(aring[0], 0);
-  load_a(aring[0], min(D, nk - 1));
+  load_a(aring[0], min(D, klast));
   __syncthreads();
 
   // ---- main loop, unrolled by D so ring slots are static.  A last partial
-  // group (nk % D != 0) only skips the MFMAs.
-  for (int kk0 = 0; kk0 < nk; kk0 += D) {
+  // group (ns % D != 0) only skips the MFMAs.
+  for (int kk0 = 0; kk0 < ns; kk0 += D) {
 #pragma unroll
     for (int j = 0; j < D; ++j) {
       const int kk = kk0 + j;
-      if (kk < nk) {
-        const char* abuf = lds_a[kk & 1];
-#pragma unroll
-        for (int s = 0; s < 4; ++s) {
-          bf16x8_t af[4];
-#pragma unroll
-          for (int mi = 0; mi < 4; ++mi)
-            af[mi] = *reinterpret_cast<const bf16x8_t*>(abuf + t_off(32 * mi + cl, half * 4 + s));
-          const bf16x8_t b0 = b_frag<WF>(bring[j], 0, s);
-          const bf16x8_t b1 = b_frag<WF>(bring[j], 1, s);
-#pragma unroll
-          for (int mi = 0; mi < 4; ++mi) {
-            acc[0][mi] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[mi], b0, acc[0][mi], 0, 0, 0);
-            acc[1][mi] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[mi], b1, acc[1][mi], 0, 0, 0);
-          }
-        }
-      }
-      load_b<WF>(bring[j], p0, p1, q0, q1, min(kk + D, nk - 1));
+      if (kk < ns) mfma_step(lds_a[kk & 1], bring[j], kk == nk && half);
+      load_b_step(bring[j], min(kk + D, klast));
       const int jn = (j + 1) % D;
       store_a(aring[jn], (kk + 1) & 1);
-      load_a(aring[jn], min(kk + 1 + D, nk - 1));
+      load_a(aring[jn], min(kk + 1 + D, klast));
       __syncthreads();
     }
   }
@@ -1232,8 +1263,8 @@ hipError_t launch_gg(const Dims& dm, const GGArgs& a, hipStream_t s) {
 bool grouped_gemm_ok(const Dims& dm) {
   if (dm.act != kBF16 || dm.T < kGemmMinT) return false;
   if (dm.wfmt == kNVFP4) return mx_grouped(dm.d) && mx_grouped(dm.f);
-  if (dm.wfmt == kBF16) return true;  // d, f multiples of 32: a K tail of 32 is handled
-  return dm.wfmt == kMXFP4 && dm.d % BK == 0 && dm.f % BK == 0;
+  // bf16 and MX-FP4 take d, f >= 64 (multiples of 32: a K tail of 32 is handled)
+  return (dm.wfmt == kBF16 || dm.wfmt == kMXFP4) && dm.d >= BK && dm.f >= BK;
 }
 
 size_t grouped_gemm_max_mtiles(const Dims& dm) {
