@@ -323,6 +323,44 @@ def test_combine_expert_norm_entry_point(act, d, k, T):
     assert np.all(np.abs(got - rout) <= bound), float(np.max(np.abs(got - rout) / bound))
 
 
+# ------------------------------------------------- load and shape extremes
+EXTREMES = [
+    # name, T, d, E, k, f, wfmt, logits: "hot" (every token picks the same k
+    # experts), "rand"
+    ("all_to_k_experts_bf16", 4096, 256, 64, 8, 128, "bf16", "hot"),    # 32 m-tiles per expert
+    ("all_to_k_experts_mx", 4096, 256, 64, 8, 128, "mxfp4", "hot"),
+    ("one_expert_bf16", 300, 256, 1, 1, 128, "bf16", "rand"),           # E = k = 1
+    ("one_expert_mx", 300, 256, 1, 1, 256, "mxfp4", "rand"),
+    ("k_is_E_64", 100, 128, 64, 64, 64, "bf16", "rand"),                # largest k: dense mixture
+    ("min_gemm_shape", 64, 64, 4, 2, 64, "bf16", "rand"),               # d = f = 64 on the MFMA path
+    ("many_tokens_small", 20000, 64, 16, 2, 64, "bf16", "rand"),
+]
+
+
+@pytest.mark.parametrize("case", EXTREMES, ids=[c[0] for c in EXTREMES])
+def test_routing_and_shape_extremes(case):
+    from expert_ffn_layer_softmax_amd import moe_layer_forward
+    name, T, d, E, k, f, wfmt, mode = case
+    log(f"extreme {name}")
+    wl = Workload(name, T=T, d=d, E=E, k=k, f=f, act="bf16", wfmt=wfmt,
+                  seed=zlib.crc32(name.encode()) % 100000,
+                  x_std=1.0, wg_std=d ** -0.5, wu_std=d ** -0.5, wd_std=f ** -0.5)
+    x, w, _, logits = make_inputs(wl)
+    if mode == "hot":
+        hot = torch.tensor([3, 17, 29, 30, 41, 50, 58, 63][:k], device=logits.device)
+        logits[:, hot] += 100.0
+    res = moe_layer_forward(x, w, k, logits=logits)
+    torch.cuda.synchronize()
+    lg = logits.cpu().numpy()
+    check_routing(res, lg, k, E)
+    if mode == "hot":
+        assert set(np.unique(res["topk_idx"].cpu().numpy()).tolist()) == set(hot.cpu().tolist())
+    ref = oracle.layer(to_host_act(x), lg, k, expert_getter(w, wfmt), E=E)
+    err = rel_l2(to_host_act(res["out"]), ref["out"])
+    log(f"  rel_l2={err:.3e}")
+    assert err <= (5e-3 if wfmt == "bf16" else MXFP4_TOL)
+
+
 # ------------------------------------------------------------ HIP graphs
 @pytest.mark.parametrize("T,wfmt", [(1, "bf16"), (16, "bf16"), (100, "bf16"), (100, "mxfp4"),
                                     (100, "nvfp4"), (100, "mxfp4_fp8")])
