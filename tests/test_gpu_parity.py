@@ -102,6 +102,8 @@ SMALL = [
     ("mx_t1_bigf", 1, 64, 4, 2, 8192, "bf16", "mxfp4"),
     ("bf16_t1_bigf", 1, 64, 4, 2, 16384, "bf16", "bf16"),
     ("bf16_t47", 47, 320, 16, 4, 192, "bf16", "bf16"),          # largest T on the GEMV path
+    ("bf16_longrow_t2", 2, 3584, 8, 2, 96, "bf16", "bf16"),      # rows in quarters, 2 chunks/lane
+    ("f32_longrow_t3", 3, 2048, 8, 2, 64, "f32", "f32"),         # fp32 rows in quarters
     ("mx_t47", 47, 320, 16, 4, 192, "bf16", "mxfp4"),
     # grouped MFMA GEMM path (T >= 48, d and f multiples of 64)
     ("gg_bf16_t48", 48, 256, 8, 2, 128, "bf16", "bf16"),
