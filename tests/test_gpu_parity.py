@@ -192,15 +192,18 @@ def test_determinism_and_t0():
     assert r["out"].shape == (0, 256)
 
 
-@pytest.mark.parametrize("wfmt,k", [("bf16", 8), ("mxfp4", 8), ("nvfp4", 8), ("f32", 4), ("bf16", 16)])
-def test_single_token_fused_path_equals_stagewise(wfmt, k):
+@pytest.mark.parametrize("wfmt,k,f", [("bf16", 8, 352), ("mxfp4", 8, 352), ("nvfp4", 8, 352), ("f32", 4, 352),
+                                      ("bf16", 16, 352), ("bf16", 8, 2816), ("f32", 4, 1024),
+                                      ("bf16", 12, 2048)])
+def test_single_token_fused_path_equals_stagewise(wfmt, k, f):
     """The single-token layer (fused down+combine) is bit-identical to
-    route -> permute -> expert_ffn -> combine called one by one."""
+    route -> permute -> expert_ffn -> combine called one by one, for short
+    and full-width down rows and for k up to 16."""
     from expert_ffn_layer_softmax_amd import (moe_combine, moe_expert_ffn, moe_layer_forward,
                                               moe_permute, moe_route)
     act = "f32" if wfmt == "f32" else "bf16"
-    wl = Workload("t1eq", T=1, d=1024, E=32, k=k, f=352, act=act, wfmt=wfmt, seed=31 + k,
-                  x_std=1.0, wg_std=1024 ** -0.5, wu_std=1024 ** -0.5, wd_std=352 ** -0.5)
+    wl = Workload("t1eq", T=1, d=1024, E=32, k=k, f=f, act=act, wfmt=wfmt, seed=31 + k,
+                  x_std=1.0, wg_std=1024 ** -0.5, wu_std=1024 ** -0.5, wd_std=f ** -0.5)
     x, w, _, logits = make_inputs(wl)
     fused = moe_layer_forward(x, w, k, logits=logits)["out"]
     idx, tw = moe_route(logits, k)
