@@ -38,6 +38,12 @@ __device__ __forceinline__ float e8m0_to_f32(uint32_t s) {
   return __uint_as_float(bits);
 }
 
+// An E8M0 byte as the scale operand of the gfx950 scaled FP4 converts: they
+// read only the exponent field, with E8M0 meaning (checked on the device:
+// exponent 0 scales by 2^-127, exponent 255 gives NaN), so the byte goes
+// straight into the exponent.  Not a value for fp32 arithmetic.
+__device__ __forceinline__ float e8m0_cvt_scale(uint32_t s) { return __uint_as_float(s << 23); }
+
 // OCP FP8 E4M3 byte -> fp32, exactly: 1 sign, 4 exponent bits (bias 7),
 // 3 mantissa bits, subnormals m * 2^-9 at exponent 0.  The NaN bytes 0x7F and
 // 0xFF are outside the supported inputs (they decode to +-480 here).

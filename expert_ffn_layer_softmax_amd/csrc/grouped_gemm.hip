@@ -120,7 +120,7 @@ __device__ __forceinline__ bf16x8_t b_frag(const BRegs<WF>& b, int m, int s) {
     return __builtin_bit_cast(bf16x8_t, b.v[m][s]);
   } else {
     const uint32_t w = b.v[m][s];
-    const float sc = e8m0_to_f32(b.s[m]);
+    const float sc = e8m0_cvt_scale(b.s[m]);
     u32x4 r;
     r.x = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, sc, 0));
     r.y = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, sc, 1));
@@ -670,7 +670,7 @@ __device__ __forceinline__ void mx4_step(const char* st, const char* cb, const c
         b.lo[m] = e4m3_to_f32(q[0]);
         b.hi[m] = e4m3_to_f32(q[1]);
       } else {
-        b.lo[m] = b.hi[m] = e8m0_to_f32(static_cast<uint8_t>(sb[brow[m] * 8 + u]));
+        b.lo[m] = b.hi[m] = e8m0_cvt_scale(static_cast<uint8_t>(sb[brow[m] * 8 + u]));
       }
     }
     bf16x8_t af[2][2];

@@ -366,6 +366,30 @@ def test_routing_and_shape_extremes(case):
     assert err <= (5e-3 if wfmt == "bf16" else MXFP4_TOL)
 
 
+@pytest.mark.parametrize("T", [1, 64])
+def test_mx_nan_scale_propagates(T):
+    """An E8M0 scale byte of 255 is NaN (OCP MX): the output columns that use
+    that weight block are NaN on the device as in the oracle, and all other
+    values still match.  T=1 takes the GEMV kernels, T=64 the grouped GEMM."""
+    from expert_ffn_layer_softmax_amd import moe_layer_forward
+    wl = Workload(f"mx_nan_t{T}", T=T, d=256, E=4, k=2, f=256, act="bf16", wfmt="mxfp4", seed=77 + T,
+                  x_std=1.0, wg_std=256 ** -0.5, wu_std=256 ** -0.5, wd_std=256 ** -0.5)
+    x, w, _, logits = make_inputs(wl)
+    logits[:, 1] += 50.0  # every token uses expert 1
+    w["s_down"][1, 7, 3] = 255  # W_down row 7 (output column 7), K-block 3
+    res = moe_layer_forward(x, w, wl.k, logits=logits)
+    torch.cuda.synchronize()
+    lg = logits.cpu().numpy()
+    check_routing(res, lg, wl.k, wl.E)
+    with np.errstate(invalid="ignore"):
+        ref = oracle.layer(to_host_act(x), lg, wl.k, expert_getter(w, "mxfp4"), E=wl.E)["out"]
+    got = to_host_act(res["out"])
+    assert np.array_equal(np.isnan(got), np.isnan(ref))
+    assert np.isnan(ref[:, 7]).all() and not np.isnan(np.delete(ref, 7, axis=1)).any()
+    keep = ~np.isnan(ref)
+    assert rel_l2(got[keep], ref[keep]) <= MXFP4_TOL
+
+
 # ------------------------------------------------------------ HIP graphs
 @pytest.mark.parametrize("T,wfmt", [(1, "bf16"), (16, "bf16"), (100, "bf16"), (100, "mxfp4"),
                                     (100, "nvfp4"), (100, "mxfp4_fp8")])
