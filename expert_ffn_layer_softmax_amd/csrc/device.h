@@ -31,13 +31,6 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
   return (uint16_t)(u >> 16);
 }
 
-// E8M0 block scale -> fp32 power of two 2^(s-127).  s = 0 is the subnormal
-// 2^-127; s = 255 is NaN.
-__device__ __forceinline__ float e8m0_to_f32(uint32_t s) {
-  uint32_t bits = (s == 0u) ? 0x00400000u : (s == 255u ? 0x7fc00000u : (s << 23));
-  return __uint_as_float(bits);
-}
-
 // An E8M0 byte as the scale operand of the gfx950 scaled FP4 converts: they
 // read only the exponent field, with E8M0 meaning (checked on the device:
 // exponent 0 scales by 2^-127, exponent 255 gives NaN), so the byte goes
@@ -56,19 +49,12 @@ __device__ __forceinline__ float e4m3_to_f32(uint32_t b) {
 
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 
-// Two E2M1 codes in byte `sel` of `w` -> fp32 pair (low nibble first), by
-// the gfx950 scaled-convert instruction with unit scale.
-template <int SEL>
-__device__ __forceinline__ float2 fp4x2_to_f32(uint32_t w) {
-  auto v = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, SEL);
-  return make_float2(v[0], v[1]);
-}
-
 // Two E2M1 codes in byte `sel` of `w` -> packed bf16 pair (low nibble in the
-// low half).  E2M1 values are exact in bf16.
+// low half), each times the power of two in `sc`'s exponent field.  E2M1
+// values are exact in bf16; scaled ones are while finite.
 template <int SEL>
-__device__ __forceinline__ uint32_t fp4x2_to_bf16x2(uint32_t w) {
-  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, 1.0f, SEL));
+__device__ __forceinline__ uint32_t fp4x2_to_bf16x2(uint32_t w, float sc = 1.0f) {
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, sc, SEL));
 }
 
 // acc + a.lo*b.lo + a.hi*b.hi for packed bf16 pairs (v_dot2c_f32_bf16; the

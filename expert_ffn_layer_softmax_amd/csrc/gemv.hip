@@ -69,21 +69,26 @@ struct XChunk {
   u32x4 v[WT<WF>::XB / 16];
 };
 
-// acc + <codes, x> for code word j of a 4-bit chunk (elements 8j..8j+7; byte
-// b holds elements 8j+2b, 8j+2b+1) and the matching activation vector j.
-__device__ __forceinline__ float fp4_word_dot(uint32_t cw_in, const u32x4& xv, float acc) {
-  const uint32_t cw = opaque(cw_in);
-  acc = dot2_bf16(fp4x2_to_bf16x2<0>(cw), xv.x, acc);
-  acc = dot2_bf16(fp4x2_to_bf16x2<1>(cw), xv.y, acc);
-  acc = dot2_bf16(fp4x2_to_bf16x2<2>(cw), xv.z, acc);
-  acc = dot2_bf16(fp4x2_to_bf16x2<3>(cw), xv.w, acc);
+// acc + <codes * scale, x> for code word j of a 4-bit chunk (elements
+// 8j..8j+7; byte b holds elements 8j+2b, 8j+2b+1) and the matching activation
+// vector j.  `sc` is the convert's scale operand (only its exponent is read).
+// OPQ hides the word from the optimiser, so that kernels which apply the same
+// weights to several tokens convert them again per token instead of holding
+// four times the registers.
+template <bool OPQ>
+__device__ __forceinline__ float fp4_word_dot(uint32_t cw_in, const u32x4& xv, float sc, float acc) {
+  const uint32_t cw = OPQ ? opaque(cw_in) : cw_in;
+  acc = dot2_bf16(fp4x2_to_bf16x2<0>(cw, sc), xv.x, acc);
+  acc = dot2_bf16(fp4x2_to_bf16x2<1>(cw, sc), xv.y, acc);
+  acc = dot2_bf16(fp4x2_to_bf16x2<2>(cw, sc), xv.z, acc);
+  acc = dot2_bf16(fp4x2_to_bf16x2<3>(cw, sc), xv.w, acc);
   return acc;
 }
 
-// acc + <w, x> over one chunk.  For the 4-bit formats the block scales are
-// left out: scaled_chunk applies them to the partial sums.
-template <int WF>
-__device__ __forceinline__ float dot_chunk(const u32x4& w, const XChunk<WF>& x, float acc) {
+// acc + <w, x> over one chunk.  4-bit codes are converted with scale `sc`.
+template <int WF, bool OPQ = true>
+__device__ __forceinline__ float dot_chunk(const u32x4& w, const XChunk<WF>& x, float acc,
+                                           float sc = 1.0f) {
   if constexpr (WF == kF32) {
     acc = fmaf(__uint_as_float(w.x), __uint_as_float(x.v[0].x), acc);
     acc = fmaf(__uint_as_float(w.y), __uint_as_float(x.v[0].y), acc);
@@ -96,25 +101,29 @@ __device__ __forceinline__ float dot_chunk(const u32x4& w, const XChunk<WF>& x, 
     acc = dot2_bf16(w.w, x.v[0].w, acc);
   } else {
     // activation vector j holds the 8 elements of code word j as 4 bf16 pairs
-    acc = fp4_word_dot(w.x, x.v[0], acc);
-    acc = fp4_word_dot(w.y, x.v[1], acc);
-    acc = fp4_word_dot(w.z, x.v[2], acc);
-    acc = fp4_word_dot(w.w, x.v[3], acc);
+    acc = fp4_word_dot<OPQ>(w.x, x.v[0], sc, acc);
+    acc = fp4_word_dot<OPQ>(w.y, x.v[1], sc, acc);
+    acc = fp4_word_dot<OPQ>(w.z, x.v[2], sc, acc);
+    acc = fp4_word_dot<OPQ>(w.w, x.v[3], sc, acc);
   }
   return acc;
 }
 
-// acc + the chunk's contribution with its block scales: MX-FP4 scales the
-// chunk's sum by s; NVFP4 scales elements 0..15 (words 0, 1) by s and 16..31
-// (words 2, 3) by s2; other formats have no block scale.
-template <int WF>
+// acc + the chunk's contribution with its block scales.  MX-FP4: the E8M0
+// scale (a power of two) goes into the convert, so each weight reaches the
+// dot product as code * 2^(s-127) in bf16 -- exact while it is finite in bf16
+// (block scales up to 2^125), as in the grouped GEMMs.  NVFP4 (E4M3 scales,
+// not powers of two): elements 0..15 (words 0, 1) sum to a partial that is
+// scaled by s in fp32, elements 16..31 (words 2, 3) by s2.  Other formats have
+// no block scale.
+template <int WF, bool OPQ = true>
 __device__ __forceinline__ float scaled_chunk(const u32x4& w, const XChunk<WF>& x, float s, float s2,
                                               float acc) {
   if constexpr (WF == kMXFP4) {
-    return fmaf(dot_chunk<WF>(w, x, 0.f), s, acc);
+    return dot_chunk<WF, OPQ>(w, x, acc, s);
   } else if constexpr (WF == kNVFP4) {
-    const float lo = fp4_word_dot(w.y, x.v[1], fp4_word_dot(w.x, x.v[0], 0.f));
-    const float hi = fp4_word_dot(w.w, x.v[3], fp4_word_dot(w.z, x.v[2], 0.f));
+    const float lo = fp4_word_dot<OPQ>(w.y, x.v[1], 1.0f, fp4_word_dot<OPQ>(w.x, x.v[0], 1.0f, 0.f));
+    const float hi = fp4_word_dot<OPQ>(w.w, x.v[3], 1.0f, fp4_word_dot<OPQ>(w.z, x.v[2], 1.0f, 0.f));
     return fmaf(hi, s2, fmaf(lo, s, acc));
   } else {
     return dot_chunk<WF>(w, x, acc);
@@ -144,7 +153,7 @@ __device__ __forceinline__ float matrix_scaled(float v, const float* t, int e) {
 template <int WF, int MAXC, int RPW>
 struct RowRegs {
   u32x4 w[RPW][MAXC];
-  float s[RPW][MAXC];   // 4-bit block scale (NVFP4: of elements 0..15)
+  float s[RPW][MAXC];   // MX-FP4: convert scale operand; NVFP4: scale of elements 0..15
   float s2[RPW][MAXC];  // NVFP4: block scale of elements 16..31
   uint32_t sw[RPW];     // this lane's scale word(s), until unpack()
   uint32_t sw2[RPW];    // NVFP4: second word
@@ -186,7 +195,7 @@ struct RowRegs {
         if (r < nrows && c < cend) {
           w[r][i] = ld_stream16(row0 + r * rb + (size_t)c * 16);
           if constexpr (WF == kMXFP4) {
-            if (!words) s[r][i] = e8m0_to_f32(s0[r * sb + c]);
+            if (!words) s[r][i] = e8m0_cvt_scale(s0[r * sb + c]);
           } else if constexpr (WF == kNVFP4) {
             if (!words) {
               s[r][i] = e4m3_to_f32(s0[r * sb + 2 * (size_t)c]);
@@ -209,7 +218,7 @@ struct RowRegs {
             const int src = (cl >> 2) & (kWave - 1);
             const uint32_t v = __shfl(sw[r], src, kWave);
             if constexpr (WF == kMXFP4) {
-              s[r][i] = e8m0_to_f32((v >> (8 * (cl & 3))) & 0xffu);
+              s[r][i] = e8m0_cvt_scale((v >> (8 * (cl & 3))) & 0xffu);
             } else {
               const uint32_t v2 = __shfl(sw2[r], src, kWave);
               const uint32_t word = (cl & 2) ? v2 : v;
@@ -227,12 +236,13 @@ struct RowRegs {
     load(row0, rb, s0, sb, nrows, c0, cend, lane);
     unpack(lane);
   }
-  // acc + chunk i of row r with its block scales
+  // acc + chunk i of row r with its block scales (OPQ: see fp4_word_dot)
+  template <bool OPQ = true>
   __device__ __forceinline__ float fma_chunk(int r, int i, const XChunk<WF>& x, float acc) const {
     if constexpr (WF == kNVFP4)
-      return scaled_chunk<WF>(w[r][i], x, s[r][i], s2[r][i], acc);
+      return scaled_chunk<WF, OPQ>(w[r][i], x, s[r][i], s2[r][i], acc);
     else if constexpr (WF == kMXFP4)
-      return scaled_chunk<WF>(w[r][i], x, s[r][i], 0.f, acc);
+      return scaled_chunk<WF, OPQ>(w[r][i], x, s[r][i], 0.f, acc);
     else
       return scaled_chunk<WF>(w[r][i], x, 0.f, 0.f, acc);
   }
@@ -421,8 +431,8 @@ __global__ __launch_bounds__(256) void gemv_gate_up_t1_rows_kernel(GateUpArgs a)
       for (int i = 0; i < MAXC; ++i) {
         const int c = i * kWave + lane;
         if (c < nchunks) {
-          ag = G[cur].fma_chunk(0, i, xc[i], ag);
-          au = U[cur].fma_chunk(0, i, xc[i], au);
+          ag = G[cur].template fma_chunk<false>(0, i, xc[i], ag);
+          au = U[cur].template fma_chunk<false>(0, i, xc[i], au);
         }
       }
       const float gs = matrix_scaled<WF>(wave_sum(ag), a.tg, e);
@@ -552,7 +562,7 @@ __global__ __launch_bounds__(NTH) void gemv_down_combine_t1_kernel(DownCombineAr
     const int c = i * kWave + lane;
     if (c < nchunks) {
 #pragma unroll
-      for (int r = 0; r < RPW; ++r) acc[r] = W.fma_chunk(r, i, hc[i], acc[r]);
+      for (int r = 0; r < RPW; ++r) acc[r] = W.template fma_chunk<false>(r, i, hc[i], acc[r]);
     }
   }
 #pragma unroll

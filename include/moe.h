@@ -38,6 +38,9 @@
  *                      per byte, element 2i in the low nibble; E8M0 scales
  *                      uint8 [E][f][d/32] / [E][d][f/32], one per 32
  *                      consecutive elements along the reduction dimension.
+ *                      The kernels form each weight, code * 2^(s-127), in
+ *                      bf16: scale bytes s <= 252 keep it finite; s = 255
+ *                      (NaN) propagates.
  *    NVFP4 weights:    the same codes; OCP FP8 E4M3 scales uint8 [E][f][d/16]
  *                      / [E][d][f/16], one per 16 consecutive elements along
  *                      the reduction dimension; fp32 scales t_gate, t_up,
