@@ -20,6 +20,11 @@
 // Tokens are then processed one at a time against the weights held in
 // registers.  Rows longer than MAXC*64 chunks (MULTISEG) are streamed in
 // segments, re-reading the weights per token.
+#include <algorithm>
+#include <map>
+#include <mutex>
+#include <tuple>
+
 #include "device.h"
 #include "internal.h"
 
@@ -378,67 +383,176 @@ __global__ __launch_bounds__(256) void gemv_gate_up_kernel(GateUpArgs a) {
   }
 }
 
-// Single token (one row per slot): each wave walks R consecutive rows of its
-// expert, issuing the next row's loads before computing the current one, so a
-// wave keeps a row in flight for its whole life and the per-wave start-up
-// (slot lookup, token index, activation loads) is paid once per R rows.
-template <int WF, int MAXC, int R>
-__global__ __launch_bounds__(256) void gemv_gate_up_t1_rows_kernel(GateUpArgs a) {
-  constexpr int CE = WT<WF>::CE;
-  const int lane = lane_id();
-  const int wave = threadIdx.x >> 6;
-  const int RB = 4 * R;
-  const int tiles = (a.f + RB - 1) / RB;
-  const int slot = blockIdx.x / tiles;
-  if (slot >= *a.num_active) return;
-  const int n0 = (blockIdx.x - slot * tiles) * RB + wave * R;
-  if (n0 >= a.f) return;
-  const int e = a.slot_info[4 * slot + 0];
-  const int nrows = min(R, a.f - n0);
-  const int nchunks = a.d / CE;
-  const size_t rb = WT<WF>::row_bytes(a.d);
-  const size_t sb = scale_row_bytes<WF>(a.d);
-  const size_t woff = (size_t)e * a.f + n0;
-  const char* gp = reinterpret_cast<const char*>(a.wg) + woff * rb;
-  const char* up = reinterpret_cast<const char*>(a.wu) + woff * rb;
-  const uint8_t* sgp = is_fp4(WF) ? a.sg + woff * sb : nullptr;
-  const uint8_t* sup = is_fp4(WF) ? a.su + woff * sb : nullptr;
+// Single token, balanced over the CUs: the grid is exactly the blocks the GPU
+// holds at once, and wave g of W takes rows g, g + W, g + 2W, ... of all the
+// active slots' rows laid end to end, so every CU streams the same number of
+// rows and every wave starts at once (with a few blocks per CU, whole blocks
+// per CU differ by up to half).  The activation row sits in LDS, chunk c at
+// byte 80c (64 bytes plus padding, spreading neighbouring lanes over the
+// banks), instead of in registers, leaving room for more waves.  A wave keeps
+// the next row's loads in flight while it computes the current one.  Every
+// global load and store is issued unconditionally (addresses clamped into the
+// row; past the wave's last row the prefetch is a buffer load over an empty
+// range, which returns zeros without touching memory), so the wait before a
+// row's arithmetic covers that row's loads only, not the prefetch behind them.
+// Requires d % 128 == 0 (whole 4-byte scale words per row).  Each row is
+// computed as in gemv_gate_up_kernel: same chunks per lane, same order.
+constexpr int kXStride = 80;
+// Raw buffer descriptors: word 3 of the resource (32-bit data format, as for
+// untyped loads) and the non-temporal cache-policy bit of a buffer load.
+constexpr int kBufWord3 = 0x00020000;
+constexpr int kBufNT = 2;
 
-  RowRegs<WF, MAXC, 1> G[2], U[2];
-  G[0].load(gp, rb, sgp, sb, 1, 0, nchunks, lane);
-  U[0].load(up, rb, sup, sb, 1, 0, nchunks, lane);
-  const int r0 = a.slot_info[4 * slot + 1];
-  const char* xr = reinterpret_cast<const char*>(a.x) +
-                   (size_t)(a.sorted_src[r0] / a.k) * a.d * act_bytes<WF>();
-  XChunk<WF> xc[MAXC];
+// One 4-bit weight row held by a wave: chunk c = i*64 + lane in w[i], the
+// block scales of chunks 4*lane .. 4*lane+3 in sw (NVFP4: sw, sw2) until
+// unpack().  Loads are buffer loads with in-row (clamped) offsets; live ==
+// false gives empty ranges.  Needs whole scale words: chunks % 4 == 0.
+template <int WF, int MAXC>
+struct BufRow {
+  u32x4 w[MAXC];
+  uint32_t sw, sw2;
+  float s[MAXC], s2[MAXC];
+
+  __device__ __forceinline__ void load(const char* row, const uint8_t* srow, bool live, int rb,
+                                       int sb, int nchunks, int lane) {
+    const __amdgpu_buffer_rsrc_t wr =
+        __builtin_amdgcn_make_buffer_rsrc((void*)row, 0, live ? rb : 0, kBufWord3);
+    const __amdgpu_buffer_rsrc_t sr =
+        __builtin_amdgcn_make_buffer_rsrc((void*)srow, 0, live ? sb : 0, kBufWord3);
+    const int qw = min(lane, (nchunks >> 2) - 1);
+    if constexpr (WF == kNVFP4) {
+      sw = __builtin_amdgcn_raw_buffer_load_b32(sr, 8 * qw, 0, 0);
+      sw2 = __builtin_amdgcn_raw_buffer_load_b32(sr, 8 * qw + 4, 0, 0);
+    } else {
+      sw = __builtin_amdgcn_raw_buffer_load_b32(sr, 4 * qw, 0, 0);
+    }
+#pragma unroll
+    for (int i = 0; i < MAXC; ++i)
+      w[i] = __builtin_amdgcn_raw_buffer_load_b128(wr, min(i * kWave + lane, nchunks - 1) * 16, 0, kBufNT);
+  }
+  // Every lane of the wave must call.
+  __device__ __forceinline__ void unpack(int lane) {
+#pragma unroll
+    for (int i = 0; i < MAXC; ++i) {
+      const int c = i * kWave + lane;
+      const int src = (c >> 2) & (kWave - 1);
+      const uint32_t v = __shfl(sw, src, kWave);
+      if constexpr (WF == kMXFP4) {
+        s[i] = e8m0_cvt_scale((v >> (8 * (c & 3))) & 0xffu);
+      } else {
+        const uint32_t v2 = __shfl(sw2, src, kWave);
+        const uint32_t word = (c & 2) ? v2 : v;
+        const uint32_t sh = 16 * (c & 1);
+        s[i] = e4m3_to_f32((word >> sh) & 0xffu);
+        s2[i] = e4m3_to_f32((word >> (sh + 8)) & 0xffu);
+      }
+    }
+  }
+  // acc + chunk i against x; a chunk past the row (the clamped duplicate) is
+  // left out by a select, not a branch (a branch would hide waits)
+  __device__ __forceinline__ float fma_chunk(int i, const XChunk<WF>& x, float acc, int nchunks,
+                                             int lane) const {
+    const float t = scaled_chunk<WF, false>(w[i], x, s[i], s2[i], acc);
+    return i * kWave + lane < nchunks ? t : acc;
+  }
+};
+
+// A gate/up row: gate and up weights of row n of an active slot's expert.
+template <int WF, int MAXC>
+struct T1Row {
+  BufRow<WF, MAXC> g, u;
+  int e;
+  size_t hidx;  // element of h the row's result goes to
+
+  // Row q (wave-uniform) of the active slots' rows.  Lane l of slot_e / slot_r
+  // holds slot l's expert and first row (preloaded: a table lookup here would
+  // be a vector load queued behind the prefetch, and waiting for it would wait
+  // for everything).
+  __device__ __forceinline__ void load(const GateUpArgs& a, int q, bool live, int slot_e,
+                                       int slot_r, int nchunks, int lane) {
+    const int slot = q / a.f;
+    const int n = q - slot * a.f;
+    e = __builtin_amdgcn_readlane(slot_e, slot);
+    hidx = (size_t)__builtin_amdgcn_readlane(slot_r, slot) * a.f + n;
+    const size_t woff = (size_t)e * a.f + n;
+    const int rb = (int)WT<WF>::row_bytes(a.d);
+    const int sb = (int)scale_row_bytes<WF>(a.d);
+    g.load(reinterpret_cast<const char*>(a.wg) + woff * rb, a.sg + woff * sb, live, rb, sb, nchunks, lane);
+    u.load(reinterpret_cast<const char*>(a.wu) + woff * rb, a.su + woff * sb, live, rb, sb, nchunks, lane);
+  }
+};
+
+template <int WF, int MAXC>
+__device__ __forceinline__ void t1_row_compute(const GateUpArgs& a, T1Row<WF, MAXC>& R,
+                                               const char* xs, int nchunks, int lane) {
+  R.g.unpack(lane);
+  R.u.unpack(lane);
+  float ag = 0.f, au = 0.f;
 #pragma unroll
   for (int i = 0; i < MAXC; ++i) {
-    const int c = i * kWave + lane;
-    if (c < nchunks) xc[i] = load_x<WF>(xr, c);
+    // re-read per row (the offset is hidden from the optimiser), so the
+    // activations are not hoisted back into registers
+    const char* xp = xs + opaque((uint32_t)(min(i * kWave + lane, nchunks - 1) * kXStride));
+    XChunk<WF> xc;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) xc.v[j] = *reinterpret_cast<const u32x4*>(xp + 16 * j);
+    ag = R.g.fma_chunk(i, xc, ag, nchunks, lane);
+    au = R.u.fma_chunk(i, xc, au, nchunks, lane);
   }
+  const float gs = matrix_scaled<WF>(wave_sum(ag), a.tg, R.e);
+  const float us = matrix_scaled<WF>(wave_sum(au), a.tu, R.e);
+  store_act<WF>(a.h, R.hidx, silu(gs) * us);  // every lane stores the same value
+}
+
+template <int WF, int MAXC>
+__global__ __launch_bounds__(256) void gemv_gate_up_t1_bal_kernel(GateUpArgs a) {
+  static_assert(is_fp4(WF), "4-bit weights only");
+  extern __shared__ __align__(16) char xs[];
+  const int lane = lane_id();
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int W = gridDim.x * 4;
+  const int nchunks = a.d / WT<WF>::CE;
+  const int nact = *a.num_active;  // at most k <= 64 slots for one token
+  const int N = nact * a.f;
+  if (N <= 0) return;  // uniform over the grid
+  int q = blockIdx.x * 4 + wave;
+  if (q >= N) q = N - 1;  // surplus waves (grid larger than the rows) redo the last row
+  const int sl = min(lane, nact - 1);
+  const int slot_e = a.slot_info[4 * sl + 0];
+  const int slot_r = a.slot_info[4 * sl + 1];
+
+  // the token's activations (T = 1: row 0 of x), 16 bytes per thread a step,
+  // loaded before the weights so that waiting for them does not wait for those
+  u32x4 xv[MAXC];
 #pragma unroll
-  for (int r = 0; r < R; ++r) {
-    if (r < nrows) {
-      const int cur = r & 1;
-      if (r + 1 < nrows) {
-        G[cur ^ 1].load(gp + (r + 1) * rb, rb, sgp + (r + 1) * sb, sb, 1, 0, nchunks, lane);
-        U[cur ^ 1].load(up + (r + 1) * rb, rb, sup + (r + 1) * sb, sb, 1, 0, nchunks, lane);
-      }
-      G[cur].unpack(lane);
-      U[cur].unpack(lane);
-      float ag = 0.f, au = 0.f;
+  for (int k = 0; k < MAXC; ++k) {
+    const int p = min(k * 256 + (int)threadIdx.x, nchunks * 4 - 1);
+    xv[k] = ld16(reinterpret_cast<const char*>(a.x) + (size_t)p * 16);
+  }
+  T1Row<WF, MAXC> A, B;
+  A.load(a, q, true, slot_e, slot_r, nchunks, lane);
 #pragma unroll
-      for (int i = 0; i < MAXC; ++i) {
-        const int c = i * kWave + lane;
-        if (c < nchunks) {
-          ag = G[cur].template fma_chunk<false>(0, i, xc[i], ag);
-          au = U[cur].template fma_chunk<false>(0, i, xc[i], au);
-        }
-      }
-      const float gs = matrix_scaled<WF>(wave_sum(ag), a.tg, e);
-      const float us = matrix_scaled<WF>(wave_sum(au), a.tu, e);
-      if (lane == 0) store_act<WF>(a.h, (size_t)r0 * a.f + n0 + r, silu(gs) * us);
-    }
+  for (int k = 0; k < MAXC; ++k) {
+    const int p = min(k * 256 + (int)threadIdx.x, nchunks * 4 - 1);
+    *reinterpret_cast<u32x4*>(xs + (p >> 2) * kXStride + 16 * (p & 3)) = xv[k];
+  }
+  __syncthreads();
+  for (;;) {
+    const bool lb = q + W < N;
+    const int qb = lb ? q + W : q;
+    B.load(a, qb, lb, slot_e, slot_r, nchunks, lane);
+    // memory instructions keep this order (the prefetch goes out before this
+    // row's scale shuffles); arithmetic may cross
+    __builtin_amdgcn_sched_barrier(1);
+    t1_row_compute<WF, MAXC>(a, A, xs, nchunks, lane);
+    if (!lb) break;
+    const bool la = qb + W < N;
+    const int qa = la ? qb + W : qb;
+    A.load(a, qa, la, slot_e, slot_r, nchunks, lane);
+    __builtin_amdgcn_sched_barrier(1);
+    t1_row_compute<WF, MAXC>(a, B, xs, nchunks, lane);
+    if (!la) break;
+    q = qa;
   }
 }
 
@@ -579,6 +693,71 @@ __global__ __launch_bounds__(NTH) void gemv_down_combine_t1_kernel(DownCombineAr
   }
 }
 
+// Single token, 4-bit weights: down projection fused with the weighted
+// combine as in gemv_down_combine_t1_kernel (block = k waves over the same RPW
+// output rows, wave j on slot j, results meeting in LDS and summed in slot
+// order), but a wave streams its rows through a ring of D + 1 row buffers
+// instead of holding all of them at once.  Fewer registers let the blocks the
+// grid needs be resident together (holding all rows took two rounds).  The
+// ring turns in a loop the compiler does not unroll, so it cannot hoist later
+// rows' loads and undo the ring.  Loads are issued unconditionally -- past the
+// block's rows as buffer loads over an empty range -- so the wait before a
+// row's arithmetic covers that row only.  Each row is computed as in the
+// other kernel: same chunks per lane, same order, a chunk past the row left
+// out.  Requires f % 128 == 0 and RPW % (D + 1) == 0.
+template <int WF, int MAXC, int RPW, int D, int NTH>
+__global__ __launch_bounds__(NTH) void gemv_down_combine_t1_ring_kernel(DownCombineArgs a) {
+  static_assert(is_fp4(WF), "4-bit weights only");
+  static_assert(RPW % (D + 1) == 0, "whole turns of the ring");
+  __shared__ float ys[16][RPW];
+  const int lane = lane_id();
+  const int j = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int n0 = blockIdx.x * RPW;
+  const int nrows = min(RPW, a.d - n0);
+  const int e = a.topk_idx[j];
+  const int nchunks = a.f / WT<WF>::CE;
+  const int rb = (int)WT<WF>::row_bytes(a.f);
+  const int sb = (int)scale_row_bytes<WF>(a.f);
+  // slot j's activations (its row of h), loaded first so that waiting for
+  // them does not wait for the weights
+  const char* hr = reinterpret_cast<const char*>(a.h) + (size_t)a.dest_row[j] * a.f * act_bytes<WF>();
+  XChunk<WF> hc[MAXC];
+#pragma unroll
+  for (int i = 0; i < MAXC; ++i) hc[i] = load_x<WF>(hr, min(i * kWave + lane, nchunks - 1));
+  const size_t woff = (size_t)e * a.d + n0;
+  const char* w0 = reinterpret_cast<const char*>(a.wd) + woff * rb;
+  const uint8_t* s0 = a.sd + woff * sb;
+  auto load_row = [&](BufRow<WF, MAXC>& buf, int r) {
+    const int rr = min(r, nrows - 1);
+    buf.load(w0 + (size_t)rr * rb, s0 + (size_t)rr * sb, r < nrows, rb, sb, nchunks, lane);
+  };
+  BufRow<WF, MAXC> ring[D + 1];
+#pragma unroll
+  for (int r = 0; r < D; ++r) load_row(ring[r], r);
+#pragma unroll 1
+  for (int r0 = 0; r0 < RPW; r0 += D + 1) {
+#pragma unroll
+    for (int t = 0; t <= D; ++t) {
+      load_row(ring[(t + D) % (D + 1)], r0 + t + D);
+      // memory instructions keep this order; arithmetic may cross
+      __builtin_amdgcn_sched_barrier(1);
+      ring[t].unpack(lane);
+      float acc = 0.f;
+#pragma unroll
+      for (int i = 0; i < MAXC; ++i) acc = ring[t].fma_chunk(i, hc[i], acc, nchunks, lane);
+      const float y = matrix_scaled<WF>(wave_sum(acc), a.td, e);
+      ys[j][r0 + t] = y;  // every lane writes the same value
+    }
+  }
+  __syncthreads();
+  if ((int)threadIdx.x < nrows) {
+    const int r = threadIdx.x;
+    float v = 0.f;
+    for (int q = 0; q < a.k; ++q) v = fmaf(a.topk_w[q], ys[q][r], v);
+    store_act<WF>(a.out, (size_t)n0 + r, v);
+  }
+}
+
 // ---------------------------------------------------------------- launch --
 int chunk_elems(int wf) { return wf == kF32 ? 4 : (wf == kBF16 ? 8 : 32); }  // 4-bit: 32
 
@@ -592,9 +771,6 @@ int pick_maxc(int nchunks, int wf) {
     if (need <= o && o <= cap) return o;
   return cap;
 }
-
-// Rows walked per wave by the single-token 4-bit gate/up kernel.
-constexpr int kT1Rows = 8;
 
 // Rows per wave so that a wave keeps about 12 chunks per matrix in flight.
 constexpr int rpw_for(int maxc) { return maxc >= 12 ? 1 : (maxc >= 6 ? 2 : (maxc >= 3 ? 1 : 4)); }
@@ -635,6 +811,27 @@ constexpr int rpw_t1_small(int maxc) { return maxc <= 2 ? 8 : rpw_for(maxc); }
   if (MULTI) { constexpr bool MS = true; CALL; }     \
   else { constexpr bool MS = false; CALL; }
 
+// Blocks of `threads` threads that the current device holds at once for kernel
+// `fn` with `lds` bytes of dynamic LDS: CUs times blocks per CU (cached per
+// device, kernel and LDS size).
+long long resident_blocks(const void* fn, int threads, size_t lds) {
+  static std::mutex mu;
+  static std::map<std::tuple<int, const void*, size_t>, long long> cache;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 1;
+  const auto key = std::make_tuple(dev, fn, lds);
+  std::lock_guard<std::mutex> lk(mu);
+  auto it = cache.find(key);
+  if (it != cache.end()) return it->second;
+  int cus = 0, per_cu = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, threads, lds) != hipSuccess)
+    return 1;
+  const long long n = std::max(1LL, (long long)cus * per_cu);
+  cache[key] = n;
+  return n;
+}
+
 }  // namespace
 
 hipError_t launch_gemv_gate_up(const Dims& dm, const void* x, const Plan& p, const Weights& w,
@@ -663,22 +860,27 @@ hipError_t launch_gemv_gate_up(const Dims& dm, const void* x, const Plan& p, con
     }
     return hipGetLastError();
   }
-  if (dm.T == 1 && is_fp4(dm.wfmt) && !multi) {
-    // short rows: each wave walks kT1Rows rows with the next row in flight
-    const dim3 grid((unsigned)(max_active * ((dm.f + 4 * kT1Rows - 1) / (4 * kT1Rows)))), block(256);
-#define MOE_T1ROWS(WFV)                                                                          \
-  switch (maxc) {                                                                                \
-    case 1: gemv_gate_up_t1_rows_kernel<WFV, 1, kT1Rows><<<grid, block, 0, s>>>(a); break;       \
-    case 2: gemv_gate_up_t1_rows_kernel<WFV, 2, kT1Rows><<<grid, block, 0, s>>>(a); break;       \
-    case 3: gemv_gate_up_t1_rows_kernel<WFV, 3, kT1Rows><<<grid, block, 0, s>>>(a); break;       \
-    default: gemv_gate_up_t1_rows_kernel<WFV, 4, kT1Rows><<<grid, block, 0, s>>>(a); break;      \
+  if (dm.T == 1 && is_fp4(dm.wfmt) && !multi && dm.d % 128 == 0 && dm.k <= kWave) {
+    // short rows, one token: rows dealt evenly over a grid the GPU holds at once
+    const size_t lds = (size_t)nchunks * kXStride;
+    const long long rows = max_active * dm.f;
+    auto go = [&](const void* fn, auto kern) {
+      const long long g = std::min<long long>(resident_blocks(fn, 256, lds), (rows + 3) / 4);
+      kern<<<dim3((unsigned)std::max<long long>(g, 1)), dim3(256), lds, s>>>(a);
+    };
+#define MOE_T1BAL(WFV)                                                                                       \
+  switch (maxc) {                                                                                            \
+    case 1: go((const void*)gemv_gate_up_t1_bal_kernel<WFV, 1>, gemv_gate_up_t1_bal_kernel<WFV, 1>); break;  \
+    case 2: go((const void*)gemv_gate_up_t1_bal_kernel<WFV, 2>, gemv_gate_up_t1_bal_kernel<WFV, 2>); break;  \
+    case 3: go((const void*)gemv_gate_up_t1_bal_kernel<WFV, 3>, gemv_gate_up_t1_bal_kernel<WFV, 3>); break;  \
+    default: go((const void*)gemv_gate_up_t1_bal_kernel<WFV, 4>, gemv_gate_up_t1_bal_kernel<WFV, 4>); break; \
   }
     if (dm.wfmt == kMXFP4) {
-      MOE_T1ROWS(kMXFP4)
+      MOE_T1BAL(kMXFP4)
     } else {
-      MOE_T1ROWS(kNVFP4)
+      MOE_T1BAL(kNVFP4)
     }
-#undef MOE_T1ROWS
+#undef MOE_T1BAL
     return hipGetLastError();
   }
   const int rpw = rpw_for(maxc);
@@ -719,6 +921,19 @@ hipError_t launch_gemv_down_combine_t1(const Dims& dm, const void* h, const Plan
   DownCombineArgs a{h, w.wd, w.sd, w.td, topk_idx, topk_w, p.dest_row, out, dm.d, dm.f, dm.k};
   const int maxc = pick_maxc(dm.f / chunk_elems(dm.wfmt), dm.wfmt);
   const dim3 block(64 * dm.k);
+  if (is_fp4(dm.wfmt) && dm.k <= 8 && maxc <= 2 && dm.f % 128 == 0) {
+    // 4-bit rows of up to 128 chunks: 12 output rows per block streamed
+    // through a four-row ring (d = 6144 gives 512 blocks, two per CU)
+    const dim3 grid((unsigned)((dm.d + 11) / 12));
+    if (dm.wfmt == kMXFP4) {
+      if (maxc == 1) gemv_down_combine_t1_ring_kernel<kMXFP4, 1, 12, 3, 512><<<grid, block, 0, s>>>(a);
+      else gemv_down_combine_t1_ring_kernel<kMXFP4, 2, 12, 3, 512><<<grid, block, 0, s>>>(a);
+    } else {
+      if (maxc == 1) gemv_down_combine_t1_ring_kernel<kNVFP4, 1, 12, 3, 512><<<grid, block, 0, s>>>(a);
+      else gemv_down_combine_t1_ring_kernel<kNVFP4, 2, 12, 3, 512><<<grid, block, 0, s>>>(a);
+    }
+    return hipGetLastError();
+  }
   if (dm.k <= 8) {  // 512-thread blocks: up to 256 registers, twice the short rows per wave
     const int rpw = rpw_t1_small(maxc);
     const dim3 grid((unsigned)((dm.d + rpw - 1) / rpw));

@@ -100,6 +100,14 @@ SMALL = [
     ("bf16_t1_k20", 1, 256, 32, 20, 64, "bf16", "bf16"),
     ("f32_t1", 1, 128, 8, 3, 64, "f32", "f32"),
     ("mx_t1_bigf", 1, 64, 4, 2, 8192, "bf16", "mxfp4"),
+    # single token, 4-bit, the balanced gate/up and ring down+combine kernels:
+    # 40 and 88 chunks per row (partial last chunk slot), d % 12 != 0 (partial
+    # last block of 12 output rows), 64 slots, 256 chunks per gate/up row
+    ("mx_t1_ring", 1, 1280, 16, 8, 2816, "bf16", "mxfp4"),
+    ("nv_t1_ring", 1, 1280, 16, 6, 1408, "bf16", "nvfp4"),
+    ("mx_t1_k64", 1, 256, 64, 64, 128, "bf16", "mxfp4"),
+    ("mx_t1_bigd", 1, 8192, 8, 2, 256, "bf16", "mxfp4"),
+    ("nv_t1_bigd", 1, 8192, 8, 3, 384, "bf16", "nvfp4"),
     ("bf16_t1_bigf", 1, 64, 4, 2, 16384, "bf16", "bf16"),
     ("bf16_t47", 47, 320, 16, 4, 192, "bf16", "bf16"),          # largest T on the GEMV path
     ("bf16_longrow_t2", 2, 3584, 8, 2, 96, "bf16", "bf16"),      # rows in quarters, 2 chunks/lane
@@ -194,7 +202,8 @@ def test_determinism_and_t0():
 
 @pytest.mark.parametrize("wfmt,k,f", [("bf16", 8, 352), ("mxfp4", 8, 352), ("nvfp4", 8, 352), ("f32", 4, 352),
                                       ("bf16", 16, 352), ("bf16", 8, 2816), ("f32", 4, 1024),
-                                      ("bf16", 12, 2048)])
+                                      ("bf16", 12, 2048), ("mxfp4", 8, 2816), ("nvfp4", 6, 1408),
+                                      ("mxfp4", 4, 4096)])
 def test_single_token_fused_path_equals_stagewise(wfmt, k, f):
     """The single-token layer (fused down+combine) is bit-identical to
     route -> permute -> expert_ffn -> combine called one by one, for short
