@@ -22,11 +22,13 @@
 // segments, re-reading the weights per token.
 #include <algorithm>
 #include <map>
+#include <type_traits>
 #include <mutex>
 #include <tuple>
 
 #include "device.h"
 #include "internal.h"
+#include "route_dev.h"
 
 namespace moe {
 namespace {
@@ -504,39 +506,34 @@ __device__ __forceinline__ void t1_row_compute(const GateUpArgs& a, T1Row<WF, MA
   store_act<WF>(a.h, R.hidx, silu(gs) * us);  // every lane stores the same value
 }
 
-template <int WF, int MAXC>
-__global__ __launch_bounds__(256) void gemv_gate_up_t1_bal_kernel(GateUpArgs a) {
-  static_assert(is_fp4(WF), "4-bit weights only");
-  extern __shared__ __align__(16) char xs[];
-  const int lane = lane_id();
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int W = gridDim.x * 4;
-  const int nchunks = a.d / WT<WF>::CE;
-  const int nact = *a.num_active;  // at most k <= 64 slots for one token
-  const int N = nact * a.f;
-  if (N <= 0) return;  // uniform over the grid
-  int q = blockIdx.x * 4 + wave;
-  if (q >= N) q = N - 1;  // surplus waves (grid larger than the rows) redo the last row
-  const int sl = min(lane, nact - 1);
-  const int slot_e = a.slot_info[4 * sl + 0];
-  const int slot_r = a.slot_info[4 * sl + 1];
-
-  // the token's activations (T = 1: row 0 of x), 16 bytes per thread a step,
-  // loaded before the weights so that waiting for them does not wait for those
+// The token's activations (T = 1: row 0 of x) into LDS, 16 bytes per thread
+// a step.  Every thread of the block calls; the loads go out first.
+template <int MAXC>
+__device__ __forceinline__ void t1_x_to_lds(const void* x, char* xs, int nchunks) {
   u32x4 xv[MAXC];
 #pragma unroll
   for (int k = 0; k < MAXC; ++k) {
     const int p = min(k * 256 + (int)threadIdx.x, nchunks * 4 - 1);
-    xv[k] = ld16(reinterpret_cast<const char*>(a.x) + (size_t)p * 16);
+    xv[k] = ld16(reinterpret_cast<const char*>(x) + (size_t)p * 16);
   }
-  T1Row<WF, MAXC> A, B;
-  A.load(a, q, true, slot_e, slot_r, nchunks, lane);
 #pragma unroll
   for (int k = 0; k < MAXC; ++k) {
     const int p = min(k * 256 + (int)threadIdx.x, nchunks * 4 - 1);
     *reinterpret_cast<u32x4*>(xs + (p >> 2) * kXStride + 16 * (p & 3)) = xv[k];
   }
-  __syncthreads();
+}
+
+// The row loop of the balanced single-token kernels, after x is in LDS (and a
+// barrier): wave g of W takes rows g, g + W, ... of the nact * f rows.
+template <int WF, int MAXC>
+__device__ __forceinline__ void t1_bal_rows(const GateUpArgs& a, const char* xs, int nact, int slot_e,
+                                            int slot_r, int nchunks, int lane, int wave) {
+  const int W = gridDim.x * 4;
+  const int N = nact * a.f;
+  int q = blockIdx.x * 4 + wave;
+  if (q >= N) q = N - 1;  // surplus waves (grid larger than the rows) redo the last row
+  T1Row<WF, MAXC> A, B;
+  A.load(a, q, true, slot_e, slot_r, nchunks, lane);
   for (;;) {
     const bool lb = q + W < N;
     const int qb = lb ? q + W : q;
@@ -554,6 +551,62 @@ __global__ __launch_bounds__(256) void gemv_gate_up_t1_bal_kernel(GateUpArgs a) 
     if (!la) break;
     q = qa;
   }
+}
+
+template <int WF, int MAXC>
+__global__ __launch_bounds__(256) void gemv_gate_up_t1_bal_kernel(GateUpArgs a) {
+  static_assert(is_fp4(WF), "4-bit weights only");
+  extern __shared__ __align__(16) char xs[];
+  const int lane = lane_id();
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int nchunks = a.d / WT<WF>::CE;
+  const int nact = *a.num_active;  // at most k <= 64 slots for one token
+  if (nact * a.f <= 0) return;     // uniform over the grid
+  const int sl = min(lane, nact - 1);
+  const int slot_e = a.slot_info[4 * sl + 0];
+  const int slot_r = a.slot_info[4 * sl + 1];
+  t1_x_to_lds<MAXC>(a.x, xs, nchunks);
+  __syncthreads();
+  t1_bal_rows<WF, MAXC>(a, xs, nact, slot_e, slot_r, nchunks, lane, wave);
+}
+
+// Routing for the routed variant: the token's logits and the outputs of the
+// route and permute steps.
+struct T1RouteArgs {
+  const float* logits;
+  int E;
+  int* topk_idx;
+  float* topk_w;
+  Plan plan;
+};
+
+// gemv_gate_up_t1_bal_kernel with the routing step folded in, for one token:
+// wave 0 of every block routes the token (the same selection and weights as
+// the routing kernels) while the other waves stage x, and block 0 also writes
+// the routing outputs and the whole plan for the kernels after it.  This
+// saves a kernel launch, which costs more than the routing itself.
+template <int WF, int MAXC, int VPL>
+__global__ __launch_bounds__(256) void gemv_gate_up_t1_routed_kernel(GateUpArgs a, T1RouteArgs r) {
+  static_assert(is_fp4(WF), "4-bit weights only");
+  extern __shared__ __align__(16) char xs[];
+  __shared__ int slot_expert[kWave];
+  const int lane = lane_id();
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int nchunks = a.d / WT<WF>::CE;
+  const int k = a.k;
+  if (wave == 0) {
+    int sel_i;
+    float sel_w;
+    route_token<VPL>(r.logits, r.E, k, sel_i, sel_w);
+    const int rank = selected_rank(sel_i, k);
+    if (lane < k) slot_expert[rank] = sel_i;
+    if (blockIdx.x == 0) write_plan_t1(sel_i, sel_w, rank, r.E, k, r.topk_idx, r.topk_w, r.plan);
+  }
+  t1_x_to_lds<MAXC>(a.x, xs, nchunks);
+  __syncthreads();
+  // slot s (rank s) holds the s-th smallest selected expert and row s
+  const int sl = min(lane, k - 1);
+  t1_bal_rows<WF, MAXC>(a, xs, k, slot_expert[sl], sl, nchunks, lane, wave);
 }
 
 struct DownArgs {
@@ -887,6 +940,51 @@ hipError_t launch_gemv_gate_up(const Dims& dm, const void* x, const Plan& p, con
   const dim3 grid((unsigned)(max_active * ((dm.f + 4 * rpw - 1) / (4 * rpw)))), block(256);
   MOE_WF_SWITCH(dm.wfmt, MOE_MAXC_SWITCH(WF, maxc, MOE_SEG_SWITCH(multi, (
       gemv_gate_up_kernel<WF, MC, rpw_for(MC), 1, MS><<<grid, block, 0, s>>>(a)))));
+  return hipGetLastError();
+}
+
+bool gemv_gate_up_t1_routed_ok(const Dims& dm) {
+  const int nchunks = dm.d / chunk_elems(dm.wfmt);
+  return dm.T == 1 && is_fp4(dm.wfmt) && nchunks <= 4 * kWave && dm.d % 128 == 0 && dm.k <= kWave &&
+         dm.E <= 16 * kWave;
+}
+
+hipError_t launch_gemv_gate_up_t1_routed(const Dims& dm, const float* logits, const void* x,
+                                         const Plan& p, const Weights& w, void* h, int* topk_idx,
+                                         float* topk_w, hipStream_t s) {
+  LaunchTimer tm("gemv_gate_up", s);
+  GateUpArgs a{x, w.wg, w.wu, w.sg, w.su, w.tg, w.tu, p.sorted_src, p.slot_info, p.num_active,
+               h, dm.d, dm.f, dm.k};
+  const T1RouteArgs r{logits, dm.E, topk_idx, topk_w, p};
+  const int nchunks = dm.d / chunk_elems(dm.wfmt);
+  const int maxc = pick_maxc(nchunks, dm.wfmt);
+  const size_t lds = (size_t)nchunks * kXStride;
+  const long long rows = (long long)dm.k * dm.f;
+  auto go = [&](auto kern) {
+    const long long g = std::min<long long>(resident_blocks((const void*)kern, 256, lds), (rows + 3) / 4);
+    kern<<<dim3((unsigned)std::max<long long>(g, 1)), dim3(256), lds, s>>>(a, r);
+  };
+  // logits per lane: E <= 64 * VPL
+  auto by_vpl = [&](auto wf, auto mc) {
+    constexpr int WF = decltype(wf)::value, MC = decltype(mc)::value;
+    if (dm.E <= 64) go(gemv_gate_up_t1_routed_kernel<WF, MC, 1>);
+    else if (dm.E <= 128) go(gemv_gate_up_t1_routed_kernel<WF, MC, 2>);
+    else if (dm.E <= 256) go(gemv_gate_up_t1_routed_kernel<WF, MC, 4>);
+    else if (dm.E <= 512) go(gemv_gate_up_t1_routed_kernel<WF, MC, 8>);
+    else go(gemv_gate_up_t1_routed_kernel<WF, MC, 16>);
+  };
+  auto by_maxc = [&](auto wf) {
+    switch (maxc) {
+      case 1: by_vpl(wf, std::integral_constant<int, 1>{}); break;
+      case 2: by_vpl(wf, std::integral_constant<int, 2>{}); break;
+      case 3: by_vpl(wf, std::integral_constant<int, 3>{}); break;
+      default: by_vpl(wf, std::integral_constant<int, 4>{}); break;
+    }
+  };
+  if (dm.wfmt == kMXFP4)
+    by_maxc(std::integral_constant<int, kMXFP4>{});
+  else
+    by_maxc(std::integral_constant<int, kNVFP4>{});
   return hipGetLastError();
 }
 

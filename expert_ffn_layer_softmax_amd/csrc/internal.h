@@ -95,6 +95,12 @@ hipError_t launch_gemv_gate_up(const Dims& dm, const void* x, const Plan& p, con
                                void* h, hipStream_t s);
 hipError_t launch_gemv_down(const Dims& dm, const void* h, const Plan& p, const Weights& w,
                             float* y_sorted, hipStream_t s);
+// T == 1 with 4-bit weights: routing (as launch_route_plan_t1, whose outputs
+// and plan it writes) folded into the gate/up GEMV, saving a launch.
+bool gemv_gate_up_t1_routed_ok(const Dims& dm);
+hipError_t launch_gemv_gate_up_t1_routed(const Dims& dm, const float* logits, const void* x,
+                                         const Plan& p, const Weights& w, void* h, int* topk_idx,
+                                         float* topk_w, hipStream_t s);
 // T == 1 (k <= 16, one segment per row): down projection and weighted
 // combine in one kernel, writing `out` directly.
 bool gemv_down_combine_t1_ok(const Dims& dm);

@@ -160,50 +160,14 @@ __global__ __launch_bounds__(kPermThreads) void route_permute_small_kernel(
 }
 
 // Single-token layers: one wave routes the token and writes the whole plan.
-// The k selected experts are distinct, so pair j's sorted position is the
-// number of selected experts below its own.
 template <int VPL>
 __global__ __launch_bounds__(64) void route_plan_t1_kernel(const float* __restrict__ logits, int E,
                                                            int k, int* __restrict__ topk_idx,
                                                            float* __restrict__ topk_w, Plan p) {
-  const int lane = lane_id();
   int sel_i;
   float sel_w;
   route_token<VPL>(logits, E, k, sel_i, sel_w);
-  int rank = 0;
-  for (int j = 0; j < k; ++j) rank += (__builtin_amdgcn_readlane(sel_i, j) < sel_i) ? 1 : 0;
-  if (lane < k) {
-    topk_idx[lane] = sel_i;
-    topk_w[lane] = sel_w;
-    p.sorted_src[rank] = lane;
-    p.dest_row[lane] = rank;
-    p.active[rank] = sel_i;
-    p.slot_info[4 * rank + 0] = sel_i;
-    p.slot_info[4 * rank + 1] = rank;
-    p.slot_info[4 * rank + 2] = 1;
-    p.slot_info[4 * rank + 3] = 0;
-    int* m = p.mtiles + kMtileInts * rank;
-    m[0] = sel_i;
-    m[1] = rank;
-    m[2] = 1;
-    m[3] = rank;
-    m[4] = 1;
-  }
-  for (int e = lane; e < E; e += kWave) {
-    int c = 0, below = 0;
-    for (int j = 0; j < k; ++j) {
-      const int o = __builtin_amdgcn_readlane(sel_i, j);
-      c += (o == e) ? 1 : 0;
-      below += (o < e) ? 1 : 0;
-    }
-    p.counts[e] = c;
-    p.offsets[e] = below;
-  }
-  if (lane == 0) {
-    p.offsets[E] = k;
-    *p.num_active = k;
-    *p.num_mtiles = k;
-  }
+  write_plan_t1(sel_i, sel_w, selected_rank(sel_i, k), E, k, topk_idx, topk_w, p);
 }
 
 }  // namespace

@@ -54,12 +54,12 @@ __device__ __forceinline__ void route_token(const float* __restrict__ row, int E
   const int lane = lane_id();
   float v[VPL];
   uint32_t key[VPL];
+  // all loads first, from clamped (in-row) positions: a load under a
+  // condition would be waited for before the next one is issued
 #pragma unroll
-  for (int i = 0; i < VPL; ++i) {
-    const int e = lane * VPL + i;
-    v[i] = (e < E) ? row[e] : 0.f;
-    key[i] = (e < E) ? route_key(v[i]) : 0u;
-  }
+  for (int i = 0; i < VPL; ++i) v[i] = row[min(lane * VPL + i, E - 1)];
+#pragma unroll
+  for (int i = 0; i < VPL; ++i) key[i] = (lane * VPL + i < E) ? route_key(v[i]) : 0u;
   float sel_v = 0.f;
   sel_i = 0;
   for (int j = 0; j < k; ++j) {
@@ -94,6 +94,55 @@ __device__ __forceinline__ void route_token(const float* __restrict__ row, int E
   if (lane < k) ex = (sel_v == l0) ? 1.0f : expf(sel_v - l0);
   const float sum = wave_sum(ex);
   sel_w = ex / sum;
+}
+
+// Lane j < k holding selected expert sel_i (the k are distinct): the number
+// of selected experts below it, i.e. slot j's position in expert order.
+__device__ __forceinline__ int selected_rank(int sel_i, int k) {
+  int rank = 0;
+  for (int j = 0; j < k; ++j) rank += (__builtin_amdgcn_readlane(sel_i, j) < sel_i) ? 1 : 0;
+  return rank;
+}
+
+// The whole permutation plan of a single-token layer from one wave's routing
+// (lane j < k: slot j's expert, weight and rank): every active expert has one
+// row, at the position of its rank.  Every lane of the wave must call.
+__device__ __forceinline__ void write_plan_t1(int sel_i, float sel_w, int rank, int E, int k,
+                                              int* __restrict__ topk_idx, float* __restrict__ topk_w,
+                                              const Plan& p) {
+  const int lane = lane_id();
+  if (lane < k) {
+    topk_idx[lane] = sel_i;
+    topk_w[lane] = sel_w;
+    p.sorted_src[rank] = lane;
+    p.dest_row[lane] = rank;
+    p.active[rank] = sel_i;
+    p.slot_info[4 * rank + 0] = sel_i;
+    p.slot_info[4 * rank + 1] = rank;
+    p.slot_info[4 * rank + 2] = 1;
+    p.slot_info[4 * rank + 3] = 0;
+    int* m = p.mtiles + kMtileInts * rank;
+    m[0] = sel_i;
+    m[1] = rank;
+    m[2] = 1;
+    m[3] = rank;
+    m[4] = 1;
+  }
+  for (int e = lane; e < E; e += kWave) {
+    int c = 0, below = 0;
+    for (int j = 0; j < k; ++j) {
+      const int o = __builtin_amdgcn_readlane(sel_i, j);
+      c += (o == e) ? 1 : 0;
+      below += (o < e) ? 1 : 0;
+    }
+    p.counts[e] = c;
+    p.offsets[e] = below;
+  }
+  if (lane == 0) {
+    p.offsets[E] = k;
+    *p.num_active = k;
+    *p.num_mtiles = k;
+  }
 }
 
 }  // namespace moe
