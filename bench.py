@@ -85,7 +85,8 @@ def _source_digest(files) -> str:
 # counters recorded under profiles/).
 DOMINANT = {
     "decode": ("gemv_gate_up", ["expert_ffn_layer_softmax_amd/csrc/gemv.hip",
-                                "expert_ffn_layer_softmax_amd/csrc/device.h"]),
+                                "expert_ffn_layer_softmax_amd/csrc/device.h",
+                                "expert_ffn_layer_softmax_amd/csrc/route_dev.h"]),
     "prefill": ("gg_gate_up", ["expert_ffn_layer_softmax_amd/csrc/grouped_gemm.hip",
                                "expert_ffn_layer_softmax_amd/csrc/device.h"]),
 }
