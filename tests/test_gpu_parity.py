@@ -108,6 +108,10 @@ SMALL = [
     ("mx_t1_k64", 1, 256, 64, 64, 128, "bf16", "mxfp4"),
     ("mx_t1_bigd", 1, 8192, 8, 2, 256, "bf16", "mxfp4"),
     ("nv_t1_bigd", 1, 8192, 8, 3, 384, "bf16", "nvfp4"),
+    # routing inside the single-token gate/up kernel at 2, 8 and 16 logits per lane
+    ("mx_t1_e128", 1, 256, 128, 8, 128, "bf16", "mxfp4"),
+    ("nv_t1_e512", 1, 256, 512, 4, 128, "bf16", "nvfp4"),
+    ("mx_t1_e1024", 1, 256, 1024, 16, 256, "bf16", "mxfp4"),
     ("bf16_t1_bigf", 1, 64, 4, 2, 16384, "bf16", "bf16"),
     ("bf16_t47", 47, 320, 16, 4, 192, "bf16", "bf16"),          # largest T on the GEMV path
     ("bf16_longrow_t2", 2, 3584, 8, 2, 96, "bf16", "bf16"),      # rows in quarters, 2 chunks/lane
