@@ -834,30 +834,50 @@ __global__ __launch_bounds__(kThreads) void gg_mx_group_kernel(GGArgs a) {
   issue_a(0);
   issue_a(1);
 
+  // Groups run three to a loop turn, so group g's buffer (g % 3) and step
+  // kk's activation stage (kk % 3 = (g + p) % 3, as 4 = 1 mod 3) are
+  // compile-time: every LDS fragment address is then a loop-invariant register
+  // plus an immediate offset, instead of two adds per fragment per step.
   auto main_loop = [&](auto vm_c) {
     constexpr int VM = decltype(vm_c)::value;
-    for (int g = 0; g < ng; ++g) {
-      const char* cb = lds_c + (g % kGroupBufs) * kCodesGroup;
-      const char* sb = lds_s + (g % kGroupBufs) * GS::kBytes;
-#pragma unroll
-      for (int p = 0; p < kGroupSteps; ++p) {
+    auto group = [&](int g, auto j_c) {
+      constexpr int J = decltype(j_c)::value;  // g % 3
+      const char* cb = lds_c + J * kCodesGroup;
+      const char* sb = lds_s + J * GS::kBytes;
+      auto step = [&](auto p_c) {
+        constexpr int p = decltype(p_c)::value;
         const int kk = kGroupSteps * g + p;
         // loads younger than activation stage kk: those of step kk-1 (three,
         // three plus the scale DMAs after a group's first step); at step 0
         // only stage 1's two
-        if (p == 1)
+        if constexpr (p == 1)
           wait_and_barrier<3 + GS::kDmas>();
-        else if (p == 0)
+        else if constexpr (p == 0)
           wait_and_barrier<2>();
         else
           wait_and_barrier<3>();
         issue_codes(g + 2, p);
-        if (p == 0) issue_scales(g + 2);
+        if constexpr (p == 0) issue_scales(g + 2);
         asm volatile("" ::: "memory");  // activation DMAs are the step's youngest loads
         issue_a(kk + 2);
-        mx4_step<WF, VM>(lds_a + (kk % kMx4A) * kStageA, cb, sb, p, aoff, brow, half, acc);
-      }
+        mx4_step<WF, VM>(lds_a + ((J + p) % kMx4A) * kStageA, cb, sb, p, aoff, brow, half, acc);
+      };
+      step(std::integral_constant<int, 0>{});
+      step(std::integral_constant<int, 1>{});
+      step(std::integral_constant<int, 2>{});
+      step(std::integral_constant<int, 3>{});
+    };
+    using I0 = std::integral_constant<int, 0>;
+    using I1 = std::integral_constant<int, 1>;
+    using I2 = std::integral_constant<int, 2>;
+    int g = 0;
+    for (; g + 3 <= ng; g += 3) {
+      group(g, I0{});
+      group(g + 1, I1{});
+      group(g + 2, I2{});
     }
+    if (g < ng) group(g, I0{});
+    if (g + 1 < ng) group(g + 1, I1{});
   };
   if (vm == 2)
     main_loop(std::integral_constant<int, 2>{});
