@@ -204,19 +204,23 @@ def test_determinism_and_t0():
     assert r["out"].shape == (0, 256)
 
 
-@pytest.mark.parametrize("wfmt,k,f", [("bf16", 8, 352), ("mxfp4", 8, 352), ("nvfp4", 8, 352), ("f32", 4, 352),
-                                      ("bf16", 16, 352), ("bf16", 8, 2816), ("f32", 4, 1024),
-                                      ("bf16", 12, 2048), ("mxfp4", 8, 2816), ("nvfp4", 6, 1408),
-                                      ("mxfp4", 4, 4096)])
-def test_single_token_fused_path_equals_stagewise(wfmt, k, f):
+@pytest.mark.parametrize("wfmt,k,f,d", [("bf16", 8, 352, 1024), ("mxfp4", 8, 352, 1024), ("nvfp4", 8, 352, 1024),
+                                        ("f32", 4, 352, 1024), ("bf16", 16, 352, 1024), ("bf16", 8, 2816, 1024),
+                                        ("f32", 4, 1024, 1024), ("bf16", 12, 2048, 1024),
+                                        ("mxfp4", 8, 2816, 1024), ("nvfp4", 6, 1408, 1024),
+                                        ("mxfp4", 4, 4096, 1024),
+                                        # bf16 rows split four ways, routing inside the gate/up kernel
+                                        ("bf16", 8, 704, 4096), ("bf16", 16, 352, 6144),
+                                        ("bf16", 3, 128, 3104)])
+def test_single_token_fused_path_equals_stagewise(wfmt, k, f, d):
     """The single-token layer (fused down+combine) is bit-identical to
     route -> permute -> expert_ffn -> combine called one by one, for short
     and full-width down rows and for k up to 16."""
     from expert_ffn_layer_softmax_amd import (moe_combine, moe_expert_ffn, moe_layer_forward,
                                               moe_permute, moe_route)
     act = "f32" if wfmt == "f32" else "bf16"
-    wl = Workload("t1eq", T=1, d=1024, E=32, k=k, f=f, act=act, wfmt=wfmt, seed=31 + k,
-                  x_std=1.0, wg_std=1024 ** -0.5, wu_std=1024 ** -0.5, wd_std=f ** -0.5)
+    wl = Workload("t1eq", T=1, d=d, E=32, k=k, f=f, act=act, wfmt=wfmt, seed=31 + k,
+                  x_std=1.0, wg_std=d ** -0.5, wu_std=d ** -0.5, wd_std=f ** -0.5)
     x, w, _, logits = make_inputs(wl)
     fused = moe_layer_forward(x, w, k, logits=logits)["out"]
     idx, tw = moe_route(logits, k)
