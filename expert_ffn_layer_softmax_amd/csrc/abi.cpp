@@ -281,9 +281,10 @@ moe_status_t moe_layer_forward(const moe_dims_t* dims, const void* x, const void
 
   hipError_t e = hipSuccess;
   if (w_router) e = launch_router_logits(x, w_router, logits, dm.T, dm.d, dm.E, dm.act, s);
-  if (!dm.fp8 && !dm.expert_norm && gemv_down_combine_t1_ok(dm)) {
+  if (!dm.fp8 && gemv_down_combine_t1_ok(dm)) {
     // single token: one-wave route+plan, gate/up GEMV (4-bit: one kernel for
-    // both), down GEMV + combine
+    // both), down GEMV + combine (fused unless the expert outputs are
+    // normalised first)
     if (gemv_gate_up_t1_routed_ok(dm)) {
       if (e == hipSuccess)
         e = launch_gemv_gate_up_t1_routed(dm, logits, x, p, w, h, topk_idx, topk_w, s);
@@ -291,8 +292,13 @@ moe_status_t moe_layer_forward(const moe_dims_t* dims, const void* x, const void
       if (e == hipSuccess) e = launch_route_plan_t1(logits, dm.E, dm.k, topk_idx, topk_w, p, s);
       if (e == hipSuccess) e = launch_gemv_gate_up(dm, x, p, w, h, s);
     }
-    if (e == hipSuccess)
-      e = launch_gemv_down_combine_t1(dm, h, p, topk_idx, topk_w, w, out, s);
+    if (!dm.expert_norm) {
+      if (e == hipSuccess)
+        e = launch_gemv_down_combine_t1(dm, h, p, topk_idx, topk_w, w, out, s);
+    } else {
+      if (e == hipSuccess) e = launch_gemv_down(dm, h, p, w, y_sorted, s);
+      if (e == hipSuccess) e = launch_combine(dm, y_sorted, p.dest_row, topk_w, out, s);
+    }
     return device_status(e);
   }
   if (dm.T <= kDecodeMaxT) {

@@ -271,6 +271,8 @@ NORM_CASES = [
     # name, T, d, E, k, f, act, wfmt, fp8
     ("norm_t1_bf16", 1, 512, 32, 8, 160, "bf16", "bf16", False),
     ("norm_t1_f32", 1, 128, 8, 3, 64, "f32", "f32", False),
+    ("norm_t1_mx", 1, 512, 32, 8, 256, "bf16", "mxfp4", False),          # routing inside gate/up
+    ("norm_t1_bf16_long", 1, 4096, 16, 4, 256, "bf16", "bf16", False),   # rows split four ways
     ("norm_t16_mx", 16, 512, 32, 8, 256, "bf16", "mxfp4", False),
     ("norm_t40_nv", 40, 256, 8, 2, 128, "bf16", "nvfp4", False),
     ("norm_gg_bf16", 300, 512, 16, 4, 384, "bf16", "bf16", False),
