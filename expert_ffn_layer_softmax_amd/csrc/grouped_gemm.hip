@@ -28,6 +28,9 @@
 // converted to bf16 in registers by the gfx950 scaled convert (block scale
 // applied by the instruction) just before their MFMAs.
 //
+// gg_mx_row_kernel (NVFP4 weights, K % 256 == 0): the same loads, with the
+// eight waves side by side, each owning all 128 rows and 32 weight rows.
+//
 // gg_direct_b_kernel (MX-FP4 weights, other K): each wave owns all 128 rows
 // and two 32-column weight operands that stream from memory into a register
 // ring; the activation rows go through a register ring into double-buffered
@@ -926,6 +929,272 @@ __global__ __launch_bounds__(kThreads) void gg_mx_group_kernel(GGArgs a) {
   }
 }
 
+// MFMAs of one K-step for a wave owning all VM valid row sub-tiles and one
+// 32-column weight operand (gg_mx_row_kernel): the operand is converted once
+// per substep and feeds VM MFMAs.
+template <int WF, int VM>
+__device__ __forceinline__ void mx4_row_step(const char* st, const char* cb, const char* sb, int p,
+                                             const int* aoff, int brow, int half, f32x16_t (&acc)[4]) {
+  Fp4Regs b;
+  const int u = 2 * p + half;  // the lane's 32-element block inside the line
+  b.v[0] = *reinterpret_cast<const u32x4*>(cb + brow * 128 + ((u ^ (brow & 7)) << 4));
+  if constexpr (WF == kNVFP4) {
+    const uint8_t* q = reinterpret_cast<const uint8_t*>(sb) + brow * 16 + 2 * u;
+    b.lo[0] = e4m3_to_f32(q[0]);
+    b.hi[0] = e4m3_to_f32(q[1]);
+  } else {
+    b.lo[0] = b.hi[0] = e8m0_cvt_scale(static_cast<uint8_t>(sb[brow * 8 + u]));
+  }
+  bf16x8_t af[2][VM];
+#pragma unroll
+  for (int mi = 0; mi < VM; ++mi) af[0][mi] = *reinterpret_cast<const bf16x8_t*>(st + aoff[4 * mi]);
+#pragma unroll
+  for (int s = 0; s < 4; ++s) {
+    if (s + 1 < 4) {
+#pragma unroll
+      for (int mi = 0; mi < VM; ++mi)
+        af[(s + 1) & 1][mi] = *reinterpret_cast<const bf16x8_t*>(st + aoff[4 * mi + s + 1]);
+    }
+    const bf16x8_t bb = fp4_frag<WF>(b, 0, s);
+#pragma unroll
+    for (int mi = 0; mi < VM; ++mi)
+      acc[mi] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[s & 1][mi], bb, acc[mi], 0, 0, 0);
+  }
+}
+
+// gg_mx_group_kernel with the eight waves side by side (1 x 8): each wave
+// owns all 128 rows of the tile and 32 of its 256 weight rows.  Every wave
+// then works on every tile whatever its fill (with the 2 x 4 grid the lower
+// half of the waves idles on tiles of up to 64 rows, leaving one working wave
+// per SIMD), and each weight operand is converted once instead of by two
+// waves; the activation fragments are read from LDS twice as often.  Loads,
+// waits and LDS layout are gg_mx_group_kernel's.  Used for NVFP4, whose
+// conversion (E2M1 x E4M3 formed in fp32) costs four instructions per code
+// pair: prefill 5.88 -> 5.34 ms.  For MX-FP4 (one convert per pair) the extra
+// activation reads cost more than the halved conversions save (gate/up 2.65
+// -> 2.84 ms), so it keeps the 2 x 4 grid.
+template <int WF, bool GATEUP>
+__global__ __launch_bounds__(kThreads) void gg_mx_row_kernel(GGArgs a) {
+  using GS = GroupScales<WF>;
+  __shared__ __align__(1024) char lds[GS::kLds];
+  char* const lds_a = lds;
+  char* const lds_c = lds + kMx4A * kStageA;
+  char* const lds_s = lds_c + kGroupBufs * kCodesGroup;
+  const int tid = threadIdx.x;
+  const int lane = lane_id();
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int half = lane >> 5;
+  const int cl = lane & 31;
+
+  // ---- tile (as in the other kernels)
+  const int num_tiles = *a.num_mtiles * a.ntiles;
+  const int per_xcd = (num_tiles + kXcds - 1) / kXcds;
+  const int slot = blockIdx.x / kXcds;
+  if (slot >= per_xcd) return;
+  const int L = (blockIdx.x % kXcds) * per_xcd + slot;
+  if (L >= num_tiles) return;
+  const int* eq = a.mtiles + kMtileInts * (L / a.ntiles);
+  const int e = eq[0];
+  const int first_mt = eq[3];
+  const int nmt = eq[4];
+  const int local = L - first_mt * a.ntiles;
+  const int ntile = local / nmt;
+  const int* em = a.mtiles + kMtileInts * (first_mt + (local - ntile * nmt));
+  const int row0 = em[1];
+  const int nrows = em[2];
+  const int nbase = ntile * (GATEUP ? BN / 2 : BN);
+
+  // weight row r of the tile (0..255) -> its codes and scales
+  auto wrow = [&](int r, const char*& code, const uint8_t*& scale) {
+    const void* w = a.w0;
+    const uint8_t* sc = a.s0;
+    int col;
+    if (GATEUP) {
+      const bool up = r >= BN / 2;
+      w = up ? a.w1 : a.w0;
+      sc = up ? a.s1 : a.s0;
+      col = nbase + (up ? r - BN / 2 : r);
+    } else {
+      col = nbase + r;
+    }
+    col = min(col, a.N - 1);
+    code = reinterpret_cast<const char*>(w) + ((size_t)e * a.N + col) * (a.K / 2);
+    scale = sc + ((size_t)e * a.N + col) * ((size_t)a.K / 256 * GS::kBytesPerRow);
+  };
+
+  // ---- activation DMA sources (see gg_dma_kernel)
+  const size_t rb = (size_t)a.K * 2;
+  const int slot16 = lane & 7;
+  const char* asrc[kDmaA];
+#pragma unroll
+  for (int j = 0; j < kDmaA; ++j) {
+    const int r = (kDmaA * 8) * wave + 8 * j + (lane >> 3);
+    const int f = (r & 7) ^ ((r >> 3) & 1);
+    const int src = row0 + min(r, nrows - 1);
+    asrc[j] = reinterpret_cast<const char*>(a.a_src) +
+              (GATEUP ? (size_t)(a.sorted_src[src] / a.k) : (size_t)src) * rb + ((slot16 ^ f) << 4);
+  }
+  char* const adst = lds_a + (kDmaA * 8) * wave * (BK * 2);
+
+  // ---- code DMA sources: at group place p, wave w fills weight rows
+  // 32 w + 8 p + lane/8, line slot lane%8 <- global unit (lane%8) ^ (row & 7)
+  const char* csrc[kGroupSteps];
+#pragma unroll
+  for (int p = 0; p < kGroupSteps; ++p) {
+    const int r = 32 * wave + 8 * p + (lane >> 3);
+    const char* code;
+    const uint8_t* scale;
+    wrow(r, code, scale);
+    csrc[p] = code + ((slot16 ^ (r & 7)) << 4);
+  }
+  // ---- scale DMA sources: dword d = 64 (kDmas w + i) + lane of the group
+  // covers weight row d / W, bytes 4 (d % W) .. +3 of the row's group bytes
+  // (W = words per row)
+  constexpr int W = GS::kBytesPerRow / 4;
+  const uint8_t* ssrc[GS::kDmas];
+#pragma unroll
+  for (int i = 0; i < GS::kDmas; ++i) {
+    const int d = kWave * (GS::kDmas * wave + i) + lane;
+    const char* code;
+    wrow(d / W, code, ssrc[i]);
+    ssrc[i] += 4 * (d % W);
+  }
+  const int nk = a.K / BK;
+  const int ng = nk / kGroupSteps;
+
+  // Loads for group g / step kk go to that group's / step's buffer; past the
+  // end they re-read the last group or step, still into the buffer that is
+  // free at that point.
+  auto issue_codes = [&](int g, int p) {  // part p of group g
+    char* d = lds_c + (g % kGroupBufs) * kCodesGroup + (32 * wave + 8 * p) * 128;
+    dma16<0>(csrc[p] + (size_t)min(g, ng - 1) * 128, d);
+  };
+  auto issue_scales = [&](int g) {
+    char* d = lds_s + (g % kGroupBufs) * GS::kBytes + GS::kDmas * wave * kWave * 4;
+    const size_t go = (size_t)min(g, ng - 1) * GS::kBytesPerRow;
+#pragma unroll
+    for (int i = 0; i < GS::kDmas; ++i)
+      __builtin_amdgcn_global_load_lds(ssrc[i] + go, (lds_void_t*)(d + i * kWave * 4), 4, 0, 0);
+  };
+  auto issue_a = [&](int kk) {
+    char* d = adst + (kk % kMx4A) * kStageA;
+    const size_t go = (size_t)min(kk, nk - 1) * (BK * 2);
+#pragma unroll
+    for (int j = 0; j < kDmaA; ++j) dma16<kAuxA>(asrc[j] + go, d + j * 8 * (BK * 2));
+  };
+
+  // ---- fragment offsets: all four 32-row sub-tiles, one 32-column weight
+  // operand (gate/up: 16 columns of W_gate and the same 16 of W_up)
+  int aoff[16];
+#pragma unroll
+  for (int mi = 0; mi < 4; ++mi)
+#pragma unroll
+    for (int s = 0; s < 4; ++s) aoff[4 * mi + s] = t_off(32 * mi + cl, half * 4 + s);
+  const int brow = GATEUP ? (cl < 16 ? 16 * wave + cl : BN / 2 + 16 * wave + (cl - 16)) : 32 * wave + cl;
+
+  f32x16_t acc[4];
+#pragma unroll
+  for (int mi = 0; mi < 4; ++mi) acc[mi] = f32x16_t{};
+
+  const int vm = min((nrows + 31) / 32, 4);
+
+  // ---- prologue: groups 0 and 1, then activation steps 0 and 1 (youngest)
+#pragma unroll
+  for (int g = 0; g < 2; ++g) {
+#pragma unroll
+    for (int p = 0; p < kGroupSteps; ++p) issue_codes(g, p);
+    issue_scales(g);
+  }
+  asm volatile("" ::: "memory");  // activation DMAs are the youngest loads
+  issue_a(0);
+  issue_a(1);
+
+  // Groups run three to a loop turn, so group g's buffer (g % 3) and step
+  // kk's activation stage (kk % 3 = (g + p) % 3, as 4 = 1 mod 3) are
+  // compile-time: every LDS fragment address is then a loop-invariant register
+  // plus an immediate offset, instead of two adds per fragment per step.
+  auto main_loop = [&](auto vm_c) {
+    constexpr int VM = decltype(vm_c)::value;
+    auto group = [&](int g, auto j_c) {
+      constexpr int J = decltype(j_c)::value;  // g % 3
+      const char* cb = lds_c + J * kCodesGroup;
+      const char* sb = lds_s + J * GS::kBytes;
+      auto step = [&](auto p_c) {
+        constexpr int p = decltype(p_c)::value;
+        const int kk = kGroupSteps * g + p;
+        // loads younger than activation stage kk: those of step kk-1 (three,
+        // three plus the scale DMAs after a group's first step); at step 0
+        // only stage 1's two
+        if constexpr (p == 1)
+          wait_and_barrier<3 + GS::kDmas>();
+        else if constexpr (p == 0)
+          wait_and_barrier<2>();
+        else
+          wait_and_barrier<3>();
+        issue_codes(g + 2, p);
+        if constexpr (p == 0) issue_scales(g + 2);
+        asm volatile("" ::: "memory");  // activation DMAs are the step's youngest loads
+        issue_a(kk + 2);
+        mx4_row_step<WF, VM>(lds_a + ((J + p) % kMx4A) * kStageA, cb, sb, p, aoff, brow, half, acc);
+      };
+      step(std::integral_constant<int, 0>{});
+      step(std::integral_constant<int, 1>{});
+      step(std::integral_constant<int, 2>{});
+      step(std::integral_constant<int, 3>{});
+    };
+    using I0 = std::integral_constant<int, 0>;
+    using I1 = std::integral_constant<int, 1>;
+    using I2 = std::integral_constant<int, 2>;
+    int g = 0;
+    for (; g + 3 <= ng; g += 3) {
+      group(g, I0{});
+      group(g + 1, I1{});
+      group(g + 2, I2{});
+    }
+    if (g < ng) group(g, I0{});
+    if (g + 1 < ng) group(g + 1, I1{});
+  };
+  if (vm == 4)
+    main_loop(std::integral_constant<int, 4>{});
+  else if (vm == 3)
+    main_loop(std::integral_constant<int, 3>{});
+  else if (vm == 2)
+    main_loop(std::integral_constant<int, 2>{});
+  else
+    main_loop(std::integral_constant<int, 1>{});
+  // the clamped loads past the end must land before the block's LDS is released
+  __builtin_amdgcn_s_waitcnt(0);
+
+  // ---- epilogue (C layout of a 32x32 MFMA: lane holds column lane%32 and
+  // rows 8*(i/4) + 4*(lane/32) + i%4).  Gate/up: lanes with column < 16 hold
+  // W_gate, the lane 16 above holds W_up of the same output column.
+  if constexpr (WF == kNVFP4) {
+    const float t = (GATEUP && cl >= 16) ? a.t1[e] : a.t0[e];
+#pragma unroll
+    for (int mi = 0; mi < 4; ++mi) acc[mi] *= t;
+  }
+#pragma unroll
+  for (int mi = 0; mi < 4; ++mi) {
+    if (mi < vm) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int row = 32 * mi + 8 * (i >> 2) + 4 * half + (i & 3);
+        const float v = acc[mi][i];
+        if (GATEUP) {
+          const float u = __shfl_xor(v, 16, kWave);  // every lane takes part
+          const int col = nbase + 16 * wave + cl;
+          if (cl < 16 && row < nrows && col < a.N)
+            reinterpret_cast<uint16_t*>(a.out)[(size_t)(row0 + row) * a.N + col] =
+                f32_to_bf16(v / (1.0f + expf(-v)) * u);
+        } else {
+          const int col = nbase + 32 * wave + cl;
+          if (row < nrows && col < a.N) reinterpret_cast<float*>(a.out)[(size_t)(row0 + row) * a.N + col] = v;
+        }
+      }
+    }
+  }
+}
+
 // ---- FP8 activations x MX-FP4 weights on the scaled MFMA.
 //
 // The pages run the experts with FP8 compute and 4-bit weights
@@ -1268,7 +1537,7 @@ hipError_t launch_gg(const Dims& dm, const GGArgs& a, hipStream_t s) {
   const size_t max_tiles = grouped_gemm_max_mtiles(dm) * (size_t)a.ntiles;
   const dim3 grid((unsigned)((max_tiles + kXcds - 1) / kXcds * kXcds)), block(kThreads);
   if (dm.wfmt == kNVFP4)
-    gg_mx_group_kernel<kNVFP4, GATEUP><<<grid, block, 0, s>>>(a);
+    gg_mx_row_kernel<kNVFP4, GATEUP><<<grid, block, 0, s>>>(a);
   else if (dm.wfmt == kMXFP4 && mx_grouped(a.K))
     gg_mx_group_kernel<kMXFP4, GATEUP><<<grid, block, 0, s>>>(a);
   else if (dm.wfmt == kMXFP4)
