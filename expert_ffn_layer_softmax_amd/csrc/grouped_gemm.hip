@@ -41,7 +41,11 @@
 // by m-tile, and each XCD (blockIdx % 8 under round-robin dispatch) takes a
 // contiguous range.  The m-tiles of one (expert, n-tile) panel therefore run
 // together on one XCD and share the weight panel through its L2; the n-tiles
-// of one expert follow each other there and reuse its activation rows.
+// of one expert follow each other there and reuse its activation rows.  The
+// MX-FP4 group kernel and the FP8-by-FP4 kernel swap the inner two levels
+// (m-tile by m-tile, then n-tile): their weight panels are a quarter or half
+// the bytes of bf16 ones, and keeping one m-tile's activation rows hot was
+// measured faster there, while for bf16 weights it raised the fetched bytes.
 #include <type_traits>
 
 #include "device.h"
@@ -722,10 +726,13 @@ __global__ __launch_bounds__(kThreads) void gg_mx_group_kernel(GGArgs a) {
   const int* eq = a.mtiles + kMtileInts * (L / a.ntiles);
   const int e = eq[0];
   const int first_mt = eq[3];
-  const int nmt = eq[4];
   const int local = L - first_mt * a.ntiles;
-  const int ntile = local / nmt;
-  const int* em = a.mtiles + kMtileInts * (first_mt + (local - ntile * nmt));
+  // m-tile by m-tile within the expert: the n-tiles of one m-tile run
+  // back to back, so its activation rows stay in L2 (the packed weights
+  // are small enough that their re-reads cost less here)
+  const int mloc = local / a.ntiles;
+  const int ntile = local - mloc * a.ntiles;
+  const int* em = a.mtiles + kMtileInts * (first_mt + mloc);
   const int row0 = em[1];
   const int nrows = em[2];
   const int nbase = ntile * (GATEUP ? BN / 2 : BN);
@@ -1296,10 +1303,13 @@ __global__ __launch_bounds__(kThreads) void gg_f8f4_kernel(GGArgs a) {
   const int* eq = a.mtiles + kMtileInts * (L / a.ntiles);
   const int e = eq[0];
   const int first_mt = eq[3];
-  const int nmt = eq[4];
   const int local = L - first_mt * a.ntiles;
-  const int ntile = local / nmt;
-  const int* em = a.mtiles + kMtileInts * (first_mt + (local - ntile * nmt));
+  // m-tile by m-tile within the expert: the n-tiles of one m-tile run
+  // back to back, so its activation rows stay in L2 (the packed weights
+  // are small enough that their re-reads cost less here)
+  const int mloc = local / a.ntiles;
+  const int ntile = local - mloc * a.ntiles;
+  const int* em = a.mtiles + kMtileInts * (first_mt + mloc);
   const int row0 = em[1];
   const int nrows = em[2];
   const int nbase = ntile * (GATEUP ? BN / 2 : BN);
