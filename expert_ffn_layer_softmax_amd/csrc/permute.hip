@@ -52,8 +52,8 @@ __device__ void write_lists(int c, int first, int E, const Plan& p, int* tmp) {
   if (threadIdx.x == 0) *p.num_mtiles = total;
 }
 
-// Counting sort of N keys (key(q) in [0, E) after clamping) by one block of
-// kPermThreads threads.  Inside a wave, lanes with the same key are found by
+// Counting sort of N >= 1 keys (key(q) in [0, E) after clamping) by one
+// block of kPermThreads threads.  Inside a wave, lanes with the same key are found by
 // one ballot per key bit; across waves, by per-wave counts in LDS.
 template <typename KeyFn>
 __device__ void permute_block(KeyFn key, int N, int E, const Plan& p, bool with_lists,
@@ -68,9 +68,16 @@ __device__ void permute_block(KeyFn key, int N, int E, const Plan& p, bool with_
     for (int w = 0; w < kPermThreads / kWave; ++w) sh.wave_cnt[w][i] = 0;
   }
   __syncthreads();
-  for (int q = tid; q < N; q += kPermThreads) {
-    const int e = min(max(key(q), 0), E - 1);
-    atomicAdd(&sh.hist[e], 1);  // integer: order independent
+  // keys in batches of kKeyBatch per thread, all loads before the adds (a
+  // load-then-add loop waits out each load's latency in turn)
+  constexpr int kKeyBatch = 8;
+  for (int q0 = tid; q0 < N; q0 += kPermThreads * kKeyBatch) {
+    int ks[kKeyBatch];
+#pragma unroll
+    for (int u = 0; u < kKeyBatch; ++u) ks[u] = key(min(q0 + u * kPermThreads, N - 1));
+#pragma unroll
+    for (int u = 0; u < kKeyBatch; ++u)
+      if (q0 + u * kPermThreads < N) atomicAdd(&sh.hist[min(max(ks[u], 0), E - 1)], 1);  // integer: order independent
   }
   __syncthreads();
 
@@ -88,10 +95,13 @@ __device__ void permute_block(KeyFn key, int N, int E, const Plan& p, bool with_
 
   const int nbits = (E > 1) ? 32 - __clz(E - 1) : 0;
   const uint64_t lt_mask = (1ull << lane) - 1ull;
+  // each round's key is loaded one round ahead
+  int key_next = key(min(tid, N - 1));
   for (int base = 0; base < N; base += kPermThreads) {
     const int q = base + tid;
     const bool valid = q < N;
-    const int e = valid ? min(max(key(q), 0), E - 1) : 0;
+    const int e = valid ? min(max(key_next, 0), E - 1) : 0;
+    key_next = key(min(q + kPermThreads, N - 1));
     uint64_t peers = __ballot(valid);
     for (int b = 0; b < nbits; ++b) {
       const bool bit = (e >> b) & 1;
