@@ -17,9 +17,7 @@ constexpr int kPermThreads = 1024;  // 16 waves
 constexpr int kMaxE = 1024;
 
 struct PermShared {
-  int hist[kMaxE];
-  int cursor[kMaxE];
-  int wave_cnt[kPermThreads / kWave][kMaxE];
+  int wave_cnt[kPermThreads / kWave][kMaxE];  // per wave: counts, then cursors
   int tmp[32];
 };
 
@@ -53,41 +51,62 @@ __device__ void write_lists(int c, int first, int E, const Plan& p, int* tmp) {
 }
 
 // Counting sort of N >= 1 keys (key(q) in [0, E) after clamping) by one
-// block of kPermThreads threads.  Inside a wave, lanes with the same key are found by
-// one ballot per key bit; across waves, by per-wave counts in LDS.
+// block of kPermThreads threads.  Wave w owns the contiguous chunk of keys
+// [w C, (w + 1) C) (C a multiple of 64): it counts its chunk per expert into
+// its own LDS row, the block turns the rows into each wave's first position
+// per expert (expert offset plus the counts of the waves before), and each
+// wave then walks its chunk 64 keys at a time, in order, with no block
+// barrier: lanes with the same key are found by one ballot per key bit, and
+// one lane per key advances the wave's cursor.  Positions therefore ascend
+// with the flat id within every expert (stable).
 template <typename KeyFn>
 __device__ void permute_block(KeyFn key, int N, int E, const Plan& p, bool with_lists,
                               PermShared& sh) {
+  constexpr int W = kPermThreads / kWave;
   const int tid = threadIdx.x;
   const int lane = lane_id();
   const int wave = tid >> 6;
+  const int C = ((N + W - 1) / W + kWave - 1) / kWave * kWave;
+  const int q0 = min(wave * C, N);
+  const int q1 = min(q0 + C, N);
 
   for (int i = tid; i < E; i += kPermThreads) {
-    sh.hist[i] = 0;
 #pragma unroll
-    for (int w = 0; w < kPermThreads / kWave; ++w) sh.wave_cnt[w][i] = 0;
+    for (int w = 0; w < W; ++w) sh.wave_cnt[w][i] = 0;
   }
   __syncthreads();
-  // keys in batches of kKeyBatch per thread, all loads before the adds (a
-  // load-then-add loop waits out each load's latency in turn)
-  constexpr int kKeyBatch = 8;
-  for (int q0 = tid; q0 < N; q0 += kPermThreads * kKeyBatch) {
+  // per-wave counts; keys in groups of kKeyBatch per lane, all loads before
+  // the adds (a load-then-add loop waits out each load's latency in turn)
+  constexpr int kKeyBatch = 32;
+  for (int b = q0; b < q1; b += kWave * kKeyBatch) {
     int ks[kKeyBatch];
 #pragma unroll
-    for (int u = 0; u < kKeyBatch; ++u) ks[u] = key(min(q0 + u * kPermThreads, N - 1));
+    for (int u = 0; u < kKeyBatch; ++u) ks[u] = key(min(b + u * kWave + lane, N - 1));
 #pragma unroll
-    for (int u = 0; u < kKeyBatch; ++u)
-      if (q0 + u * kPermThreads < N) atomicAdd(&sh.hist[min(max(ks[u], 0), E - 1)], 1);  // integer: order independent
+    for (int u = 0; u < kKeyBatch; ++u) {
+      if (b + u * kWave >= q1) break;  // wave-uniform
+      if (b + u * kWave + lane < q1) atomicAdd(&sh.wave_cnt[wave][min(max(ks[u], 0), E - 1)], 1);
+    }
   }
   __syncthreads();
 
-  const int c = tid < E ? sh.hist[tid] : 0;
+  int c = 0;
+  if (tid < E) {
+#pragma unroll
+    for (int w = 0; w < W; ++w) c += sh.wave_cnt[w][tid];
+  }
   int total = 0;
   const int excl = block_exclusive_scan(c, sh.tmp, &total);
   if (tid < E) {
     p.counts[tid] = c;
     p.offsets[tid] = excl;
-    sh.cursor[tid] = excl;
+    int run = excl;  // wave w's first position for expert tid
+#pragma unroll
+    for (int w = 0; w < W; ++w) {
+      const int n = sh.wave_cnt[w][tid];
+      sh.wave_cnt[w][tid] = run;
+      run += n;
+    }
   }
   if (tid == 0) p.offsets[E] = total;
   if (with_lists) write_lists(c, excl, E, p, sh.tmp);
@@ -95,37 +114,35 @@ __device__ void permute_block(KeyFn key, int N, int E, const Plan& p, bool with_
 
   const int nbits = (E > 1) ? 32 - __clz(E - 1) : 0;
   const uint64_t lt_mask = (1ull << lane) - 1ull;
-  // each round's key is loaded one round ahead
-  int key_next = key(min(tid, N - 1));
-  for (int base = 0; base < N; base += kPermThreads) {
-    const int q = base + tid;
-    const bool valid = q < N;
-    const int e = valid ? min(max(key_next, 0), E - 1) : 0;
-    key_next = key(min(q + kPermThreads, N - 1));
-    uint64_t peers = __ballot(valid);
-    for (int b = 0; b < nbits; ++b) {
-      const bool bit = (e >> b) & 1;
-      const uint64_t bal = __ballot(valid && bit);
-      peers &= bit ? bal : ~bal;
+  volatile int* const cursor = sh.wave_cnt[wave];  // read and moved in program order
+  // the keys of kKeyBatch batches are loaded together, then sorted in order
+  for (int g = q0; g < q1; g += kWave * kKeyBatch) {
+    int ks[kKeyBatch];
+#pragma unroll
+    for (int u = 0; u < kKeyBatch; ++u) ks[u] = key(min(g + u * kWave + lane, N - 1));
+#pragma unroll
+    for (int u = 0; u < kKeyBatch; ++u) {
+      if (g + u * kWave >= q1) break;  // wave-uniform: the chunk's last batch is done
+      const int q = g + u * kWave + lane;
+      const bool valid = q < q1;
+      const int e = valid ? min(max(ks[u], 0), E - 1) : 0;
+      uint64_t peers = __ballot(valid);
+      for (int b = 0; b < nbits; ++b) {
+        const bool bit = (e >> b) & 1;
+        const uint64_t bal = __ballot(valid && bit);
+        peers &= bit ? bal : ~bal;
+      }
+      const int rank = __popcll(peers & lt_mask);
+      // every lane reads its key's cursor before the leaders move them (one
+      // wave: its LDS accesses happen in program order)
+      const int start = cursor[e];
+      if (valid) {
+        const int pos = start + rank;
+        p.sorted_src[pos] = q;
+        p.dest_row[q] = pos;
+      }
+      if (valid && rank == 0) cursor[e] = start + __popcll(peers);
     }
-    const int rank = __popcll(peers & lt_mask);
-    const int cnt = __popcll(peers);
-    const bool leader = valid && rank == 0;
-    if (leader) sh.wave_cnt[wave][e] = cnt;
-    __syncthreads();
-    if (valid) {
-      int prefix = 0;
-      for (int w = 0; w < wave; ++w) prefix += sh.wave_cnt[w][e];
-      const int pos = sh.cursor[e] + prefix + rank;
-      p.sorted_src[pos] = q;
-      p.dest_row[q] = pos;
-    }
-    __syncthreads();
-    if (leader) {
-      atomicAdd(&sh.cursor[e], cnt);
-      sh.wave_cnt[wave][e] = 0;
-    }
-    __syncthreads();
   }
 }
 
