@@ -61,7 +61,9 @@ def test_route(T, E, k, mode):
 
 # ------------------------------------------------------------------- permute
 @pytest.mark.parametrize("T,E,k", [(1, 256, 8), (16, 256, 8), (4096, 256, 8), (333, 1024, 3),
-                                   (1000, 1, 1), (50, 7, 7), (2048, 64, 64), (129, 1000, 8)])
+                                   (1000, 1, 1), (50, 7, 7), (2048, 64, 64), (129, 1000, 8),
+                                   # a wave's chunk over several key groups, ragged at the end
+                                   (8191, 256, 8), (4097, 1024, 8), (3001, 512, 5)])
 def test_permute(T, E, k):
     from expert_ffn_layer_softmax_amd import moe_permute
     log(f"permute T={T} E={E} k={k}")
