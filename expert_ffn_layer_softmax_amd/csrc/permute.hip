@@ -66,9 +66,13 @@ __device__ void permute_block(KeyFn key, int N, int E, const Plan& p, bool with_
   const int tid = threadIdx.x;
   const int lane = lane_id();
   const int wave = tid >> 6;
-  const int C = ((N + W - 1) / W + kWave - 1) / kWave * kWave;
-  const int q0 = min(wave * C, N);
-  const int q1 = min(q0 + C, N);
+  // positions in uint32_t: N < 2^31, so chunk ends and batch steps past
+  // them stay representable
+  const uint32_t n = (uint32_t)N;
+  const uint32_t C = ((n + W - 1) / W + kWave - 1) / kWave * kWave;
+  const uint32_t q0 = min((uint32_t)wave * C, n);
+  const uint32_t q1 = q0 + min(C, n - q0);
+  auto kat = [&](uint32_t q) { return key((int)min(q, n - 1)); };  // clamped key load
 
   for (int i = tid; i < E; i += kPermThreads) {
 #pragma unroll
@@ -78,10 +82,10 @@ __device__ void permute_block(KeyFn key, int N, int E, const Plan& p, bool with_
   // per-wave counts; keys in groups of kKeyBatch per lane, all loads before
   // the adds (a load-then-add loop waits out each load's latency in turn)
   constexpr int kKeyBatch = 32;
-  for (int b = q0; b < q1; b += kWave * kKeyBatch) {
+  for (uint32_t b = q0; b < q1; b += kWave * kKeyBatch) {
     int ks[kKeyBatch];
 #pragma unroll
-    for (int u = 0; u < kKeyBatch; ++u) ks[u] = key(min(b + u * kWave + lane, N - 1));
+    for (int u = 0; u < kKeyBatch; ++u) ks[u] = kat(b + u * kWave + lane);
 #pragma unroll
     for (int u = 0; u < kKeyBatch; ++u) {
       if (b + u * kWave >= q1) break;  // wave-uniform
@@ -103,9 +107,9 @@ __device__ void permute_block(KeyFn key, int N, int E, const Plan& p, bool with_
     int run = excl;  // wave w's first position for expert tid
 #pragma unroll
     for (int w = 0; w < W; ++w) {
-      const int n = sh.wave_cnt[w][tid];
+      const int cw = sh.wave_cnt[w][tid];
       sh.wave_cnt[w][tid] = run;
-      run += n;
+      run += cw;
     }
   }
   if (tid == 0) p.offsets[E] = total;
@@ -116,14 +120,14 @@ __device__ void permute_block(KeyFn key, int N, int E, const Plan& p, bool with_
   const uint64_t lt_mask = (1ull << lane) - 1ull;
   volatile int* const cursor = sh.wave_cnt[wave];  // read and moved in program order
   // the keys of kKeyBatch batches are loaded together, then sorted in order
-  for (int g = q0; g < q1; g += kWave * kKeyBatch) {
+  for (uint32_t g = q0; g < q1; g += kWave * kKeyBatch) {
     int ks[kKeyBatch];
 #pragma unroll
-    for (int u = 0; u < kKeyBatch; ++u) ks[u] = key(min(g + u * kWave + lane, N - 1));
+    for (int u = 0; u < kKeyBatch; ++u) ks[u] = kat(g + u * kWave + lane);
 #pragma unroll
     for (int u = 0; u < kKeyBatch; ++u) {
       if (g + u * kWave >= q1) break;  // wave-uniform: the chunk's last batch is done
-      const int q = g + u * kWave + lane;
+      const uint32_t q = g + u * kWave + lane;
       const bool valid = q < q1;
       const int e = valid ? min(max(ks[u], 0), E - 1) : 0;
       uint64_t peers = __ballot(valid);
@@ -138,7 +142,7 @@ __device__ void permute_block(KeyFn key, int N, int E, const Plan& p, bool with_
       const int start = cursor[e];
       if (valid) {
         const int pos = start + rank;
-        p.sorted_src[pos] = q;
+        p.sorted_src[pos] = (int)q;
         p.dest_row[q] = pos;
       }
       if (valid && rank == 0) cursor[e] = start + __popcll(peers);
