@@ -595,3 +595,46 @@ def test_decode_fp4_full(name):
         assert err <= MXFP4_TOL
     del w
     torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("name", ["decode_mxfp4", "prefill_bf16"])
+def test_ep8_share_sampled(name):
+    """One GPU's expert-parallel share at G = 8, as the bench's ep8 share times
+    it: E/8 = 32 local experts, each of the T*k/8 dispatched rows routed to one
+    of them (k = 1), at the real d and f."""
+    import dataclasses
+    base = WORKLOADS[name]
+    wl = dataclasses.replace(base, E=base.E // 8, k=1, T=max(1, base.T * base.k // 8),
+                             name=f"{name}_ep8_share", logit_sets=1)
+    log(f"{wl.name}: T={wl.T} E={wl.E} k=1 d={wl.d} f={wl.f} {wl.wfmt}")
+    x, w, w_r, logits = make_inputs(wl)
+    S = None if wl.T <= 16 else np.random.default_rng(5).choice(wl.T, 6, replace=False)
+    got, ref, res = run_layer_and_oracle(wl, x, w, w_r, logits, sample=S)
+    err = rel_l2(got, ref["out"])
+    log(f"  rel_l2={err:.3e}")
+    assert err <= _tol(wl)
+    del w, res
+    torch.cuda.empty_cache()
+
+
+def test_prefill_expert_norm_full_sampled(full_bf16_weights):
+    """T=4096 with MOE_FLAG_EXPERT_NORM: the grouped GEMMs feed the
+    register-resident normalising combine at the real d and k."""
+    from expert_ffn_layer_softmax_amd import moe_layer_forward
+    wl = WORKLOADS["prefill_bf16"]
+    log("prefill_bf16 full (T=4096) with per-expert RMS normalisation, sampled tokens")
+    x, w, _, logits = make_inputs(wl, weights=full_bf16_weights)
+    res = moe_layer_forward(x, w, wl.k, logits=logits, expert_norm=True)
+    torch.cuda.synchronize()
+    lg = res["logits"].cpu().numpy()
+    check_routing(res, lg, wl.k, wl.E)
+    S = np.random.default_rng(11).choice(wl.T, 5, replace=False)
+    get = expert_getter(w, wl.wfmt)
+    xh = to_host_act(x)[S]
+    ref = oracle.layer(xh, lg[S], wl.k, get, E=wl.E, expert_norm=True)
+    plain = oracle.layer(xh, lg[S], wl.k, get, E=wl.E)
+    err = rel_l2(to_host_act(res["out"])[S], ref["out"])
+    sep = rel_l2(plain["out"], ref["out"])
+    log(f"  sampled tokens {sorted(S.tolist())}: rel_l2={err:.3e} (unnormalised differs by {sep:.3e})")
+    assert err <= 5e-3
+    assert sep > 0.1
