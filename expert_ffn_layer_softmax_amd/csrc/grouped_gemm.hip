@@ -1221,7 +1221,8 @@ __global__ __launch_bounds__(kThreads) void gg_mx_row_kernel(GGArgs a) {
 // group (8 bytes per row) come with one 32-lane 4-byte DMA per wave at the
 // group's first step.  The gate/up epilogue writes h as MXFP8: each wave's 32
 // columns are one block, whose maximum it takes across the 32 lanes of a half.
-constexpr int kF8A = 3;                                   // activation stages
+constexpr int kF8D = 4;                                   // activation steps in flight
+constexpr int kF8A = kF8D + 1;                            // activation stages
 constexpr int kStageA8 = BM * 64;                         // 8 KB
 constexpr int kAScalesGroup = BM * 8;                     // 1 KB
 constexpr int kF8Lds = kF8A * kStageA8 + kGroupBufs * (kCodesGroup + BN * 8 + kAScalesGroup);
@@ -1400,7 +1401,7 @@ __global__ __launch_bounds__(kThreads) void gg_f8f4_kernel(GGArgs a) {
 
   const int vm = min(max((nrows + 31) / 32 - 2 * wm, 0), 2);
 
-  // ---- prologue: groups 0 and 1, then activation steps 0 and 1 (youngest)
+  // ---- prologue: groups 0 and 1, then activation steps 0 .. kF8D-1 (youngest)
 #pragma unroll
   for (int g = 0; g < 2; ++g) {
 #pragma unroll
@@ -1408,35 +1409,43 @@ __global__ __launch_bounds__(kThreads) void gg_f8f4_kernel(GGArgs a) {
     issue_scales(g);
   }
   asm volatile("" ::: "memory");
-  issue_a(0);
-  issue_a(1);
+#pragma unroll
+  for (int kk = 0; kk < kF8D; ++kk) issue_a(kk);
 
   // Loads per step: one code DMA, at a group's first step the weight- and
-  // activation-scale DMAs, then the activation DMA (youngest).  Younger than
-  // activation stage kk: the loads of step kk-1 (two, four after a group's
-  // first step); at step 0 only stage 1's one.
+  // activation-scale DMAs, then the activation DMA (youngest), for step
+  // kk + kF8D.  Younger than activation stage kk are the loads of steps
+  // kk-3 .. kk-1 (two each, four at a group's first step): 6 at a group's
+  // first step, else 8.  In group 0 the prologue's younger activation stages
+  // stand in for the steps before 0: 3, 6, 7, 8.
+  static_assert(kF8D == 4 && kGroupSteps == 4, "wait counts below");
   auto main_loop = [&](auto vm_c) {
     constexpr int VM = decltype(vm_c)::value;
-    for (int g = 0; g < ng; ++g) {
+    auto group = [&](int g, auto n0, auto n1, auto n2, auto n3) {
       const char* cb = lds_c + (g % kGroupBufs) * kCodesGroup;
       const char* sb = lds_s + (g % kGroupBufs) * (BN * 8);
       const char* ab = lds_as + (g % kGroupBufs) * kAScalesGroup;
-#pragma unroll
-      for (int p = 0; p < kGroupSteps; ++p) {
+      auto step = [&](auto p_c, auto n_c) {
+        constexpr int p = decltype(p_c)::value;
         const int kk = kGroupSteps * g + p;
-        if (p == 1)
-          wait_and_barrier<4>();
-        else if (p == 0)
-          wait_and_barrier<1>();
-        else
-          wait_and_barrier<2>();
+        wait_and_barrier<decltype(n_c)::value>();
         issue_codes(g + 2, p);
-        if (p == 0) issue_scales(g + 2);
+        if constexpr (p == 0) issue_scales(g + 2);
         asm volatile("" ::: "memory");
-        issue_a(kk + 2);
+        issue_a(kk + kF8D);
         f8_step<VM>(lds_a + (kk % kF8A) * kStageA8, cb, sb, ab, p, arow, brow, half, acc);
-      }
-    }
+      };
+      step(std::integral_constant<int, 0>{}, n0);
+      step(std::integral_constant<int, 1>{}, n1);
+      step(std::integral_constant<int, 2>{}, n2);
+      step(std::integral_constant<int, 3>{}, n3);
+    };
+    using C3 = std::integral_constant<int, 3>;
+    using C6 = std::integral_constant<int, 6>;
+    using C7 = std::integral_constant<int, 7>;
+    using C8 = std::integral_constant<int, 8>;
+    if (ng > 0) group(0, C3{}, C6{}, C7{}, C8{});
+    for (int g = 1; g < ng; ++g) group(g, C6{}, C8{}, C8{}, C8{});
   };
   if (vm == 2)
     main_loop(std::integral_constant<int, 2>{});
