@@ -290,7 +290,9 @@ def measure(wl, ws_list, args, with_cpu: bool):
     step_bytes, step_flops = nl * layer_bytes, nl * layer_flops
     t_floor = max(step_bytes / (HBM_PEAK_GBS * 1e9), step_flops / (mfma_peak * 1e12))
     digest = _source_digest(srcs)
-    traffic = _traffic(kname, wl.name, digest) if nl == 1 else None
+    # counters are kept per path: the FP8 GEMMs are other kernels than the
+    # bf16-activation ones of the same workload
+    traffic = _traffic(kname, wl.name + ("_fp8" if args.fp8 else ""), digest) if nl == 1 else None
     breakdown = {}
     for kn in moe_timing_names():
         n, t = moe_timing_query(kn)
