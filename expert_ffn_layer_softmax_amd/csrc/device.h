@@ -39,14 +39,12 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
 // straight into the exponent.  Not a value for fp32 arithmetic.
 __device__ __forceinline__ float e8m0_cvt_scale(uint32_t s) { return __uint_as_float(s << 23); }
 
-// OCP FP8 E4M3 byte -> fp32, exactly: 1 sign, 4 exponent bits (bias 7),
-// 3 mantissa bits, subnormals m * 2^-9 at exponent 0.  The NaN bytes 0x7F and
-// 0xFF are outside the supported inputs (they decode to +-480 here).
+// OCP FP8 E4M3 byte (the low byte of b) -> fp32, exactly, by the gfx950
+// convert, which reads the OCP format: 1 sign, 4 exponent bits (bias 7), 3
+// mantissa bits, subnormals m * 2^-9 at exponent 0, NaN for 0x7F and 0xFF
+// (outside the supported inputs).
 __device__ __forceinline__ float e4m3_to_f32(uint32_t b) {
-  const uint32_t e = (b >> 3) & 15u;
-  const uint32_t m = b & 7u;
-  const float v = (e == 0u) ? (float)m * 0.001953125f : __uint_as_float(((e + 120u) << 23) | (m << 20));
-  return (b & 0x80u) ? -v : v;
+  return __builtin_amdgcn_cvt_f32_fp8((int)b, 0);
 }
 
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
