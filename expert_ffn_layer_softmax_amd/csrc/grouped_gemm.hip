@@ -54,6 +54,17 @@
 namespace moe {
 namespace {
 
+// silu(g) * u = g * u / (1 + e^-g) for the gate/up epilogues, with the
+// hardware exponential and reciprocal (each about one ulp of fp32) instead of
+// the library expf and an IEEE division: h is rounded to bf16 or MXFP8 right
+// after, far more coarsely, and with one block per CU nothing hides the
+// epilogue's instructions.  Large negative g gives 0 (the exponential
+// overflows to inf, its reciprocal to 0), as the exact form does.
+__device__ __forceinline__ float silu_mul(float g, float u) {
+  return g * u * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-1.44269504088896f * g));
+}
+
+
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 
@@ -305,7 +316,7 @@ __global__ __launch_bounds__(kThreads) void gg_direct_b_kernel(GGArgs a) {
           if (col0 < a.N) {
             const float g = acc[0][mi][i];
             const float u = acc[1][mi][i];
-            reinterpret_cast<uint16_t*>(a.out)[orow + col0] = f32_to_bf16(g / (1.0f + expf(-g)) * u);
+            reinterpret_cast<uint16_t*>(a.out)[orow + col0] = f32_to_bf16(silu_mul(g, u));
           }
         } else {
           if (col0 < a.N) reinterpret_cast<float*>(a.out)[orow + col0] = acc[0][mi][i];
@@ -563,7 +574,7 @@ __global__ __launch_bounds__(kThreads) void gg_dma_kernel(GGArgs a) {
             if (col < a.N) {
               const float g = acc[0][mi][i];
               const float u = acc[1][mi][i];
-              reinterpret_cast<uint16_t*>(a.out)[orow + col] = f32_to_bf16(g / (1.0f + expf(-g)) * u);
+              reinterpret_cast<uint16_t*>(a.out)[orow + col] = f32_to_bf16(silu_mul(g, u));
             }
           } else {
 #pragma unroll
@@ -921,7 +932,7 @@ __global__ __launch_bounds__(kThreads) void gg_mx_group_kernel(GGArgs a) {
             if (col < a.N) {
               const float g = acc[0][mi][i];
               const float u = acc[1][mi][i];
-              reinterpret_cast<uint16_t*>(a.out)[orow + col] = f32_to_bf16(g / (1.0f + expf(-g)) * u);
+              reinterpret_cast<uint16_t*>(a.out)[orow + col] = f32_to_bf16(silu_mul(g, u));
             }
           } else {
 #pragma unroll
@@ -1192,7 +1203,7 @@ __global__ __launch_bounds__(kThreads) void gg_mx_row_kernel(GGArgs a) {
           const int col = nbase + 16 * wave + cl;
           if (cl < 16 && row < nrows && col < a.N)
             reinterpret_cast<uint16_t*>(a.out)[(size_t)(row0 + row) * a.N + col] =
-                f32_to_bf16(v / (1.0f + expf(-v)) * u);
+                f32_to_bf16(silu_mul(v, u));
         } else {
           const int col = nbase + 32 * wave + cl;
           if (row < nrows && col < a.N) reinterpret_cast<float*>(a.out)[(size_t)(row0 + row) * a.N + col] = v;
@@ -1470,7 +1481,7 @@ __global__ __launch_bounds__(kThreads) void gg_f8f4_kernel(GGArgs a) {
         for (int i = 0; i < 16; ++i) {
           const int row = 64 * wm + 32 * mi + 8 * (i >> 2) + 4 * half + (i & 3);
           const float g = acc[0][mi][i];
-          const float h = g / (1.0f + expf(-g)) * acc[1][mi][i];
+          const float h = silu_mul(g, acc[1][mi][i]);
           float amax = fabsf(h);
 #pragma unroll
           for (int o = 1; o < 32; o <<= 1) amax = fmaxf(amax, __shfl_xor(amax, o, kWave));
