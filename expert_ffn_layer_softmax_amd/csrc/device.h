@@ -23,14 +23,11 @@ __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w 
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 __device__ __forceinline__ float bf16_to_f32(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
 
-// fp32 -> bf16, round to nearest even; NaN stays a (quiet) NaN.  Written as a
-// select, not a branch: a data-dependent branch inside a streaming loop makes
-// the compiler's wait counting conservative.
+// fp32 -> bf16, round to nearest even; NaN stays a (quiet) NaN.  One gfx950
+// convert (v_cvt_pk_bf16_f32), with no branch: a data-dependent branch inside
+// a streaming loop makes the compiler's wait counting conservative.
 __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
-  const uint32_t u = __float_as_uint(f);
-  const uint32_t rounded = (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
-  const uint32_t quiet = (u >> 16) | 0x40u;
-  return (uint16_t)(((u & 0x7fffffffu) > 0x7f800000u) ? quiet : rounded);
+  return __builtin_bit_cast(uint16_t, (__bf16)f);
 }
 
 // An E8M0 byte as the scale operand of the gfx950 scaled FP4 converts: they
