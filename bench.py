@@ -2,12 +2,19 @@
 
 A step is one ``moe_layer_forward`` call (route -> permute -> expert FFN ->
 combine) over one synthetic batch whose inputs are already resident in HBM.
-Each step routes by the next of 64 pre-drawn logit sets, so consecutive steps
-touch different experts and the 256 MB Infinity Cache cannot serve the weights.
+Decode steps route by the next of 64 pre-drawn logit sets, so consecutive
+steps touch different experts and the 256 MB Infinity Cache cannot serve the
+weights.
 
-Prints one JSON line: tokens/s, the dominant kernel's roofline fraction
-(its algorithmic bytes over its HIP-event duration, measured on the launch
-stream inside this run), and the CPU oracle timed on a bounded sample.
+Prints one JSON line per workload: tokens/s (median of three timed loops),
+the dominant kernel's roofline fraction (its algorithmic bytes or FLOPs over
+its HIP-event duration, measured on the launch stream inside this run), and
+the CPU oracle timed on a bounded sample.  Without --workload it runs
+single-token bf16 decode, then MX-FP4 prefill, then bf16 prefill (T=4096).
+
+``--calibrate-counters`` instead runs three plain 1 GiB device-to-device
+copies: the reference that scales the FETCH_SIZE / WRITE_SIZE hardware
+counters into bytes.
 """
 
 from __future__ import annotations
@@ -28,13 +35,24 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
 FP8_PEAK_TFLOPS = 5000.0       # MI355X dense fp8 MFMA (the FP8 x FP4 scaled MFMA runs at this rate)
 
+# Default workloads, in print order: the single-token decode the headline is
+# quoted on, then 4K-token prefill with MX-FP4 and with bf16 weights.
+DEFAULT_WORKLOADS = ("decode_bf16", "prefill_mxfp4", "prefill_bf16")
+
 
 def _parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
-    p.add_argument("--steps", type=int, default=500)
-    p.add_argument("--warmup", type=int, default=50)
-    p.add_argument("--workload", default="decode_bf16")
+    p.add_argument("--steps", type=int, default=100)
+    p.add_argument("--warmup", type=int, default=10)
+    p.add_argument("--workload", default=None,
+                   help="one workload (default: " + ", ".join(DEFAULT_WORKLOADS) + ", in that order)")
+    p.add_argument("--repeats", type=int, default=3,
+                   help="timed loops of --steps steps each; value is their median")
+    p.add_argument("--cpu-tokens", type=int, default=16,
+                   help="tokens per CPU oracle call on workloads with more tokens than that")
+    p.add_argument("--calibrate-counters", action="store_true",
+                   help="run three 1 GiB device copies (counter calibration) and exit")
     p.add_argument("--cpu-seconds", type=float, default=12.0,
                    help="CPU oracle sample budget (seconds of oracle work)")
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle leg")
@@ -106,10 +124,13 @@ def _traffic(kernel: str, workload: str, digest: str):
 
 
 def cpu_baseline(wl, x, w, logit_sets, budget_s: float, fp8: bool = False,
-                 expert_norm: bool = False):
-    """The oracle, as it stands, on the host: one token per logit set until the
-    budget is spent.  Expert weights are copied to host memory untimed; decoding
-    them to fp64 is part of the oracle's timed work."""
+                 expert_norm: bool = False, chunk: int = 16):
+    """The oracle, as it stands, on the host, until the budget is spent.
+    Workloads of up to `chunk` tokens run whole, one call per logit set; larger
+    ones run `chunk` consecutive tokens of the batch per call (the layer is
+    per-token independent), from the first token on.  Expert weights are
+    copied to host memory untimed; decoding them to fp64 is part of the
+    oracle's timed work."""
     import numpy as np
     import torch
 
@@ -127,16 +148,22 @@ def cpu_baseline(wl, x, w, logit_sets, budget_s: float, fp8: bool = False,
             return t.contiguous().view(torch.uint8).cpu().numpy()
         return t.cpu().numpy()
 
-    xh_raw = raw(x)
+    xh_all = raw(x)
     T = wl.T
-    done_tokens, spent, sets_used = 0, 0.0, 0
-    for s in range(logit_sets.shape[0]):
-        lg = logit_sets[s].cpu().numpy()
+    calls = []  # (logit set, first token, tokens)
+    if T <= chunk:
+        calls = [(s, 0, T) for s in range(logit_sets.shape[0])]
+    else:
+        calls = [(0, t0, min(chunk, T - t0)) for t0 in range(0, T, chunk)]
+    done_tokens, spent, ncalls = 0, 0.0, 0
+    for s, t0, n in calls:
+        lg = logit_sets[s][t0:t0 + n].cpu().numpy()
+        xh_raw = xh_all[t0:t0 + n]
         idx, _ = oracle.route(lg, wl.k)
         experts = sorted(set(idx.ravel().tolist()))
         host = {}
         for e in experts:      # untimed staging to host memory
-            host[e] = {n: raw(w[n][e]) for n in w}
+            host[e] = {nm: raw(w[nm][e]) for nm in w}
 
         def get(e):
             h = host[e]
@@ -149,19 +176,24 @@ def cpu_baseline(wl, x, w, logit_sets, budget_s: float, fp8: bool = False,
                 return tuple(h["w_" + n].astype(np.float64) for n in ("gate", "up", "down"))
             return tuple(oracle.decode_bf16(h["w_" + n]) for n in ("gate", "up", "down"))
 
-        t0 = time.perf_counter()
+        t_start = time.perf_counter()
         xh = oracle.decode_bf16(xh_raw) if wl.act == "bf16" else xh_raw.astype(np.float64)
         oracle.layer(xh, lg, wl.k, get, E=wl.E, act_quant=oracle.quantize_mxfp8 if fp8 else None,
                      expert_norm=expert_norm)
-        spent += time.perf_counter() - t0
-        done_tokens += T
-        sets_used += 1
+        spent += time.perf_counter() - t_start
+        done_tokens += n
+        ncalls += 1
         del host
         if spent >= budget_s:
             break
+    if T <= chunk:
+        what = (f"{ncalls} layer call(s) of the {wl.name} workload ({done_tokens} tokens, each call "
+                f"with its own routing)")
+    else:
+        what = (f"the first {done_tokens} of the {T} tokens of the {wl.name} workload, {chunk} tokens "
+                f"per oracle call ({ncalls} calls), with the batch's own routing")
     return {"value": done_tokens / spent, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"{sets_used} layer call(s) of the {wl.name} workload ({done_tokens} tokens, "
-                      f"each with its own routing), numpy fp64, {spent:.1f} s; host affinity "
+            "sample": f"{what}; numpy fp64, {spent:.1f} s; host affinity "
                       f"{len(os.sched_getaffinity(0))} cores"}
 
 
@@ -249,11 +281,14 @@ def measure(wl, ws_list, args, with_cpu: bool):
     torch.cuda.synchronize()
     print(f"[bench] {wl.name}: timing {args.steps} steps of {nl} layer(s)"
           f"{' from HIP graphs' if graphs else ''}", file=sys.stderr, flush=True)
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        step(i)
-    torch.cuda.synchronize()
-    el = time.perf_counter() - t0
+    loops = []
+    for r in range(max(1, args.repeats)):
+        t0 = time.perf_counter()
+        for i in range(args.steps):
+            step(r * args.steps + i)
+        torch.cuda.synchronize()
+        loops.append(time.perf_counter() - t0)
+    el = sorted(loops)[len(loops) // 2]
     ms = el * 1e3 / args.steps
     tokens_per_s = getattr(args, "job_tokens", wl.T) * args.steps / el
 
@@ -312,6 +347,7 @@ def measure(wl, ws_list, args, with_cpu: bool):
     rec = {
         "metric": METRIC, "value": round(tokens_per_s, 2), "unit": "tokens/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 5),
+        "repeats": len(loops), "ms_per_step_loops": [round(v * 1e3 / args.steps, 5) for v in loops],
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "fp8" if args.fp8 else ("bf16" if wl.act == "bf16" else "f32"), "data": "synthetic",
         "config": cfg,
@@ -329,24 +365,33 @@ def measure(wl, ws_list, args, with_cpu: bool):
     if with_cpu:
         print("[bench] CPU oracle baseline", file=sys.stderr, flush=True)
         rec["cpu_baseline"] = cpu_baseline(wl, x, ws_list[0], sets, args.cpu_seconds, args.fp8,
-                                           args.expert_norm)
+                                           args.expert_norm, chunk=args.cpu_tokens)
     else:
         rec["cpu_baseline"] = None
     return rec
 
 
-def main():
-    args = _parse()
-    if args.gpus != 1:
-        print(f"bench.py measures one GPU only (got --gpus {args.gpus}); this library has no "
-              "multi-GPU path", file=sys.stderr)
-        sys.exit(2)
+def calibrate_counters():
+    """Three plain 1 GiB device-to-device copies: what FETCH_SIZE and
+    WRITE_SIZE read for them gives the factors that turn the counters into
+    bytes (run under rocprofv3 --pmc with the copy kernel's name)."""
+    import torch
 
+    a = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+    b = torch.empty_like(a)
+    a.fill_(1)
+    for _ in range(3):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print("copied 3 x 1 GiB device to device", flush=True)
+
+
+def run_workload(name, args):
     import torch
 
     from synth import WORKLOADS, gen_expert_weights
 
-    base = WORKLOADS[args.workload]
+    base = WORKLOADS[name]
     assert not base.router, "bench workloads route by pre-drawn logits"
     if args.share:
         # One GPU's share at G = 8.  Expert parallelism: E/8 local experts
@@ -360,8 +405,6 @@ def main():
             base = dataclasses.replace(base, f=base.f // 8, name=f"{base.name}_tp8_share")
         if args.T is not None or args.sweep:
             raise SystemExit("--share takes the workload's own T")
-    if args.layers < 1:
-        raise SystemExit("--layers must be >= 1")
     dev = torch.device("cuda:0")
     print(f"[bench] generating {base.name} weights for {args.layers} layer(s)", file=sys.stderr, flush=True)
     # each layer's experts come from their own seed
@@ -371,15 +414,34 @@ def main():
         for T in [int(t) for t in args.sweep.split(",")]:
             wl = dataclasses.replace(base, T=T, name=f"{base.name}_T{T}")
             print(json.dumps(measure(wl, ws_list, args, with_cpu=False)), flush=True)
+    else:
+        wl = base
+        if args.T is not None:
+            wl = dataclasses.replace(base, T=args.T, name=f"{base.name}_T{args.T}")
+        rec = measure(wl, ws_list, args, with_cpu=not args.no_cpu and args.layers == 1 and not args.share)
+        if args.share:
+            rec["config"]["share"] = args.share
+            rec["config"]["job_tokens"] = args.job_tokens
+        print(json.dumps(rec), flush=True)
+    del ws_list
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+
+
+def main():
+    args = _parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (got --gpus {args.gpus}); this library has no "
+              "multi-GPU path", file=sys.stderr)
+        sys.exit(2)
+    if args.calibrate_counters:
+        calibrate_counters()
         return
-    wl = base
-    if args.T is not None:
-        wl = dataclasses.replace(base, T=args.T, name=f"{base.name}_T{args.T}")
-    rec = measure(wl, ws_list, args, with_cpu=not args.no_cpu and args.layers == 1 and not args.share)
-    if args.share:
-        rec["config"]["share"] = args.share
-        rec["config"]["job_tokens"] = args.job_tokens
-    print(json.dumps(rec), flush=True)
+    if args.layers < 1:
+        raise SystemExit("--layers must be >= 1")
+    names = [args.workload] if args.workload else list(DEFAULT_WORKLOADS)
+    for name in names:
+        run_workload(name, args)
 
 
 if __name__ == "__main__":

@@ -2,9 +2,9 @@
 
 Thin ctypes marshalling over the C ABI in ``include/moe.h``; every step of
 the layer runs in the HIP kernels of ``libmoe_mi355x.so``.  PyTorch supplies
-device memory and the current HIP stream only.  Importing this module raises
-if the library has not been built (``python -m expert_ffn_layer_softmax_amd.build``);
-there is no CPU fallback.
+device memory and the current HIP stream only.  The library is opened on
+first use; that first call raises ImportError if it has not been built
+(``python -m expert_ffn_layer_softmax_amd.build``).  There is no CPU fallback.
 """
 
 from ._lib import (  # noqa: F401
@@ -17,10 +17,12 @@ from ._lib import (  # noqa: F401
     MOE_FLAG_FP8_ACTIVATIONS,
     MoeError,
     lib,
+    load,
     moe_combine,
     moe_expert_ffn,
     moe_layer_forward,
     moe_permute,
+    moe_quantize_mxfp8,
     moe_route,
     moe_status_string,
     moe_timing_names,

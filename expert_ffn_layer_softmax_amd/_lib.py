@@ -21,13 +21,6 @@ LIB_PATH = os.environ.get("MOE_MI355X_LIB") or os.path.join(_PKG, "libmoe_mi355x
 MOE_OK = 0
 MOE_DTYPE_F32, MOE_DTYPE_BF16, MOE_DTYPE_MXFP4, MOE_DTYPE_NVFP4 = 0, 1, 2, 3
 
-if not os.path.exists(LIB_PATH):
-    raise ImportError(
-        f"{LIB_PATH} is missing: build the HIP library first "
-        "(python -m expert_ffn_layer_softmax_amd.build); there is no CPU fallback")
-
-lib = ctypes.CDLL(LIB_PATH, mode=ctypes.RTLD_GLOBAL)
-
 
 class MoeDims(ctypes.Structure):
     _fields_ = [("T", ctypes.c_int32), ("d", ctypes.c_int32), ("E", ctypes.c_int32),
@@ -56,13 +49,49 @@ _SIGS = {
     "moe_timing_query": [ctypes.c_char_p, _P(_i32), _P(ctypes.c_double)],
     "moe_timing_names": [ctypes.c_char_p, _sz],
     "moe_last_device_error": [],
+    "moe_quantize_mxfp8": [_vp, ctypes.c_int64, _i32, _vp, _vp, _vp],
 }
-for _name, _args in _SIGS.items():
-    _fn = getattr(lib, _name)
-    _fn.argtypes = _args
-    _fn.restype = ctypes.c_int32
-lib.moe_status_string.argtypes = [ctypes.c_int32]
-lib.moe_status_string.restype = ctypes.c_char_p
+
+
+class _Library:
+    """``libmoe_mi355x.so``, opened on first use.
+
+    Importing the package needs no built library (so a fresh checkout can run
+    the build); the first call into the library opens it and raises
+    ImportError if it has not been built.  There is no CPU fallback.
+    """
+
+    def __init__(self):
+        self._cdll = None
+
+    def _open(self):
+        if self._cdll is None:
+            if not os.path.exists(LIB_PATH):
+                raise ImportError(
+                    f"{LIB_PATH} is missing: build the HIP library first "
+                    "(python -m expert_ffn_layer_softmax_amd.build); there is no CPU fallback")
+            cdll = ctypes.CDLL(LIB_PATH, mode=ctypes.RTLD_GLOBAL)
+            for name, args in _SIGS.items():
+                fn = getattr(cdll, name)
+                fn.argtypes = args
+                fn.restype = ctypes.c_int32
+            cdll.moe_status_string.argtypes = [ctypes.c_int32]
+            cdll.moe_status_string.restype = ctypes.c_char_p
+            self._cdll = cdll
+        return self._cdll
+
+    def __getattr__(self, name):
+        if name.startswith("_"):
+            raise AttributeError(name)
+        return getattr(self._open(), name)
+
+
+lib = _Library()
+
+
+def load():
+    """Open the library now (raises ImportError if it is not built)."""
+    return lib._open()
 
 
 class MoeError(RuntimeError):
@@ -286,6 +315,21 @@ def moe_layer_forward(x, weights: dict, k, logits=None, w_router=None, topk_idx=
                                  ctypes.byref(w), _ptr(topk_idx), _ptr(topk_w), _ptr(out), _ptr(ws),
                                  ws.numel(), _stream(x)), "moe_layer_forward")
     return dict(out=out, logits=logits, topk_idx=topk_idx, topk_w=topk_w, workspace=ws)
+
+
+def moe_quantize_mxfp8(x, q=None, scales=None):
+    """MXFP8 codes and E8M0 block scales of bf16 ``x[rows][K]`` (the FP8
+    path's activation quantisation, exposed for checking)."""
+    _need(x, "x", torch.bfloat16)
+    rows, K = x.shape
+    dev = x.device
+    q = torch.empty(rows, K, dtype=torch.uint8, device=dev) if q is None else q
+    scales = torch.empty(rows, K // 32, dtype=torch.uint8, device=dev) if scales is None else scales
+    _need(q, "q", torch.uint8, (rows, K), dev)
+    _need(scales, "scales", torch.uint8, (rows, K // 32), dev)
+    _check(lib.moe_quantize_mxfp8(_ptr(x), rows, K, _ptr(q), _ptr(scales), _stream(x)),
+           "moe_quantize_mxfp8")
+    return q, scales
 
 
 def moe_timing_start():

@@ -3,6 +3,8 @@
 // queues no work.  No device memory is allocated here.
 #include <hip/hip_runtime.h>
 
+#include <atomic>
+#include <cstring>
 #include <mutex>
 #include <string>
 #include <vector>
@@ -22,14 +24,19 @@ size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 // ------------------------------------------------------------------ timing --
+// `enabled` is read without the lock on every launch (the common, disabled
+// case); everything else is guarded by `mu`.  `generation` counts
+// moe_timing_start calls, so a launch whose slot was handed out before a
+// restart does not record into a slot that now belongs to another launch.
 constexpr int kMaxTimed = 8192;
 struct TimerState {
   std::mutex mu;
-  bool enabled = false;
+  std::atomic<bool> enabled{false};
   bool created = false;
   std::vector<hipEvent_t> ev0, ev1;
   std::vector<std::string> names;
   int used = 0;
+  unsigned generation = 0;
 };
 TimerState& timer() {
   static TimerState t;
@@ -38,19 +45,22 @@ TimerState& timer() {
 
 }  // namespace
 
-LaunchTimer::LaunchTimer(const char* name, hipStream_t s) : name_(name), s_(s), slot_(-1) {
+LaunchTimer::LaunchTimer(const char* name, hipStream_t s) : name_(name), s_(s), slot_(-1), gen_(0) {
   TimerState& t = timer();
-  if (!t.enabled) return;
+  if (!t.enabled.load(std::memory_order_relaxed)) return;
   std::lock_guard<std::mutex> lk(t.mu);
-  if (!t.enabled || t.used >= kMaxTimed) return;
+  if (!t.enabled.load(std::memory_order_relaxed) || t.used >= kMaxTimed) return;
   slot_ = t.used++;
+  gen_ = t.generation;
   t.names[slot_] = name;
   (void)hipEventRecord(t.ev0[slot_], s);
 }
 
 LaunchTimer::~LaunchTimer() {
   if (slot_ < 0) return;
-  (void)hipEventRecord(timer().ev1[slot_], s_);
+  TimerState& t = timer();
+  std::lock_guard<std::mutex> lk(t.mu);
+  if (t.generation == gen_) (void)hipEventRecord(t.ev1[slot_], s_);
 }
 
 WsLayout ws_layout(const Dims& dm) {
@@ -313,8 +323,25 @@ moe_status_t moe_layer_forward(const moe_dims_t* dims, const void* x, const void
   return device_status(e);
 }
 
+moe_status_t moe_quantize_mxfp8(const void* x, int64_t rows, int32_t K, uint8_t* q,
+                                uint8_t* scales, moe_stream_t stream) {
+  if (rows < 0 || K <= 0) return MOE_ERR_INVALID_ARGUMENT;
+  if (K % 32 != 0) return MOE_ERR_UNSUPPORTED;
+  // one thread per 32-element block: at most 2^31 threads in the grid
+  if (rows > ((int64_t)1 << 31) / (K / 32)) return MOE_ERR_UNSUPPORTED;
+  if (rows == 0) return MOE_OK;
+  if (!x || !q || !scales) return MOE_ERR_INVALID_ARGUMENT;
+  if (!aligned16(x) || !aligned16(q)) return MOE_ERR_INVALID_ARGUMENT;
+  return device_status(launch_quantize_mxfp8(x, rows, K, q, scales, (hipStream_t)stream));
+}
+
 const char* moe_status_string(moe_status_t status) {
-  switch (status) {
+  // A C caller may pass any int; in C++ loading an enum outside its declared
+  // values is undefined, so the argument's bits are read as an int first.
+  int32_t code = 0;
+  static_assert(sizeof(status) == sizeof(code), "moe_status_t is an int");
+  std::memcpy(&code, &status, sizeof code);
+  switch (code) {
     case MOE_OK: return "ok";
     case MOE_ERR_INVALID_ARGUMENT: return "invalid argument";
     case MOE_ERR_UNSUPPORTED: return "unsupported shape or dtype combination";
@@ -341,14 +368,15 @@ moe_status_t moe_timing_start(void) {
     t.created = true;
   }
   t.used = 0;
-  t.enabled = true;
+  ++t.generation;
+  t.enabled.store(true, std::memory_order_relaxed);
   return MOE_OK;
 }
 
 moe_status_t moe_timing_stop(void) {
   TimerState& t = timer();
   std::lock_guard<std::mutex> lk(t.mu);
-  t.enabled = false;
+  t.enabled.store(false, std::memory_order_relaxed);
   return MOE_OK;
 }
 

@@ -59,9 +59,11 @@ namespace {
 // the library expf and an IEEE division: h is rounded to bf16 or MXFP8 right
 // after, far more coarsely, and with one block per CU nothing hides the
 // epilogue's instructions.  Large negative g gives 0 (the exponential
-// overflows to inf, its reciprocal to 0), as the exact form does.
+// overflows to inf, its reciprocal to 0), as the exact form does; silu(g) is
+// formed before the product with u, so a large u cannot turn that 0 into
+// inf * 0 = NaN.
 __device__ __forceinline__ float silu_mul(float g, float u) {
-  return g * u * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-1.44269504088896f * g));
+  return g * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-1.44269504088896f * g)) * u;
 }
 
 
@@ -1279,14 +1281,17 @@ __device__ __forceinline__ void f8_step(const char* st, const char* cb, const ch
 }
 
 // OCP FP8 E4M3 byte of v (already divided by its block scale): round to
-// nearest even, saturating at +-448 (the convert itself would give NaN).
+// nearest even, saturating at +-448 (the convert itself would give NaN).  A
+// NaN stays NaN: the clamp would turn it into -448, so it is selected around.
 __device__ __forceinline__ uint32_t e4m3_byte(float v) {
-  v = fminf(fmaxf(v, -448.0f), 448.0f);
+  const float c = fminf(fmaxf(v, -448.0f), 448.0f);
+  v = v != v ? v : c;
   return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(v, v, 0, false) & 0xffu;
 }
 
 // E8M0 byte of a block whose largest magnitude is amax: 2^(floor(log2 amax)
-// - 8), the MX rule for E4M3 elements, kept in [1, 254].
+// - 8), the MX rule for E4M3 elements, kept in [1, 254].  amax is taken with
+// fmaxf, which skips NaN: a block's scale comes from its non-NaN elements.
 __device__ __forceinline__ uint32_t mxfp8_scale_byte(float amax) {
   const int ef = (int)((__float_as_uint(amax) >> 23) & 0xffu);
   return (uint32_t)min(max(ef - 8, 1), 254);

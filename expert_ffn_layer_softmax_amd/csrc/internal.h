@@ -75,6 +75,7 @@ struct LaunchTimer {
   const char* name_;
   hipStream_t s_;
   int slot_;
+  unsigned gen_;  // timing generation the slot was taken in
 };
 
 // Launchers: each queues one kernel on `s` and returns hipGetLastError().

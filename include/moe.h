@@ -155,7 +155,11 @@ moe_status_t moe_route(const float* logits, int32_t T, int32_t E, int32_t k,
                        int32_t* topk_idx, float* topk_w, moe_stream_t stream);
 
 /* Group the T*k (token, slot) pairs by expert (a stable counting sort of
- * flat ids q = t*k + j by topk_idx.flat[q]).
+ * flat ids q = t*k + j by topk_idx.flat[q]).  Each token is sent to k of the
+ * E experts (8 of 256 in the pages' model: SGLang-TorchTPU on TPU v7 page,
+ * "Introduction"), so every expert computes on the rows routed to it; this
+ * call lays those rows out expert by expert for the grouped expert FFN and
+ * records where each pair landed for the combine.
  *   counts[E]        pairs routed to each expert
  *   offsets[E+1]     exclusive prefix sum of counts, offsets[E] = T*k
  *   sorted_src[T*k]  flat ids ordered by expert, ascending q within an expert
@@ -190,7 +194,13 @@ moe_status_t moe_combine(const moe_dims_t* dims, const float* y_sorted, const in
                          const float* topk_w, void* out, moe_stream_t stream);
 
 /* The whole layer: [router logits] -> route -> permute -> expert FFN ->
- * combine.  If w_router is non-NULL, logits[T][E] = x . w_router^T (fp32
+ * combine, i.e. the forward pass of one Mixture-of-Experts decoder layer that
+ * sends each token to k of its E experts (SGLang-TorchTPU on TPU v7 page,
+ * "Introduction") and combines the selected experts' outputs after their
+ * normalisation (TensorSharp Muse Spark report, "Performance" section):
+ *   out[t] = sum_{j<k} topk_w[t][j] * FFN_{topk_idx[t][j]}(x[t])
+ * with the routing of moe_route, the FFN of moe_expert_ffn and the sum of
+ * moe_combine.  If w_router is non-NULL, logits[T][E] = x . w_router^T (fp32
  * accumulation) is written to `logits`; otherwise `logits` is read as input.
  * topk_idx / topk_w receive the routing.  For T == 1 (k <= 16, no
  * MOE_FLAG_* set) the down projection is fused with the combine; the per-token sum keeps slot order
@@ -201,6 +211,22 @@ moe_status_t moe_layer_forward(const moe_dims_t* dims, const void* x, const void
                                float* logits, const moe_expert_weights_t* weights,
                                int32_t* topk_idx, float* topk_w, void* out, void* workspace,
                                size_t workspace_bytes, moe_stream_t stream);
+
+/* MXFP8 quantisation of bf16 activations, the first step of the FP8-compute
+ * path (MOE_FLAG_FP8_ACTIVATIONS; "FP8 compute" with 4-bit expert weights:
+ * SGLang-TorchTPU on TPU v7 page, "Results").  For each run of 32
+ * consecutive elements of a row of x (bf16 [rows][K], K a positive multiple
+ * of 32):
+ *   scales[r][b] = E8M0 byte of 2^(floor(log2 amax) - 8), amax the largest
+ *                  magnitude of the block's non-NaN elements, kept in [1, 254]
+ *   q[r][32b + i] = OCP FP8 E4M3 byte of x / 2^(scales[r][b] - 127), rounded
+ *                  to nearest even and saturated at +-448; NaN stays NaN.
+ * So each block decodes to E4M3(q) * 2^(s - 127).  An all-zero block gives
+ * zero codes (its scale byte is then 1).  Infinite inputs are outside the
+ * domain.  q is uint8 [rows][K], scales uint8 [rows][K/32]; x and q must be
+ * 16-byte aligned.  rows == 0 is a no-op. */
+moe_status_t moe_quantize_mxfp8(const void* x, int64_t rows, int32_t K, uint8_t* q,
+                                uint8_t* scales, moe_stream_t stream);
 
 /* Static, NUL-terminated description of a status code. */
 const char* moe_status_string(moe_status_t status);
@@ -214,8 +240,10 @@ int32_t moe_last_device_error(void);
  * not).  moe_timing_start clears earlier records and enables; moe_timing_stop
  * disables.  moe_timing_query waits for the recorded events and returns, for
  * the kernel named `kernel` (e.g. "gemv_gate_up"), the number of recorded
- * launches and their summed duration in milliseconds.  moe_timing_names
- * writes the distinct recorded kernel names, comma separated, into buf. */
+ * launches and their summed duration in milliseconds; call it after the
+ * launches it should cover have returned.  moe_timing_names writes the
+ * distinct recorded kernel names, comma separated, into buf.  All four are
+ * thread-safe. */
 moe_status_t moe_timing_start(void);
 moe_status_t moe_timing_stop(void);
 moe_status_t moe_timing_query(const char* kernel, int32_t* launches, double* total_ms);

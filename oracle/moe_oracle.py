@@ -227,12 +227,15 @@ def quantize_mxfp8(v: np.ndarray) -> np.ndarray:
     """The values an MXFP8 encoding of ``v[..., K]`` (K % 32 == 0) decodes to.
     Per 32-element block: shared exponent s = floor(log2 amax) - 8 (E4M3's
     largest exponent), clamped to the E8M0 range [-126, 127]; elements are
-    v / 2**s rounded to E4M3 (saturating at +-448); an all-zero block stays 0."""
+    v / 2**s rounded to E4M3 (saturating at +-448); an all-zero block stays 0.
+    A NaN element stays NaN and takes no part in amax (the pages say nothing
+    of NaN; this keeps it visible in the outputs it reaches).  Infinite
+    elements are outside the domain."""
     v = np.asarray(v, dtype=np.float64)
     K = v.shape[-1]
     assert K % 32 == 0, "MXFP8 rows must hold whole 32-element blocks"
     b = v.reshape(*v.shape[:-1], K // 32, 32)
-    amax = np.abs(b).max(axis=-1)
+    amax = np.where(np.isnan(b), 0.0, np.abs(b)).max(axis=-1)
     s = np.floor(np.log2(np.where(amax > 0, amax, 1.0))) - 8
     s = np.clip(s, -126, 127)
     scale = np.ldexp(1.0, s.astype(np.int64))[..., None]

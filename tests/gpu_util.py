@@ -4,6 +4,8 @@ from ``oracle/`` applied to the exact bytes the device consumed."""
 
 from __future__ import annotations
 
+import concurrent.futures as cf
+import json
 import os
 import sys
 
@@ -24,7 +26,8 @@ def log(msg: str):
 def require_gpu():
     if not torch.cuda.is_available():
         raise RuntimeError("GPU test run without a visible GPU")
-    import expert_ffn_layer_softmax_amd  # noqa: F401  (raises if the library is missing)
+    import expert_ffn_layer_softmax_amd
+    expert_ffn_layer_softmax_amd.load()  # raises if the library is missing
 
 
 def to_host_act(t: torch.Tensor) -> np.ndarray:
@@ -53,6 +56,95 @@ def rel_l2(got: np.ndarray, ref: np.ndarray) -> float:
     num = np.linalg.norm((got - ref).ravel())
     den = np.linalg.norm(ref.ravel())
     return float(num / den) if den > 0 else float(num)
+
+
+def token_rel_l2(got: np.ndarray, ref: np.ndarray) -> np.ndarray:
+    """Relative L2 error of each token's output row ([T, d] -> [T])."""
+    num = np.linalg.norm(got - ref, axis=1)
+    den = np.linalg.norm(ref, axis=1)
+    return np.where(den > 0, num / np.where(den > 0, den, 1.0), num)
+
+
+def record(case: str, **fields):
+    """Append one parity measurement to $MOE_PARITY_LOG (JSON lines), if set."""
+    path = os.environ.get("MOE_PARITY_LOG")
+    if not path:
+        return
+    os.makedirs(os.path.dirname(os.path.abspath(path)), exist_ok=True)
+    with open(path, "a") as fh:
+        fh.write(json.dumps(dict(case=case, **fields)) + "\n")
+
+
+def check_out(case: str, got: np.ndarray, ref: np.ndarray, tol: float, tokens=None) -> float:
+    """Layer output parity: the relative L2 error over the whole [T, d] output
+    AND that of every single token's row must be within `tol`.  Logs and
+    records both; returns the global error."""
+    err = rel_l2(got, ref)
+    per = token_rel_l2(got, ref)
+    worst = float(per.max()) if per.size else 0.0
+    wt = int(np.argmax(per)) if per.size else -1
+    if tokens is not None and wt >= 0:
+        wt = int(np.asarray(tokens)[wt])
+    log(f"  {case}: rel_l2={err:.3e} worst token={worst:.3e} (token {wt}, {per.size} tokens) tol={tol:.0e}")
+    record(case, rel_l2=err, worst_token=worst, worst_token_index=wt, tokens=int(per.size), tol=tol)
+    assert err <= tol, f"{case}: relative L2 {err:.3e} > {tol:.0e}"
+    assert worst <= tol, f"{case}: token {wt} relative L2 {worst:.3e} > {tol:.0e}"
+    return err
+
+
+class PrefetchGetter:
+    """The oracle's expert getter with decoding done ahead, on host threads.
+
+    ``oracle.layer`` asks for experts in ascending order (only those with
+    routed rows); this decodes up to `window` of the next ones in parallel
+    with what the oracle is computing.  The decode itself is the oracle's."""
+
+    def __init__(self, get, experts, workers: int = 8, window: int = 12):
+        self._get = get
+        self._order = list(experts)
+        self._pool = cf.ThreadPoolExecutor(workers)
+        self._fut = {}
+        self._next = 0
+        self._window = window
+        self._fill()
+
+    def _fill(self):
+        while self._next < len(self._order) and len(self._fut) < self._window:
+            e = self._order[self._next]
+            self._fut[e] = self._pool.submit(self._get, e)
+            self._next += 1
+
+    def __call__(self, e):
+        fut = self._fut.pop(e, None)
+        val = fut.result() if fut is not None else self._get(e)
+        self._fill()
+        return val
+
+    def close(self):
+        self._pool.shutdown(wait=True, cancel_futures=True)
+
+
+def stratified_tokens(topk_idx: np.ndarray, E: int, bm: int = 128, extra: int = 8, seed: int = 7):
+    """Tokens that own the rows at every edge of the grouped GEMM's row
+    tiling: the first and last row of every expert's segment (so every
+    expert's last, ragged m-tile) and the rows either side of each m-tile
+    boundary inside a segment, plus `extra` random tokens.  Each sampled
+    token's whole output row (all d columns, so every column-tile edge of the
+    down projection) is compared."""
+    T, k = topk_idx.shape
+    _, offsets, sorted_src, _ = oracle.permute(topk_idx, E)
+    rows = []
+    for e in range(E):
+        r0, r1 = int(offsets[e]), int(offsets[e + 1])
+        if r1 == r0:
+            continue
+        rows += [r0, r1 - 1]
+        for b in range(r0 + bm, r1, bm):
+            rows += [b - 1, b]
+    toks = set((sorted_src[np.asarray(rows)] // k).tolist())
+    rng = np.random.default_rng(seed)
+    toks |= set(rng.choice(T, min(extra, T), replace=False).tolist())
+    return np.array(sorted(toks))
 
 
 def make_inputs(wl: Workload, device="cuda", weights=None, logit_set=0):

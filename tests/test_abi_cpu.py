@@ -17,6 +17,7 @@ OK, INVALID, UNSUPPORTED, WS_SMALL = 0, 1, 2, 3
 @pytest.fixture(scope="module")
 def m():
     import expert_ffn_layer_softmax_amd as mod
+    mod.load()
     return mod
 
 
@@ -172,3 +173,15 @@ def test_status_strings(m):
 def test_timing_query_validation(m):
     assert m.lib.moe_timing_query(None, None, None) == INVALID
     assert m.lib.moe_timing_names(None, 0) == INVALID
+
+
+def test_quantize_mxfp8_validation(m):
+    L = m.lib
+    assert L.moe_quantize_mxfp8(None, 0, 64, None, None, None) == OK           # rows == 0
+    assert L.moe_quantize_mxfp8(FAKE, 4, 48, FAKE, FAKE, None) == UNSUPPORTED  # K % 32
+    assert L.moe_quantize_mxfp8(FAKE, 4, 0, FAKE, FAKE, None) == INVALID
+    assert L.moe_quantize_mxfp8(FAKE, -1, 64, FAKE, FAKE, None) == INVALID
+    assert L.moe_quantize_mxfp8(FAKE, 4, 64, None, FAKE, None) == INVALID
+    assert L.moe_quantize_mxfp8(MISALIGNED, 4, 64, FAKE, FAKE, None) == INVALID
+    assert L.moe_quantize_mxfp8(FAKE, 4, 64, MISALIGNED, FAKE, None) == INVALID
+    assert L.moe_quantize_mxfp8(FAKE, 1 << 40, 64, FAKE, FAKE, None) == UNSUPPORTED

@@ -2,9 +2,12 @@
 
 Routing (indices, counts, offsets, sorted_src, dest_row) must match bit for
 bit given the device's own fp32 logits; routing weights to 1e-5 relative;
-layer outputs to relative L2 <= 1e-5 (fp32), 5e-3 (bf16) and 2e-2 (MX-FP4
-weights).  Shapes span several tiles with ragged tails; full-size decode and
-verify workloads run in the launch configuration the bench times.
+layer outputs to relative L2 <= 1e-5 (fp32), 5e-3 (bf16) and 2e-2 (4-bit
+weights), both over the whole output and for every token's row on its own.
+Shapes span several tiles with ragged tails; full-size decode and verify
+workloads run in the launch configuration the bench times, and full-size
+prefill is checked on every token that owns a row at an edge of the grouped
+GEMM's row tiling.
 """
 
 import zlib
@@ -14,8 +17,9 @@ import pytest
 import torch
 
 import oracle
-from gpu_util import (ACT_TOL, MXFP4_TOL, check_routing, expert_getter, log, make_inputs,
-                      rel_l2, require_gpu, run_layer_and_oracle, to_host_act)
+from gpu_util import (ACT_TOL, MXFP4_TOL, PrefetchGetter, check_out, check_routing, expert_getter,
+                      log, make_inputs, record, rel_l2, require_gpu, run_layer_and_oracle,
+                      stratified_tokens, to_host_act, token_rel_l2)
 from synth import WORKLOADS, Workload, gen_expert_weights
 
 pytestmark = pytest.mark.gpu
@@ -156,9 +160,7 @@ def test_layer_small(case):
                   x_std=1.0, wg_std=d ** -0.5, wu_std=d ** -0.5, wd_std=f ** -0.5)
     x, w, w_r, logits = make_inputs(wl)
     got, ref, _ = run_layer_and_oracle(wl, x, w, w_r, logits)
-    err = rel_l2(got, ref["out"])
-    log(f"  rel_l2={err:.3e}")
-    assert err <= _tol(wl)
+    check_out(name, got, ref["out"], _tol(wl))
 
 
 @pytest.mark.parametrize("name", ["tiny_fp32", "tiny_fp32_stress"])
@@ -167,9 +169,34 @@ def test_layer_tiny_fp32_with_router(name):
     log(f"layer {name}")
     x, w, w_r, logits = make_inputs(wl)
     got, ref, _ = run_layer_and_oracle(wl, x, w, w_r, logits)
-    err = rel_l2(got, ref["out"])
-    log(f"  rel_l2={err:.3e}")
-    assert err <= 1e-5
+    check_out(name, got, ref["out"], 1e-5)
+
+
+# bf16 layers with the router GEMV in the path: logits within 1e-5 of the
+# oracle's, routing bit-exact on the device's own logits
+ROUTER_BF16 = [
+    # name, T, d, E, k, f
+    ("router_bf16_t1", 1, 6144, 256, 8, 256),      # the real router shape, single token
+    ("router_bf16_t16", 16, 6144, 256, 8, 256),
+    ("router_bf16_t37", 37, 512, 64, 8, 256),
+    ("router_bf16_t300", 300, 320, 24, 6, 128),    # grouped GEMM path
+]
+
+
+@pytest.mark.parametrize("case", ROUTER_BF16, ids=[c[0] for c in ROUTER_BF16])
+def test_layer_bf16_router(case):
+    name, T, d, E, k, f = case
+    log(f"layer {name}")
+    wl = Workload(name, T=T, d=d, E=E, k=k, f=f, act="bf16", wfmt="bf16", router=True,
+                  seed=zlib.crc32(name.encode()) % 100000,
+                  x_std=1.0, wg_std=d ** -0.5, wu_std=d ** -0.5, wd_std=f ** -0.5)
+    x, w, w_r, logits = make_inputs(wl)
+    assert w_r is not None and w_r.dtype == torch.bfloat16 and logits is None
+    got, ref, res = run_layer_and_oracle(wl, x, w, w_r, logits)
+    lg = res["logits"].cpu().numpy().astype(np.float64)
+    lerr = rel_l2(lg, oracle.router_logits(to_host_act(x), to_host_act(w_r)))
+    record(name + ":logits", rel_l2=lerr, tol=1e-5)
+    check_out(name, got, ref["out"], 5e-3)
 
 
 def test_layer_k_equals_E_uniform_is_dense_mixture():
@@ -183,7 +210,7 @@ def test_layer_k_equals_E_uniform_is_dense_mixture():
     xh = to_host_act(x)
     get = expert_getter(w, "f32")
     dense = sum(oracle.swiglu_expert(xh, *get(e)) for e in range(8)) / 8
-    assert rel_l2(to_host_act(res["out"]), dense) <= 1e-5
+    check_out("dense_mix", to_host_act(res["out"]), dense, 1e-5)
 
 
 def test_determinism_and_t0():
@@ -257,12 +284,11 @@ def test_layer_fp8_activations(case):
                   x_std=1.0, wg_std=d ** -0.5, wu_std=d ** -0.5, wd_std=f ** -0.5)
     x, w, w_r, logits = make_inputs(wl)
     got, ref, _ = run_layer_and_oracle(wl, x, w, w_r, logits, fp8=True)
-    err = rel_l2(got, ref["out"])
+    check_out(name, got, ref["out"], 5e-3)
     # the FP8 rounding is real: the bf16-activation result differs by about 2-4 %
     plain = oracle.layer(to_host_act(x), logits.cpu().numpy(), k, expert_getter(w, "mxfp4"), E=E)
     sep = rel_l2(plain["out"], ref["out"])
-    log(f"  rel_l2={err:.3e} (bf16-activation reference differs by {sep:.3e})")
-    assert err <= 5e-3
+    log(f"  bf16-activation reference differs by {sep:.3e}")
     assert sep > 5e-3
 
 
@@ -300,10 +326,10 @@ def test_layer_expert_norm(case):
     get = expert_getter(w, wfmt)
     ref = oracle.layer(to_host_act(x), lg, k, get, E=E, act_quant=aq, expert_norm=True)
     plain = oracle.layer(to_host_act(x), lg, k, get, E=E, act_quant=aq)
-    err = rel_l2(to_host_act(res["out"]), ref["out"])
+    check_out(name, to_host_act(res["out"]), ref["out"],
+              1e-5 if act == "f32" else 5e-3 if wfmt == "bf16" or fp8 else _tol(wl))
     sep = rel_l2(plain["out"], ref["out"])
-    log(f"  rel_l2={err:.3e} (unnormalised reference differs by {sep:.3e})")
-    assert err <= (1e-5 if act == "f32" else 5e-3 if wfmt == "bf16" or fp8 else _tol(wl))
+    log(f"  unnormalised reference differs by {sep:.3e}")
     assert sep > 0.1
 
 
@@ -382,9 +408,7 @@ def test_routing_and_shape_extremes(case):
     if mode == "hot":
         assert set(np.unique(res["topk_idx"].cpu().numpy()).tolist()) == set(hot.cpu().tolist())
     ref = oracle.layer(to_host_act(x), lg, k, expert_getter(w, wfmt), E=E)
-    err = rel_l2(to_host_act(res["out"]), ref["out"])
-    log(f"  rel_l2={err:.3e}")
-    assert err <= (5e-3 if wfmt == "bf16" else MXFP4_TOL)
+    check_out(name, to_host_act(res["out"]), ref["out"], 5e-3 if wfmt == "bf16" else MXFP4_TOL)
 
 
 @pytest.mark.parametrize("T", [1, 64])
@@ -407,8 +431,8 @@ def test_mx_nan_scale_propagates(T):
     got = to_host_act(res["out"])
     assert np.array_equal(np.isnan(got), np.isnan(ref))
     assert np.isnan(ref[:, 7]).all() and not np.isnan(np.delete(ref, 7, axis=1)).any()
-    keep = ~np.isnan(ref)
-    assert rel_l2(got[keep], ref[keep]) <= MXFP4_TOL
+    cols = ~np.isnan(ref).any(axis=0)
+    check_out(f"mx_nan_t{T}", got[:, cols], ref[:, cols], MXFP4_TOL)
 
 
 # ------------------------------------------------------------ HIP graphs
@@ -474,7 +498,7 @@ def test_stagewise_entry_points(wfmt, T):
     xh = to_host_act(x)
     ry = oracle.expert_ffn(xh, ro, rs, wl.k, expert_getter(w, wfmt))
     yh = y.cpu().numpy().astype(np.float64)
-    assert rel_l2(yh, ry) <= _tol(wl)
+    check_out(f"stages_{wfmt}_T{T}:y_sorted", yh, ry, _tol(wl))   # every row of y_sorted
     # combine alone: fp32 sum of the device's own y_sorted, rounded once
     twh = tw.cpu().numpy().astype(np.float64)
     rout = oracle.combine(yh, rd, twh)
@@ -506,9 +530,7 @@ def test_decode_bf16_full(full_bf16_weights, logit_set):
     log(f"decode_bf16 full, logit set {logit_set}")
     x, w, w_r, logits = make_inputs(wl, weights=full_bf16_weights, logit_set=logit_set)
     got, ref, _ = run_layer_and_oracle(wl, x, w, w_r, logits)
-    err = rel_l2(got, ref["out"])
-    log(f"  rel_l2={err:.3e}")
-    assert err <= 5e-3
+    check_out(f"decode_bf16_full_set{logit_set}", got, ref["out"], 5e-3)
 
 
 def test_verify_bf16_full(full_bf16_weights):
@@ -516,53 +538,62 @@ def test_verify_bf16_full(full_bf16_weights):
     log("verify_bf16 full (T=16)")
     x, w, w_r, logits = make_inputs(wl, weights=full_bf16_weights, logit_set=5)
     got, ref, _ = run_layer_and_oracle(wl, x, w, w_r, logits)
-    err = rel_l2(got, ref["out"])
-    log(f"  rel_l2={err:.3e} unique experts={int((ref['counts'] > 0).sum())}")
-    assert err <= 5e-3
+    log(f"  unique experts={int((ref['counts'] > 0).sum())}")
+    check_out("verify_bf16_full", got, ref["out"], 5e-3)
+
+
+def _oracle_on_tokens(x, lg, k, w, wfmt, E, S, act_quant=None, expert_norm=False):
+    """oracle.layer on the tokens S (the layer is per-token independent), with
+    the experts those tokens use decoded ahead on host threads."""
+    idx, _ = oracle.route(lg[S], k)
+    get = PrefetchGetter(expert_getter(w, wfmt), sorted(set(idx.ravel().tolist())))
+    try:
+        return oracle.layer(to_host_act(x)[S], lg[S], k, get, E=E, act_quant=act_quant,
+                            expert_norm=expert_norm)
+    finally:
+        get.close()
 
 
 @pytest.mark.parametrize("name", ["prefill_bf16", "prefill_mxfp4", "prefill_nvfp4", "prefill_mxfp4_fp8"])
-def test_prefill_full_sampled(name, full_bf16_weights):
-    """T=4096 with skewed load: routing checked in full; outputs on sampled
-    tokens (each token's output depends only on its own row and logits)."""
+def test_prefill_full_stratified(name, full_bf16_weights):
+    """T=4096 with skewed load, in the bench's launch configuration: routing
+    checked in full; outputs on every token that owns the first or last row
+    of an expert's segment or a row either side of an m-tile boundary (so
+    every expert's ragged last m-tile), plus random tokens, each over all d
+    columns (every column-tile edge)."""
     fp8 = name.endswith("_fp8")
     wl = WORKLOADS[name[:-4] if fp8 else name]
-    log(f"{name} full (T=4096), sampled tokens")
+    log(f"{name} full (T=4096), stratified tokens")
     w = full_bf16_weights if wl.wfmt == "bf16" else gen_expert_weights(wl, "cuda")
     x, w, w_r, logits = make_inputs(wl, weights=w)
     from expert_ffn_layer_softmax_amd import moe_layer_forward
     res = moe_layer_forward(x, w, wl.k, logits=logits, fp8=fp8)
     torch.cuda.synchronize()
     lg = res["logits"].cpu().numpy()
-    check_routing(res, lg, wl.k, wl.E)
-    counts = np.bincount(res["topk_idx"].cpu().numpy().ravel(), minlength=wl.E)
+    idx, _ = check_routing(res, lg, wl.k, wl.E)
+    counts = np.bincount(idx.ravel(), minlength=wl.E)
     log(f"  expert load: min {counts.min()} mean {counts.mean():.0f} max {counts.max()}")
-    rng = np.random.default_rng(7)
-    # include the tokens routed to the hottest expert's last rows (ragged m-tile)
-    hot = int(np.argmax(counts))
-    hot_tokens = np.nonzero((res["topk_idx"].cpu().numpy() == hot).any(1))[0]
-    S = np.unique(np.concatenate([rng.choice(wl.T, 4, replace=False), hot_tokens[-2:]]))
-    xh = to_host_act(x)
-    ref = oracle.layer(xh[S], lg[S], wl.k, expert_getter(w, wl.wfmt), E=wl.E,
-                       act_quant=oracle.quantize_mxfp8 if fp8 else None)
+    S = stratified_tokens(idx, wl.E)
+    log(f"  {S.size} tokens cover {int((counts > 0).sum())} experts' segment edges")
+    ref = _oracle_on_tokens(x, lg, wl.k, w, wl.wfmt, wl.E, S,
+                            act_quant=oracle.quantize_mxfp8 if fp8 else None)
     got = to_host_act(res["out"])[S]
-    err = rel_l2(got, ref["out"])
-    log(f"  sampled tokens {S.tolist()}: rel_l2={err:.3e}")
-    assert err <= (MXFP4_TOL if wl.wfmt in ("mxfp4", "nvfp4") and not fp8 else 5e-3)
+    check_out(name + "_full", got, ref["out"],
+              MXFP4_TOL if wl.wfmt in ("mxfp4", "nvfp4") and not fp8 else 5e-3, tokens=S)
     if wl.wfmt != "bf16":
         del w
         torch.cuda.empty_cache()
 
 
 @pytest.mark.parametrize("wfmt", ["bf16", "mxfp4"])
-def test_prefill_tp8_shard_width_sampled(wfmt):
+def test_prefill_tp8_shard_width_stratified(wfmt):
     """One GPU's tensor-parallel share at G = 8: f = 2816/8 = 352, a K tail of
     32 in the down projection and a 96-column n-tile in gate/up, at T=4096."""
     base = WORKLOADS["prefill_bf16"]
     wl = Workload(f"prefill_{wfmt}_f352", T=base.T, d=base.d, E=base.E, k=base.k, f=352, act="bf16",
                   wfmt=wfmt, seed=base.seed + 11, logit_sets=1, bias_std=base.bias_std,
                   x_std=1.0, wg_std=base.d ** -0.5, wu_std=base.d ** -0.5, wd_std=352 ** -0.5)
-    log(f"prefill {wfmt} f=352 (T=4096), sampled tokens")
+    log(f"prefill {wfmt} f=352 (T=4096), stratified tokens")
     x, w, _, logits = make_inputs(wl)
     from expert_ffn_layer_softmax_amd import moe_layer_forward, moe_timing_query, moe_timing_start, \
         moe_timing_stop
@@ -572,12 +603,11 @@ def test_prefill_tp8_shard_width_sampled(wfmt):
     moe_timing_stop()
     assert moe_timing_query("gg_down")[0] == 1, "the grouped GEMM path must take f = 352"
     lg = res["logits"].cpu().numpy()
-    check_routing(res, lg, wl.k, wl.E)
-    S = np.random.default_rng(3).choice(wl.T, 6, replace=False)
-    ref = oracle.layer(to_host_act(x)[S], lg[S], wl.k, expert_getter(w, wfmt), E=wl.E)
-    err = rel_l2(to_host_act(res["out"])[S], ref["out"])
-    log(f"  sampled tokens {sorted(S.tolist())}: rel_l2={err:.3e}")
-    assert err <= (5e-3 if wfmt == "bf16" else MXFP4_TOL)
+    idx, _ = check_routing(res, lg, wl.k, wl.E)
+    S = stratified_tokens(idx, wl.E)
+    ref = _oracle_on_tokens(x, lg, wl.k, w, wfmt, wl.E, S)
+    check_out(wl.name, to_host_act(res["out"])[S], ref["out"], 5e-3 if wfmt == "bf16" else MXFP4_TOL,
+              tokens=S)
     del w
     torch.cuda.empty_cache()
 
@@ -590,51 +620,93 @@ def test_decode_fp4_full(name):
     for s in (0, 9):
         x, w, w_r, logits = make_inputs(wl, weights=w, logit_set=s)
         got, ref, _ = run_layer_and_oracle(wl, x, w, w_r, logits)
-        err = rel_l2(got, ref["out"])
-        log(f"  set {s}: rel_l2={err:.3e}")
-        assert err <= MXFP4_TOL
+        check_out(f"{name}_full_set{s}", got, ref["out"], MXFP4_TOL)
     del w
     torch.cuda.empty_cache()
 
 
 @pytest.mark.parametrize("name", ["decode_mxfp4", "prefill_bf16"])
-def test_ep8_share_sampled(name):
+def test_ep8_share(name):
     """One GPU's expert-parallel share at G = 8, as the bench's ep8 share times
     it: E/8 = 32 local experts, each of the T*k/8 dispatched rows routed to one
-    of them (k = 1), at the real d and f."""
+    of them (k = 1), at the real d and f; decode in full, prefill on the
+    stratified tokens."""
     import dataclasses
     base = WORKLOADS[name]
     wl = dataclasses.replace(base, E=base.E // 8, k=1, T=max(1, base.T * base.k // 8),
                              name=f"{name}_ep8_share", logit_sets=1)
     log(f"{wl.name}: T={wl.T} E={wl.E} k=1 d={wl.d} f={wl.f} {wl.wfmt}")
     x, w, w_r, logits = make_inputs(wl)
-    S = None if wl.T <= 16 else np.random.default_rng(5).choice(wl.T, 6, replace=False)
-    got, ref, res = run_layer_and_oracle(wl, x, w, w_r, logits, sample=S)
-    err = rel_l2(got, ref["out"])
-    log(f"  rel_l2={err:.3e}")
-    assert err <= _tol(wl)
+    if wl.T <= 16:
+        got, ref, res = run_layer_and_oracle(wl, x, w, w_r, logits)
+        check_out(wl.name, got, ref["out"], _tol(wl))
+    else:
+        from expert_ffn_layer_softmax_amd import moe_layer_forward
+        res = moe_layer_forward(x, w, wl.k, logits=logits)
+        torch.cuda.synchronize()
+        lg = res["logits"].cpu().numpy()
+        idx, _ = check_routing(res, lg, wl.k, wl.E)
+        S = stratified_tokens(idx, wl.E)
+        ref = _oracle_on_tokens(x, lg, wl.k, w, wl.wfmt, wl.E, S)
+        check_out(wl.name, to_host_act(res["out"])[S], ref["out"], _tol(wl), tokens=S)
     del w, res
     torch.cuda.empty_cache()
 
 
-def test_prefill_expert_norm_full_sampled(full_bf16_weights):
+def test_prefill_expert_norm_full_stratified(full_bf16_weights):
     """T=4096 with MOE_FLAG_EXPERT_NORM: the grouped GEMMs feed the
     register-resident normalising combine at the real d and k."""
     from expert_ffn_layer_softmax_amd import moe_layer_forward
     wl = WORKLOADS["prefill_bf16"]
-    log("prefill_bf16 full (T=4096) with per-expert RMS normalisation, sampled tokens")
+    log("prefill_bf16 full (T=4096) with per-expert RMS normalisation, stratified tokens")
     x, w, _, logits = make_inputs(wl, weights=full_bf16_weights)
     res = moe_layer_forward(x, w, wl.k, logits=logits, expert_norm=True)
     torch.cuda.synchronize()
     lg = res["logits"].cpu().numpy()
-    check_routing(res, lg, wl.k, wl.E)
-    S = np.random.default_rng(11).choice(wl.T, 5, replace=False)
-    get = expert_getter(w, wl.wfmt)
-    xh = to_host_act(x)[S]
-    ref = oracle.layer(xh, lg[S], wl.k, get, E=wl.E, expert_norm=True)
-    plain = oracle.layer(xh, lg[S], wl.k, get, E=wl.E)
-    err = rel_l2(to_host_act(res["out"])[S], ref["out"])
-    sep = rel_l2(plain["out"], ref["out"])
-    log(f"  sampled tokens {sorted(S.tolist())}: rel_l2={err:.3e} (unnormalised differs by {sep:.3e})")
-    assert err <= 5e-3
+    idx, _ = check_routing(res, lg, wl.k, wl.E)
+    S = stratified_tokens(idx, wl.E, extra=4)[::3]   # a third of them: two oracle passes
+    ref = _oracle_on_tokens(x, lg, wl.k, w, wl.wfmt, wl.E, S, expert_norm=True)
+    plain = oracle.combine(ref["y_sorted"], ref["dest_row"], ref["w"])
+    check_out("prefill_bf16_expert_norm_full", to_host_act(res["out"])[S], ref["out"], 5e-3, tokens=S)
+    sep = rel_l2(plain, ref["out"])
+    log(f"  unnormalised combine differs by {sep:.3e}")
     assert sep > 0.1
+
+
+# ---------------------------------------------------- MXFP8 quantisation
+@pytest.mark.parametrize("rows,K", [(1, 32), (5, 256), (4096, 6144), (333, 2816), (64, 96)])
+def test_quantize_mxfp8_bit_exact(rows, K):
+    """The FP8 path's activation quantisation is byte work: the device's E4M3
+    codes and E8M0 scales, decoded, equal oracle.quantize_mxfp8 of the same
+    bf16 input exactly (NaN where the oracle has NaN).  Inputs span 2^-30 ..
+    2^30 per block, with zero blocks, NaN elements, bf16 subnormals and values
+    on rounding ties."""
+    from expert_ffn_layer_softmax_amd import moe_quantize_mxfp8
+    g = torch.Generator().manual_seed(rows * 7 + K)
+    v = torch.randn(rows, K, generator=g)
+    # one power-of-two magnitude per 32-element block
+    v = v * torch.exp2(torch.randint(-30, 30, (rows, K // 32), generator=g).float()).repeat_interleave(32, dim=1)
+    if rows * K >= 256:
+        v.view(-1)[::97] = float("nan")
+        v[0, :32] = 0.0                                     # an all-zero block
+        v.view(-1)[5::211] = 2.0 ** -130                    # bf16 subnormals among normals
+        if K >= 64:
+            # a block whose scale is 2^0 (amax 256): 1 + 1/16 is the tie of
+            # E4M3 neighbours 1 and 1.125, 3 + 1/8 that of 3 and 3.25 (both
+            # round to the even neighbour)
+            v[-1, 32:64] = torch.tensor([256.0] + [1.0 + 1.0 / 16] * 15 + [3.0 + 1.0 / 8] * 16)
+        if rows >= 2 and K >= 64:
+            # a block of bf16 subnormals only: amax 2^-129, scale clamped to 2^-126
+            v[1, 32:64] = (torch.arange(32) - 16).float() * 2.0 ** -133
+    x = v.to(torch.bfloat16).cuda()
+    q, sc = moe_quantize_mxfp8(x)
+    torch.cuda.synchronize()
+    xh = to_host_act(x)
+    got = (oracle.decode_e4m3(q.cpu().numpy()).reshape(rows, K // 32, 32)
+           * oracle.decode_e8m0(sc.cpu().numpy())[..., None]).reshape(rows, K)
+    ref = oracle.quantize_mxfp8(xh)
+    nan_g, nan_r = np.isnan(got), np.isnan(ref)
+    assert np.array_equal(nan_g, nan_r), f"NaN positions differ ({nan_g.sum()} vs {nan_r.sum()})"
+    assert np.array_equal(got[~nan_g], ref[~nan_r]), \
+        f"{int((got[~nan_g] != ref[~nan_r]).sum())} of {got.size} quantised values differ"
+    record(f"quantize_mxfp8_{rows}x{K}", mismatches=0, values=int(got.size))

@@ -215,3 +215,32 @@ def test_swiglu_with_act_quant_reduces_on_grid_inputs(rng):
     h = (g / (1 + np.exp(-g))) * (xs @ wu.T)
     np.testing.assert_allclose(swiglu_expert(xs, wg, wu, wd, quantize_mxfp8),
                                quantize_mxfp8(h) @ wd.T, rtol=0, atol=0)
+
+
+def test_mxfp8_nan_element_stays_nan_and_leaves_the_scale(rng):
+    """A NaN element quantises to NaN, and the block's other elements are
+    quantised exactly as if it were absent: a block with a NaN in place of a
+    value no larger than its amax gives the same values elsewhere as the block
+    with that position set to zero (which cannot change amax)."""
+    v = rng.normal(size=(4, 64)) * 3.0
+    with_nan = v.copy()
+    with_nan[1, 5] = np.nan
+    with_nan[3, 40] = np.nan
+    zeroed = v.copy()
+    zeroed[1, 5] = 0.0
+    zeroed[3, 40] = 0.0
+    for r, c in ((1, 5), (3, 40)):   # the replaced value is not the block maximum
+        blk = v[r, (c // 32) * 32:(c // 32 + 1) * 32]
+        assert abs(v[r, c]) < np.abs(blk).max()
+    qn = quantize_mxfp8(with_nan)
+    qz = quantize_mxfp8(zeroed)
+    assert np.isnan(qn[1, 5]) and np.isnan(qn[3, 40])
+    assert np.isnan(qn).sum() == 2
+    keep = ~np.isnan(qn)
+    np.testing.assert_array_equal(qn[keep], qz[keep])
+    # an all-NaN block: every element NaN, the rest of the row untouched
+    allnan = v.copy()
+    allnan[0, :32] = np.nan
+    q = quantize_mxfp8(allnan)
+    assert np.isnan(q[0, :32]).all()
+    np.testing.assert_array_equal(q[0, 32:], quantize_mxfp8(v)[0, 32:])
