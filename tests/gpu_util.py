@@ -16,7 +16,24 @@ import oracle
 from synth import Workload, gen_expert_weights, gen_logits, gen_router, gen_x
 
 ACT_TOL = {"f32": 1e-5, "bf16": 5e-3}
-MXFP4_TOL = 2e-2
+# 4-bit weights: the oracle decodes exactly the bytes the kernels read, and a
+# decoded weight is exact in bf16 (MX-FP4: E2M1 x 2^s; NVFP4: E2M1 x E4M3,
+# the fp32 matrix scale applied to fp32 sums), so these paths carry the bf16
+# path's roundings (h and out to bf16, fp32 sums) and are held to its bound,
+# tighter than the 2e-2 allowed for 4-bit layers.  Measured: 2.0-2.9e-3 over
+# a whole output, at most 3.3e-3 for a single token.
+MXFP4_TOL = 5e-3
+# FP8 activations, per token: h's MX block scale and E4M3 codes are decided
+# on fp32 sums on the device and on fp64 sums in the oracle.  When a block's
+# largest |h| lies within that accumulation error of a power of two, the two
+# sides choose scales a factor 2 apart and the element at amax moves by up to
+# 1/8 (it saturates at 448 on the finer scale); a code at an E4M3 rounding
+# tie flips by one step (1/16 to 1/8 of the element).  Both are outcomes of
+# the same rule on values equal within rounding.  One such block among a
+# token's 8 x f/32 blocks moves that token's output by up to ~3e-3 (measured:
+# 5.0e-3 worst token of 562 at T=4096, 1.8e-3 over the whole output), so a
+# single token is held to 1e-2 and the whole output to 5e-3.
+FP8_TOKEN_TOL = 1e-2
 
 
 def log(msg: str):
@@ -75,20 +92,25 @@ def record(case: str, **fields):
         fh.write(json.dumps(dict(case=case, **fields)) + "\n")
 
 
-def check_out(case: str, got: np.ndarray, ref: np.ndarray, tol: float, tokens=None) -> float:
+def check_out(case: str, got: np.ndarray, ref: np.ndarray, tol: float, tokens=None,
+              token_tol: float = None) -> float:
     """Layer output parity: the relative L2 error over the whole [T, d] output
-    AND that of every single token's row must be within `tol`.  Logs and
-    records both; returns the global error."""
+    must be within `tol`, and that of every single token's row within
+    `token_tol` (default `tol`).  Logs and records both; returns the global
+    error."""
+    token_tol = tol if token_tol is None else token_tol
     err = rel_l2(got, ref)
     per = token_rel_l2(got, ref)
     worst = float(per.max()) if per.size else 0.0
     wt = int(np.argmax(per)) if per.size else -1
     if tokens is not None and wt >= 0:
         wt = int(np.asarray(tokens)[wt])
-    log(f"  {case}: rel_l2={err:.3e} worst token={worst:.3e} (token {wt}, {per.size} tokens) tol={tol:.0e}")
-    record(case, rel_l2=err, worst_token=worst, worst_token_index=wt, tokens=int(per.size), tol=tol)
+    log(f"  {case}: rel_l2={err:.3e} worst token={worst:.3e} (token {wt}, {per.size} tokens) "
+        f"tol={tol:.0e}/{token_tol:.0e}")
+    record(case, rel_l2=err, worst_token=worst, worst_token_index=wt, tokens=int(per.size), tol=tol,
+           token_tol=token_tol)
     assert err <= tol, f"{case}: relative L2 {err:.3e} > {tol:.0e}"
-    assert worst <= tol, f"{case}: token {wt} relative L2 {worst:.3e} > {tol:.0e}"
+    assert worst <= token_tol, f"{case}: token {wt} relative L2 {worst:.3e} > {token_tol:.0e}"
     return err
 
 

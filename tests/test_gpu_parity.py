@@ -2,8 +2,9 @@
 
 Routing (indices, counts, offsets, sorted_src, dest_row) must match bit for
 bit given the device's own fp32 logits; routing weights to 1e-5 relative;
-layer outputs to relative L2 <= 1e-5 (fp32), 5e-3 (bf16) and 2e-2 (4-bit
-weights), both over the whole output and for every token's row on its own.
+layer outputs to relative L2 <= 1e-5 (fp32) and 5e-3 (bf16, and 4-bit weights,
+whose decoded values are exact in bf16), both over the whole output and for
+every token's row on its own (FP8 activations: 1e-2 per token).
 Shapes span several tiles with ragged tails; full-size decode and verify
 workloads run in the launch configuration the bench times, and full-size
 prefill is checked on every token that owns a row at an edge of the grouped
@@ -17,8 +18,8 @@ import pytest
 import torch
 
 import oracle
-from gpu_util import (ACT_TOL, MXFP4_TOL, PrefetchGetter, check_out, check_routing, expert_getter,
-                      log, make_inputs, record, rel_l2, require_gpu, run_layer_and_oracle,
+from gpu_util import (ACT_TOL, FP8_TOKEN_TOL, MXFP4_TOL, PrefetchGetter, check_out, check_routing,
+                      expert_getter, log, make_inputs, record, rel_l2, require_gpu, run_layer_and_oracle,
                       stratified_tokens, to_host_act, token_rel_l2)
 from synth import WORKLOADS, Workload, gen_expert_weights
 
@@ -284,7 +285,7 @@ def test_layer_fp8_activations(case):
                   x_std=1.0, wg_std=d ** -0.5, wu_std=d ** -0.5, wd_std=f ** -0.5)
     x, w, w_r, logits = make_inputs(wl)
     got, ref, _ = run_layer_and_oracle(wl, x, w, w_r, logits, fp8=True)
-    check_out(name, got, ref["out"], 5e-3)
+    check_out(name, got, ref["out"], 5e-3, token_tol=FP8_TOKEN_TOL)
     # the FP8 rounding is real: the bf16-activation result differs by about 2-4 %
     plain = oracle.layer(to_host_act(x), logits.cpu().numpy(), k, expert_getter(w, "mxfp4"), E=E)
     sep = rel_l2(plain["out"], ref["out"])
@@ -327,7 +328,8 @@ def test_layer_expert_norm(case):
     ref = oracle.layer(to_host_act(x), lg, k, get, E=E, act_quant=aq, expert_norm=True)
     plain = oracle.layer(to_host_act(x), lg, k, get, E=E, act_quant=aq)
     check_out(name, to_host_act(res["out"]), ref["out"],
-              1e-5 if act == "f32" else 5e-3 if wfmt == "bf16" or fp8 else _tol(wl))
+              1e-5 if act == "f32" else 5e-3 if wfmt == "bf16" or fp8 else _tol(wl),
+              token_tol=FP8_TOKEN_TOL if fp8 else None)
     sep = rel_l2(plain["out"], ref["out"])
     log(f"  unnormalised reference differs by {sep:.3e}")
     assert sep > 0.1
@@ -579,7 +581,8 @@ def test_prefill_full_stratified(name, full_bf16_weights):
                             act_quant=oracle.quantize_mxfp8 if fp8 else None)
     got = to_host_act(res["out"])[S]
     check_out(name + "_full", got, ref["out"],
-              MXFP4_TOL if wl.wfmt in ("mxfp4", "nvfp4") and not fp8 else 5e-3, tokens=S)
+              MXFP4_TOL if wl.wfmt in ("mxfp4", "nvfp4") and not fp8 else 5e-3, tokens=S,
+              token_tol=FP8_TOKEN_TOL if fp8 else None)
     if wl.wfmt != "bf16":
         del w
         torch.cuda.empty_cache()
