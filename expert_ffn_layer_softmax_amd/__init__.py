@@ -21,6 +21,7 @@ from ._lib import (  # noqa: F401
     moe_combine,
     moe_expert_ffn,
     moe_layer_forward,
+    moe_layer_forward_noalloc,
     moe_permute,
     moe_quantize_mxfp8,
     moe_route,

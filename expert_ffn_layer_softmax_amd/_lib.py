@@ -50,6 +50,7 @@ _SIGS = {
     "moe_timing_names": [ctypes.c_char_p, _sz],
     "moe_last_device_error": [],
     "moe_quantize_mxfp8": [_vp, ctypes.c_int64, _i32, _vp, _vp, _vp],
+    "moe_layer_forward_noalloc": [_P(MoeDims), _vp, _vp, _vp, _P(MoeExpertWeights), _vp, _vp, _vp, _vp],
 }
 
 
@@ -330,6 +331,39 @@ def moe_quantize_mxfp8(x, q=None, scales=None):
     _check(lib.moe_quantize_mxfp8(_ptr(x), rows, K, _ptr(q), _ptr(scales), _stream(x)),
            "moe_quantize_mxfp8")
     return q, scales
+
+
+def moe_layer_forward_noalloc(x, weights: dict, k, logits=None, w_router=None, topk_idx=None,
+                              topk_w=None, out=None, fp8=False, expert_norm=False):
+    """moe_layer_forward on the library's own scratch (no workspace; the C
+    call allocates nothing).  Outputs not supplied are allocated here, by
+    torch, before the call."""
+    _need(x, "x")
+    if x.dtype not in _ACT:
+        raise TypeError("x must be float32 or bfloat16")
+    T, d = x.shape
+    wfmt = _wfmt(weights)
+    E, _, f = _wshape(weights, wfmt)
+    dev = x.device
+    if w_router is None and logits is None:
+        raise ValueError("give logits or w_router")
+    if w_router is not None:
+        _need(w_router, "w_router", x.dtype, (E, d), dev)
+        if logits is None:
+            logits = torch.empty(T, E, dtype=torch.float32, device=dev)
+    _need(logits, "logits", torch.float32, (T, E), dev)
+    topk_idx = torch.empty(T, k, dtype=torch.int32, device=dev) if topk_idx is None else topk_idx
+    topk_w = torch.empty(T, k, dtype=torch.float32, device=dev) if topk_w is None else topk_w
+    out = torch.empty(T, d, dtype=x.dtype, device=dev) if out is None else out
+    _need(topk_idx, "topk_idx", torch.int32, (T, k), dev)
+    _need(topk_w, "topk_w", torch.float32, (T, k), dev)
+    _need(out, "out", x.dtype, (T, d), dev)
+    dims = _dims(T, d, E, k, f, _ACT[x.dtype], wfmt, _flags(fp8, expert_norm))
+    w = _weights(weights, E, d, f, wfmt, dev)
+    _check(lib.moe_layer_forward_noalloc(ctypes.byref(dims), _ptr(x), _ptr(w_router), _ptr(logits),
+                                         ctypes.byref(w), _ptr(topk_idx), _ptr(topk_w), _ptr(out),
+                                         _stream(x)), "moe_layer_forward_noalloc")
+    return dict(out=out, logits=logits, topk_idx=topk_idx, topk_w=topk_w)
 
 
 def moe_timing_start():

@@ -25,7 +25,8 @@ BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libmoe_mi355x.so")
 SAN_LIB = os.path.join(PKG, "libmoe_mi355x_san.so")
 
-SOURCES = ["abi.cpp", "route.hip", "permute.hip", "gemv.hip", "combine.hip", "grouped_gemm.hip"]
+SOURCES = ["abi.cpp", "route.hip", "permute.hip", "gemv.hip", "combine.hip", "grouped_gemm.hip",
+           "scratch.hip"]
 
 ARCH = "gfx950"
 # host-only sanitizers: each flag applies to the host compilation pass alone

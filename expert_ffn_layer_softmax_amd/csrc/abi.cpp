@@ -187,6 +187,64 @@ hipError_t run_expert_ffn(const Dims& dm, const void* x, const Plan& p, const We
   return launch_gemv_down(dm, h, p, w, y_sorted, s);
 }
 
+// Validation shared by the whole-layer entry points (all but the workspace).
+moe_status_t check_layer_args(const moe_dims_t* dims, const void* x, const void* w_router,
+                              const float* logits, const moe_expert_weights_t* weights,
+                              const int32_t* topk_idx, const float* topk_w, const void* out, Dims* dm,
+                              Weights* w) {
+  moe_status_t st = check_dims(dims, dm);
+  if (st != MOE_OK) return st;
+  if (dm->T == 0) return MOE_OK;
+  if ((st = check_weights(weights, *dm, w)) != MOE_OK) return st;
+  if (!x || !logits || !topk_idx || !topk_w || !out) return MOE_ERR_INVALID_ARGUMENT;
+  if (!aligned16(x) || !aligned16(logits) || !aligned16(topk_idx) || !aligned16(topk_w) ||
+      !aligned16(out) || (w_router && !aligned16(w_router)))
+    return MOE_ERR_INVALID_ARGUMENT;
+  return MOE_OK;
+}
+
+// The whole layer on a validated call and a workspace of L.total bytes.
+hipError_t run_layer(const Dims& dm, const Weights& w, const void* x, const void* w_router, float* logits,
+                     int32_t* topk_idx, float* topk_w, void* out, char* ws, const WsLayout& L,
+                     hipStream_t s) {
+  Plan p = plan_at(ws, L);
+  void* h = ws + L.h;
+  float* y_sorted = reinterpret_cast<float*>(ws + L.y_sorted);
+
+  hipError_t e = hipSuccess;
+  if (w_router) e = launch_router_logits(x, w_router, logits, dm.T, dm.d, dm.E, dm.act, s);
+  if (!dm.fp8 && gemv_down_combine_t1_ok(dm)) {
+    // single token: one-wave route+plan, gate/up GEMV (4-bit: one kernel for
+    // both), down GEMV + combine (fused unless the expert outputs are
+    // normalised first)
+    if (gemv_gate_up_t1_routed_ok(dm)) {
+      if (e == hipSuccess)
+        e = launch_gemv_gate_up_t1_routed(dm, logits, x, p, w, h, topk_idx, topk_w, s);
+    } else {
+      if (e == hipSuccess) e = launch_route_plan_t1(logits, dm.E, dm.k, topk_idx, topk_w, p, s);
+      if (e == hipSuccess) e = launch_gemv_gate_up(dm, x, p, w, h, s);
+    }
+    if (!dm.expert_norm) {
+      if (e == hipSuccess)
+        e = launch_gemv_down_combine_t1(dm, h, p, topk_idx, topk_w, w, out, s);
+    } else {
+      if (e == hipSuccess) e = launch_gemv_down(dm, h, p, w, y_sorted, s);
+      if (e == hipSuccess) e = launch_combine(dm, y_sorted, p.dest_row, topk_w, out, s);
+    }
+    return e;
+  }
+  if (dm.T <= kDecodeMaxT) {
+    if (e == hipSuccess)
+      e = launch_route_permute_small(logits, dm.T, dm.E, dm.k, topk_idx, topk_w, p, s);
+  } else {
+    if (e == hipSuccess) e = launch_route_topk(logits, dm.T, dm.E, dm.k, topk_idx, topk_w, s);
+    if (e == hipSuccess) e = launch_permute(topk_idx, dm.T, dm.E, dm.k, p, true, s);
+  }
+  if (e == hipSuccess) e = run_expert_ffn(dm, x, p, w, ws, L, y_sorted, s);
+  if (e == hipSuccess) e = launch_combine(dm, y_sorted, p.dest_row, topk_w, out, s);
+  return e;
+}
+
 }  // namespace
 }  // namespace moe
 
@@ -271,56 +329,32 @@ moe_status_t moe_layer_forward(const moe_dims_t* dims, const void* x, const void
                                int32_t* topk_idx, float* topk_w, void* out, void* workspace,
                                size_t workspace_bytes, moe_stream_t stream) {
   Dims dm;
-  moe_status_t st = check_dims(dims, &dm);
-  if (st != MOE_OK) return st;
-  if (dm.T == 0) return MOE_OK;
   Weights w;
-  if ((st = check_weights(weights, dm, &w)) != MOE_OK) return st;
-  if (!x || !logits || !topk_idx || !topk_w || !out || !workspace) return MOE_ERR_INVALID_ARGUMENT;
-  if (!aligned16(x) || !aligned16(logits) || !aligned16(topk_idx) || !aligned16(topk_w) ||
-      !aligned16(out) || (w_router && !aligned16(w_router)) ||
-      (reinterpret_cast<uintptr_t>(workspace) % kAlign) != 0)
+  moe_status_t st = check_layer_args(dims, x, w_router, logits, weights, topk_idx, topk_w, out, &dm, &w);
+  if (st != MOE_OK || dm.T == 0) return st;
+  if (!workspace || (reinterpret_cast<uintptr_t>(workspace) % kAlign) != 0)
     return MOE_ERR_INVALID_ARGUMENT;
   const WsLayout L = ws_layout(dm);
   if (workspace_bytes < L.total) return MOE_ERR_WORKSPACE_TOO_SMALL;
-  hipStream_t s = (hipStream_t)stream;
-  Plan p = plan_at(workspace, L);
-  char* ws = static_cast<char*>(workspace);
-  void* h = ws + L.h;
-  float* y_sorted = reinterpret_cast<float*>(ws + L.y_sorted);
+  return device_status(run_layer(dm, w, x, w_router, logits, topk_idx, topk_w, out,
+                                 static_cast<char*>(workspace), L, (hipStream_t)stream));
+}
 
-  hipError_t e = hipSuccess;
-  if (w_router) e = launch_router_logits(x, w_router, logits, dm.T, dm.d, dm.E, dm.act, s);
-  if (!dm.fp8 && gemv_down_combine_t1_ok(dm)) {
-    // single token: one-wave route+plan, gate/up GEMV (4-bit: one kernel for
-    // both), down GEMV + combine (fused unless the expert outputs are
-    // normalised first)
-    if (gemv_gate_up_t1_routed_ok(dm)) {
-      if (e == hipSuccess)
-        e = launch_gemv_gate_up_t1_routed(dm, logits, x, p, w, h, topk_idx, topk_w, s);
-    } else {
-      if (e == hipSuccess) e = launch_route_plan_t1(logits, dm.E, dm.k, topk_idx, topk_w, p, s);
-      if (e == hipSuccess) e = launch_gemv_gate_up(dm, x, p, w, h, s);
-    }
-    if (!dm.expert_norm) {
-      if (e == hipSuccess)
-        e = launch_gemv_down_combine_t1(dm, h, p, topk_idx, topk_w, w, out, s);
-    } else {
-      if (e == hipSuccess) e = launch_gemv_down(dm, h, p, w, y_sorted, s);
-      if (e == hipSuccess) e = launch_combine(dm, y_sorted, p.dest_row, topk_w, out, s);
-    }
-    return device_status(e);
-  }
-  if (dm.T <= kDecodeMaxT) {
-    if (e == hipSuccess)
-      e = launch_route_permute_small(logits, dm.T, dm.E, dm.k, topk_idx, topk_w, p, s);
-  } else {
-    if (e == hipSuccess) e = launch_route_topk(logits, dm.T, dm.E, dm.k, topk_idx, topk_w, s);
-    if (e == hipSuccess) e = launch_permute(topk_idx, dm.T, dm.E, dm.k, p, true, s);
-  }
-  if (e == hipSuccess) e = run_expert_ffn(dm, x, p, w, ws, L, y_sorted, s);
-  if (e == hipSuccess) e = launch_combine(dm, y_sorted, p.dest_row, topk_w, out, s);
-  return device_status(e);
+moe_status_t moe_layer_forward_noalloc(const moe_dims_t* dims, const void* x, const void* w_router,
+                                       float* logits, const moe_expert_weights_t* weights,
+                                       int32_t* topk_idx, float* topk_w, void* out,
+                                       moe_stream_t stream) {
+  Dims dm;
+  Weights w;
+  moe_status_t st = check_layer_args(dims, x, w_router, logits, weights, topk_idx, topk_w, out, &dm, &w);
+  if (st != MOE_OK || dm.T == 0) return st;
+  const WsLayout L = ws_layout(dm);
+  if (L.total > kScratchBytes) return MOE_ERR_WORKSPACE_TOO_SMALL;
+  void* scratch = nullptr;
+  hipError_t e = scratch_for_current_device(&scratch);
+  if (e != hipSuccess) return device_status(e);
+  return device_status(run_layer(dm, w, x, w_router, logits, topk_idx, topk_w, out,
+                                 static_cast<char*>(scratch), L, (hipStream_t)stream));
 }
 
 moe_status_t moe_quantize_mxfp8(const void* x, int64_t rows, int32_t K, uint8_t* q,

@@ -68,6 +68,11 @@ struct Plan {
   int* num_mtiles;  // [1]
 };
 
+// Library-owned scratch (scratch.hip) for moe_layer_forward_noalloc: its
+// size, and the current device's copy, looked up on the first call per device.
+constexpr size_t kScratchBytes = size_t(64) << 20;
+hipError_t scratch_for_current_device(void** ptr);
+
 // Per-kernel event timing (abi.cpp).  Bracket every launch with it.
 struct LaunchTimer {
   LaunchTimer(const char* name, hipStream_t s);

@@ -212,6 +212,24 @@ moe_status_t moe_layer_forward(const moe_dims_t* dims, const void* x, const void
                                int32_t* topk_idx, float* topk_w, void* out, void* workspace,
                                size_t workspace_bytes, moe_stream_t stream);
 
+/* moe_layer_forward for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): the same computation and kernels, with no workspace argument.
+ * Its scratch is a device array owned by the library, 64 MiB per GPU
+ * (moe_workspace_size(dims) must not exceed 67108864 bytes, else
+ * MOE_ERR_WORKSPACE_TOO_SMALL, returned before any device work: enough for
+ * single-token decode and small batches at d = 6144, E = 256, k = 8,
+ * f = 2816, i.e. T <= 277, not for long prefill).  Each GPU holds its copy
+ * until the process ends; the first call on a device looks it up with that
+ * device current.  Every call on one GPU uses the same scratch, so calls that
+ * overlap on one GPU (several host threads, or several streams whose work
+ * overlaps) race; calls on one stream are ordered and safe.  Allocates
+ * nothing, on the host or the device. */
+moe_status_t moe_layer_forward_noalloc(const moe_dims_t* dims, const void* x, const void* w_router,
+                                       float* logits, const moe_expert_weights_t* weights,
+                                       int32_t* topk_idx, float* topk_w, void* out,
+                                       moe_stream_t stream);
+
 /* MXFP8 quantisation of bf16 activations, the first step of the FP8-compute
  * path (MOE_FLAG_FP8_ACTIVATIONS; "FP8 compute" with 4-bit expert weights:
  * SGLang-TorchTPU on TPU v7 page, "Results").  For each run of 32

@@ -185,3 +185,22 @@ def test_quantize_mxfp8_validation(m):
     assert L.moe_quantize_mxfp8(MISALIGNED, 4, 64, FAKE, FAKE, None) == INVALID
     assert L.moe_quantize_mxfp8(FAKE, 4, 64, MISALIGNED, FAKE, None) == INVALID
     assert L.moe_quantize_mxfp8(FAKE, 1 << 40, 64, FAKE, FAKE, None) == UNSUPPORTED
+
+
+def test_layer_forward_noalloc_validation(m):
+    """The allocation-free entry point validates as moe_layer_forward does and
+    rejects shapes whose workspace exceeds its 64 MiB scratch, all before any
+    device call."""
+    L = m.lib
+    args = lambda d, w: (ctypes.byref(d), FAKE, None, FAKE, ctypes.byref(w), FAKE, FAKE, FAKE, None)
+    assert L.moe_layer_forward_noalloc(*args(_dims(m, T=0), _w(m))) == OK
+    assert L.moe_layer_forward_noalloc(*args(_dims(m, d=40), _w(m))) == UNSUPPORTED
+    assert L.moe_layer_forward_noalloc(*args(_dims(m), _w(m, bad=(1, None)))) == INVALID
+    assert L.moe_layer_forward_noalloc(*args(_dims(m), _w(m, mx=True))) == INVALID
+    assert L.moe_layer_forward_noalloc(None, None, None, None, None, None, None, None, None) == INVALID
+    big = _dims(m, T=278, d=6144, E=256, k=8, f=2816)
+    fits = _dims(m, T=277, d=6144, E=256, k=8, f=2816)
+    assert _ws(m, fits)[1] <= 64 << 20 < _ws(m, big)[1]
+    assert L.moe_layer_forward_noalloc(*args(big, _w(m))) == WS_SMALL
+    prefill = _dims(m, T=4096, d=6144, E=256, k=8, f=2816)
+    assert L.moe_layer_forward_noalloc(*args(prefill, _w(m))) == WS_SMALL
