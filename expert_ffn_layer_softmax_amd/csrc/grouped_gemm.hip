@@ -610,16 +610,26 @@ __global__ __launch_bounds__(kThreads) void gg_dma_kernel(GGArgs a) {
 // operands per wave, wave-local SwiGLU); codes are converted to bf16 (scale
 // applied by the instruction) just before their MFMAs.
 //
-// Per step the loads are issued codes, [scales,] activations, so the
-// activation DMAs of a step are its youngest loads and a step waits for the
-// activation stage issued two steps earlier by counting the loads of the
-// previous step alone; groups are older still.  Requires K % 256 == 0.
+// Per step the loads are issued activations, then codes[, scales].  A wave's
+// vector loads complete in issue order, so waiting for the activation stage
+// issued two steps earlier also waits for everything issued before it; with
+// the codes issued after the activations, that never includes the code group
+// issued at the same step for use eight steps later (issued first, it would
+// have had two steps to arrive from HBM instead of eight).  Requires
+// K % 256 == 0.
 constexpr int kGroupSteps = 4;
 constexpr int kGroupBufs = 3;
 constexpr int kCodesGroup = BN * 128;                 // 32 KB: 256 weight rows x one line
 constexpr int kMx4A = 3;                              // activation stages
 constexpr int kCodeDmaPerStep = kCodesGroup / (kWave * 16) / kWaves / kGroupSteps;  // 1
 static_assert(kCodeDmaPerStep == 1, "one code DMA per wave per step");
+
+// 16-byte unit u of 128-byte code row r (four K-steps of one weight row)
+// lives at unit u ^ c(r), c(r) = (r >> 1) & 7: a fragment read of 8 or 16
+// consecutive rows at one unit then touches distinct 16-byte bank groups (an
+// even and an odd row share a 256-byte bank line).
+__device__ __forceinline__ int code_swz(int r) { return (r >> 1) & 7; }
+__device__ __forceinline__ int code_off(int r, int unit) { return r * 128 + ((unit ^ code_swz(r)) << 4); }
 
 // Scale bytes per weight row per group, and the group's scale DMAs per wave.
 template <int WF>
@@ -684,7 +694,7 @@ __device__ __forceinline__ void mx4_step(const char* st, const char* cb, const c
 #pragma unroll
     for (int m = 0; m < 2; ++m) {
       const int u = 2 * p + half;  // the lane's 32-element block inside the line
-      b.v[m] = *reinterpret_cast<const u32x4*>(cb + brow[m] * 128 + ((u ^ (brow[m] & 7)) << 4));
+      b.v[m] = *reinterpret_cast<const u32x4*>(cb + code_off(brow[m], u));
       if constexpr (WF == kNVFP4) {
         const uint8_t* q = reinterpret_cast<const uint8_t*>(sb) + brow[m] * 16 + 2 * u;
         b.lo[m] = e4m3_to_f32(q[0]);
@@ -783,7 +793,7 @@ __global__ __launch_bounds__(kThreads) void gg_mx_group_kernel(GGArgs a) {
   char* const adst = lds_a + (kDmaA * 8) * wave * (BK * 2);
 
   // ---- code DMA sources: at group place p, wave w fills weight rows
-  // 32 w + 8 p + lane/8, line slot lane%8 <- global unit (lane%8) ^ (row & 7)
+  // 32 w + 8 p + lane/8, line slot lane%8 <- global unit (lane%8) ^ code_swz(row)
   const char* csrc[kGroupSteps];
 #pragma unroll
   for (int p = 0; p < kGroupSteps; ++p) {
@@ -791,7 +801,7 @@ __global__ __launch_bounds__(kThreads) void gg_mx_group_kernel(GGArgs a) {
     const char* code;
     const uint8_t* scale;
     wrow(r, code, scale);
-    csrc[p] = code + ((slot16 ^ (r & 7)) << 4);
+    csrc[p] = code + ((slot16 ^ code_swz(r)) << 4);
   }
   // ---- scale DMA sources: dword d = 64 (kDmas w + i) + lane of the group
   // covers weight row d / W, bytes 4 (d % W) .. +3 of the row's group bytes
@@ -870,19 +880,31 @@ __global__ __launch_bounds__(kThreads) void gg_mx_group_kernel(GGArgs a) {
       auto step = [&](auto p_c) {
         constexpr int p = decltype(p_c)::value;
         const int kk = kGroupSteps * g + p;
-        // loads younger than activation stage kk: those of step kk-1 (three,
-        // three plus the scale DMAs after a group's first step); at step 0
-        // only stage 1's two
-        if constexpr (p == 1)
-          wait_and_barrier<3 + GS::kDmas>();
-        else if constexpr (p == 0)
-          wait_and_barrier<2>();
-        else
-          wait_and_barrier<3>();
+        // Younger than activation stage kk (issued first at step kk-2): the
+        // code DMA (and at a group's first place the scale DMAs) issued after
+        // it at step kk-2, then every load of step kk-1.  In group 0 the
+        // prologue stands in for steps -2 and -1: only stage 1 (two DMAs),
+        // then step 0's loads.
+        constexpr int S = GS::kDmas;
+        if constexpr (p == 0) {
+          if (g == 0)
+            wait_and_barrier<2>();
+          else
+            wait_and_barrier<4>();
+        } else if constexpr (p == 1) {
+          if (g == 0)
+            wait_and_barrier<3 + S>();
+          else
+            wait_and_barrier<4 + S>();
+        } else if constexpr (p == 2) {
+          wait_and_barrier<4 + S>();
+        } else {
+          wait_and_barrier<4>();
+        }
+        issue_a(kk + 2);
+        asm volatile("" ::: "memory");  // codes and scales after the step's activations
         issue_codes(g + 2, p);
         if constexpr (p == 0) issue_scales(g + 2);
-        asm volatile("" ::: "memory");  // activation DMAs are the step's youngest loads
-        issue_a(kk + 2);
         mx4_step<WF, VM>(lds_a + ((J + p) % kMx4A) * kStageA, cb, sb, p, aoff, brow, half, acc);
       };
       step(std::integral_constant<int, 0>{});
@@ -957,7 +979,7 @@ __device__ __forceinline__ void mx4_row_step(const char* st, const char* cb, con
                                              const int* aoff, int brow, int half, f32x16_t (&acc)[4]) {
   Fp4Regs b;
   const int u = 2 * p + half;  // the lane's 32-element block inside the line
-  b.v[0] = *reinterpret_cast<const u32x4*>(cb + brow * 128 + ((u ^ (brow & 7)) << 4));
+  b.v[0] = *reinterpret_cast<const u32x4*>(cb + code_off(brow, u));
   if constexpr (WF == kNVFP4) {
     const uint8_t* q = reinterpret_cast<const uint8_t*>(sb) + brow * 16 + 2 * u;
     b.lo[0] = e4m3_to_f32(q[0]);
@@ -1057,7 +1079,7 @@ __global__ __launch_bounds__(kThreads) void gg_mx_row_kernel(GGArgs a) {
   char* const adst = lds_a + (kDmaA * 8) * wave * (BK * 2);
 
   // ---- code DMA sources: at group place p, wave w fills weight rows
-  // 32 w + 8 p + lane/8, line slot lane%8 <- global unit (lane%8) ^ (row & 7)
+  // 32 w + 8 p + lane/8, line slot lane%8 <- global unit (lane%8) ^ code_swz(row)
   const char* csrc[kGroupSteps];
 #pragma unroll
   for (int p = 0; p < kGroupSteps; ++p) {
@@ -1065,7 +1087,7 @@ __global__ __launch_bounds__(kThreads) void gg_mx_row_kernel(GGArgs a) {
     const char* code;
     const uint8_t* scale;
     wrow(r, code, scale);
-    csrc[p] = code + ((slot16 ^ (r & 7)) << 4);
+    csrc[p] = code + ((slot16 ^ code_swz(r)) << 4);
   }
   // ---- scale DMA sources: dword d = 64 (kDmas w + i) + lane of the group
   // covers weight row d / W, bytes 4 (d % W) .. +3 of the row's group bytes
@@ -1142,19 +1164,31 @@ __global__ __launch_bounds__(kThreads) void gg_mx_row_kernel(GGArgs a) {
       auto step = [&](auto p_c) {
         constexpr int p = decltype(p_c)::value;
         const int kk = kGroupSteps * g + p;
-        // loads younger than activation stage kk: those of step kk-1 (three,
-        // three plus the scale DMAs after a group's first step); at step 0
-        // only stage 1's two
-        if constexpr (p == 1)
-          wait_and_barrier<3 + GS::kDmas>();
-        else if constexpr (p == 0)
-          wait_and_barrier<2>();
-        else
-          wait_and_barrier<3>();
+        // Younger than activation stage kk (issued first at step kk-2): the
+        // code DMA (and at a group's first place the scale DMAs) issued after
+        // it at step kk-2, then every load of step kk-1.  In group 0 the
+        // prologue stands in for steps -2 and -1: only stage 1 (two DMAs),
+        // then step 0's loads.
+        constexpr int S = GS::kDmas;
+        if constexpr (p == 0) {
+          if (g == 0)
+            wait_and_barrier<2>();
+          else
+            wait_and_barrier<4>();
+        } else if constexpr (p == 1) {
+          if (g == 0)
+            wait_and_barrier<3 + S>();
+          else
+            wait_and_barrier<4 + S>();
+        } else if constexpr (p == 2) {
+          wait_and_barrier<4 + S>();
+        } else {
+          wait_and_barrier<4>();
+        }
+        issue_a(kk + 2);
+        asm volatile("" ::: "memory");  // codes and scales after the step's activations
         issue_codes(g + 2, p);
         if constexpr (p == 0) issue_scales(g + 2);
-        asm volatile("" ::: "memory");  // activation DMAs are the step's youngest loads
-        issue_a(kk + 2);
         mx4_row_step<WF, VM>(lds_a + ((J + p) % kMx4A) * kStageA, cb, sb, p, aoff, brow, half, acc);
       };
       step(std::integral_constant<int, 0>{});
@@ -1262,7 +1296,7 @@ __device__ __forceinline__ void f8_step(const char* st, const char* cb, const ch
 #pragma unroll
     for (int m = 0; m < 2; ++m) {
       const int u = 2 * p + half;  // the lane's 32-element block inside the line
-      const u32x4 c = *reinterpret_cast<const u32x4*>(cb + brow[m] * 128 + ((u ^ (brow[m] & 7)) << 4));
+      const u32x4 c = *reinterpret_cast<const u32x4*>(cb + code_off(brow[m], u));
       bv[m] = i32x8_t{(int)c.x, (int)c.y, (int)c.z, (int)c.w, 0, 0, 0, 0};
       bs[m] = static_cast<uint8_t>(sb[brow[m] * 8 + u]);
     }
@@ -1380,7 +1414,7 @@ __global__ __launch_bounds__(kThreads) void gg_f8f4_kernel(GGArgs a) {
     const char* code;
     const uint8_t* scale;
     wrow(r, code, scale);
-    csrc[p] = code + ((slot16 ^ (r & 7)) << 4);
+    csrc[p] = code + ((slot16 ^ code_swz(r)) << 4);
   }
   const uint8_t* ssrc;
   {
@@ -1430,12 +1464,15 @@ __global__ __launch_bounds__(kThreads) void gg_f8f4_kernel(GGArgs a) {
 #pragma unroll
   for (int kk = 0; kk < kF8D; ++kk) issue_a(kk);
 
-  // Loads per step: one code DMA, at a group's first step the weight- and
-  // activation-scale DMAs, then the activation DMA (youngest), for step
-  // kk + kF8D.  Younger than activation stage kk are the loads of steps
-  // kk-3 .. kk-1 (two each, four at a group's first step): 6 at a group's
-  // first step, else 8.  In group 0 the prologue's younger activation stages
-  // stand in for the steps before 0: 3, 6, 7, 8.
+  // Loads per step: the activation DMA for step kk + kF8D first, then one
+  // code DMA and, at a group's first step, the weight- and activation-scale
+  // DMAs.  Younger than activation stage kk (issued first at step kk-4) are
+  // the code and scale DMAs after it at step kk-4 and every load of steps
+  // kk-3 .. kk-1 (two each, four at a group's first step): 9 at every step
+  // (the four places of a group hold one four-load step between them).  In
+  // group 0 the prologue's younger activation stages stand in for the steps
+  // before 0: 3, 6, 7, 8.  A code group, needed eight steps after its first
+  // DMA, is thereby never waited for early.
   static_assert(kF8D == 4 && kGroupSteps == 4, "wait counts below");
   auto main_loop = [&](auto vm_c) {
     constexpr int VM = decltype(vm_c)::value;
@@ -1447,10 +1484,10 @@ __global__ __launch_bounds__(kThreads) void gg_f8f4_kernel(GGArgs a) {
         constexpr int p = decltype(p_c)::value;
         const int kk = kGroupSteps * g + p;
         wait_and_barrier<decltype(n_c)::value>();
+        issue_a(kk + kF8D);
+        asm volatile("" ::: "memory");  // codes and scales after the step's activations
         issue_codes(g + 2, p);
         if constexpr (p == 0) issue_scales(g + 2);
-        asm volatile("" ::: "memory");
-        issue_a(kk + kF8D);
         f8_step<VM>(lds_a + (kk % kF8A) * kStageA8, cb, sb, ab, p, arow, brow, half, acc);
       };
       step(std::integral_constant<int, 0>{}, n0);
@@ -1462,8 +1499,9 @@ __global__ __launch_bounds__(kThreads) void gg_f8f4_kernel(GGArgs a) {
     using C6 = std::integral_constant<int, 6>;
     using C7 = std::integral_constant<int, 7>;
     using C8 = std::integral_constant<int, 8>;
+    using C9 = std::integral_constant<int, 9>;
     if (ng > 0) group(0, C3{}, C6{}, C7{}, C8{});
-    for (int g = 1; g < ng; ++g) group(g, C6{}, C8{}, C8{}, C8{});
+    for (int g = 1; g < ng; ++g) group(g, C9{}, C9{}, C9{}, C9{});
   };
   if (vm == 2)
     main_loop(std::integral_constant<int, 2>{});
