@@ -64,7 +64,7 @@ def _parse():
                    help="chain this many layers per step, each with its own weights (out of one "
                         "layer is x of the next); tokens/s counts each token once per step")
     p.add_argument("--fp8", action="store_true",
-                   help="FP8 activations (MXFP8) on the scaled MFMA; MX-FP4 workloads only")
+                   help="FP8 activations (MXFP8); MX-FP4 (scaled FP8 MFMA) and NVFP4 (bf16 MFMA) workloads")
     p.add_argument("--expert-norm", action="store_true",
                    help="RMS-normalise each expert's output row before the combine "
                         "(MOE_FLAG_EXPERT_NORM)")
@@ -313,7 +313,10 @@ def measure(wl, ws_list, args, with_cpu: bool):
     # weights read once, x read, h written; 2 FLOPs per MAC over T*k rows
     k_bytes = mean_uniq * eb["gate_up"] + wl.T * wl.d * act_b + wl.T * k * wl.f * act_b
     k_flops = 4.0 * wl.T * k * wl.d * wl.f
-    mfma_peak = FP8_PEAK_TFLOPS if args.fp8 else BF16_PEAK_TFLOPS
+    # FP8 activations run on the scaled FP8 MFMA with MX-FP4 weights; with
+    # NVFP4 weights they are carried as bf16 values on the bf16 MFMA
+    scaled_fp8 = args.fp8 and wl.wfmt == "mxfp4"
+    mfma_peak = FP8_PEAK_TFLOPS if scaled_fp8 else BF16_PEAK_TFLOPS
     if k_flops / k_bytes > mfma_peak * 1e12 / (HBM_PEAK_GBS * 1e9):
         bound, unit, peak = "mfma", "TFLOP/s", mfma_peak
         achieved = k_flops / (kernel_us * 1e-6) / 1e12
@@ -349,7 +352,7 @@ def measure(wl, ws_list, args, with_cpu: bool):
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 5),
         "repeats": len(loops), "ms_per_step_loops": [round(v * 1e3 / args.steps, 5) for v in loops],
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-        "dtype": "fp8" if args.fp8 else ("bf16" if wl.act == "bf16" else "f32"), "data": "synthetic",
+        "dtype": "fp8" if scaled_fp8 else ("bf16" if wl.act == "bf16" else "f32"), "data": "synthetic",
         "config": cfg,
         "roofline": {"bound": bound, "kernel": kname, "achieved": round(achieved, 1),
                      "peak": peak, "unit": unit, "frac": round(achieved / peak, 4),

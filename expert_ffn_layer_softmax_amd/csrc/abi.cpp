@@ -79,13 +79,17 @@ WsLayout ws_layout(const Dims& dm) {
   L.slot_info = o;   o = align_up(o + E * 16);
   L.mtiles = o;      o = align_up(o + max_mtiles * kMtileInts * 4);
   L.num_mtiles = o;  o = align_up(o + 4);
-  L.h = o;           o = align_up(o + (dm.fp8 ? 0 : Tk * (size_t)dm.f * act));
+  // FP8 activations: with MX-FP4 weights x and h travel as MXFP8 codes and
+  // scales; with NVFP4 weights as bf16 values on the MXFP8 grid
+  const bool f8mx = dm.fp8 && dm.wfmt == kMXFP4;
+  const bool f8nv = dm.fp8 && dm.wfmt == kNVFP4;
+  L.h = o;           o = align_up(o + (f8mx ? 0 : Tk * (size_t)dm.f * act));
   L.y_sorted = o;    o = align_up(o + Tk * (size_t)dm.d * 4);
   const size_t T = (size_t)dm.T;
-  L.xq = o;          o = align_up(o + (dm.fp8 ? T * dm.d : 0));
-  L.xs = o;          o = align_up(o + (dm.fp8 ? T * dm.d / 32 : 0));
-  L.hq = o;          o = align_up(o + (dm.fp8 ? Tk * dm.f : 0));
-  L.hs = o;          o = align_up(o + (dm.fp8 ? Tk * dm.f / 32 : 0));
+  L.xq = o;          o = align_up(o + (f8mx ? T * dm.d : f8nv ? T * dm.d * 2 : 0));
+  L.xs = o;          o = align_up(o + (f8mx ? T * dm.d / 32 : 0));
+  L.hq = o;          o = align_up(o + (f8mx ? Tk * dm.f : 0));
+  L.hs = o;          o = align_up(o + (f8mx ? Tk * dm.f / 32 : 0));
   L.total = o;
   return L;
 }
@@ -166,6 +170,15 @@ moe_status_t check_weights(const moe_expert_weights_t* w, const Dims& dm, Weight
 // Expert FFN on a prepared plan (offsets, sorted_src, active list).
 hipError_t run_expert_ffn(const Dims& dm, const void* x, const Plan& p, const Weights& w,
                           char* ws, const WsLayout& L, float* y_sorted, hipStream_t s) {
+  if (dm.fp8 && dm.wfmt == kNVFP4) {
+    // x rounded to the MXFP8 grid (bf16); gate/up rounds h the same way
+    void* xq = ws + L.xq;
+    void* h = ws + L.h;
+    hipError_t e = launch_round_mxfp8(x, dm.T, dm.d, xq, s);
+    if (e == hipSuccess) e = launch_gg_gate_up(dm, xq, p, w, h, s);
+    if (e == hipSuccess) e = launch_gg_down(dm, h, p, w, y_sorted, s);
+    return e;
+  }
   if (dm.fp8) {
     uint8_t* xq = reinterpret_cast<uint8_t*>(ws + L.xq);
     uint8_t* xs = reinterpret_cast<uint8_t*>(ws + L.xs);

@@ -67,6 +67,37 @@ __device__ __forceinline__ float silu_mul(float g, float u) {
 }
 
 
+// OCP FP8 E4M3 byte of v (already divided by its block scale): round to
+// nearest even, saturating at +-448 (the convert itself would give NaN).  A
+// NaN stays NaN: the clamp would turn it into -448, so it is selected around.
+__device__ __forceinline__ uint32_t e4m3_byte(float v) {
+  const float c = fminf(fmaxf(v, -448.0f), 448.0f);
+  v = v != v ? v : c;
+  return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(v, v, 0, false) & 0xffu;
+}
+
+// E8M0 byte of a block whose largest magnitude is amax: 2^(floor(log2 amax)
+// - 8), the MX rule for E4M3 elements, kept in [1, 254].  amax is taken with
+// fmaxf, which skips NaN: a block's scale comes from its non-NaN elements.
+__device__ __forceinline__ uint32_t mxfp8_scale_byte(float amax) {
+  const int ef = (int)((__float_as_uint(amax) >> 23) & 0xffu);
+  return (uint32_t)min(max(ef - 8, 1), 254);
+}
+
+// v rounded to the MXFP8 grid of its 32-element block, as fp32: the block is
+// the 32 lanes of one half of the wave (one row, 32 consecutive columns of an
+// MFMA result), so every lane of the wave must call.  The value is
+// E4M3(code) * 2^(s - 127), which bf16 holds exactly for block scales
+// s >= 3 (smaller ones only below 2^-124).
+__device__ __forceinline__ float mxfp8_round_lanes32(float v) {
+  float amax = fabsf(v);
+#pragma unroll
+  for (int o = 1; o < 32; o <<= 1) amax = fmaxf(amax, __shfl_xor(amax, o, kWave));
+  const uint32_t sbyte = mxfp8_scale_byte(amax);
+  const float inv = __uint_as_float((254u - sbyte) << 23);  // 2^(127 - s)
+  return e4m3_to_f32(e4m3_byte(v * inv)) * __uint_as_float(sbyte << 23);
+}
+
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 
@@ -724,7 +755,10 @@ __device__ __forceinline__ void mx4_step(const char* st, const char* cb, const c
   }
 }
 
-template <int WF, bool GATEUP>
+// QH (gate/up only): h is rounded to the MXFP8 grid before it is stored (as
+// bf16), for FP8 activations with NVFP4 weights; the wave's 32 output columns
+// are one MX block along f.
+template <int WF, bool GATEUP, bool QH = false>
 __global__ __launch_bounds__(kThreads) void gg_mx_group_kernel(GGArgs a) {
   using GS = GroupScales<WF>;
   __shared__ __align__(1024) char lds[GS::kLds];
@@ -942,6 +976,25 @@ __global__ __launch_bounds__(kThreads) void gg_mx_group_kernel(GGArgs a) {
       acc[0][mi] *= t0;
       acc[1][mi] *= t1;
     }
+  }
+  if constexpr (GATEUP && QH) {
+    // every lane rounds (the block maximum is a cross-lane reduction); rows
+    // past the tile and columns past N are then not stored.  N % 32 == 0, so
+    // a block lies wholly inside or outside the matrix.
+    const int col = nbase + 32 * wn + cl;
+#pragma unroll
+    for (int mi = 0; mi < 2; ++mi) {
+      if (mi < vm) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int row = 64 * wm + 32 * mi + 8 * (i >> 2) + 4 * half + (i & 3);
+          const float h = mxfp8_round_lanes32(silu_mul(acc[0][mi][i], acc[1][mi][i]));
+          if (row < nrows && col < a.N)
+            reinterpret_cast<uint16_t*>(a.out)[(size_t)(row0 + row) * a.N + col] = f32_to_bf16(h);
+        }
+      }
+    }
+    return;
   }
 #pragma unroll
   for (int mi = 0; mi < 2; ++mi) {
@@ -1314,23 +1367,6 @@ __device__ __forceinline__ void f8_step(const char* st, const char* cb, const ch
   }
 }
 
-// OCP FP8 E4M3 byte of v (already divided by its block scale): round to
-// nearest even, saturating at +-448 (the convert itself would give NaN).  A
-// NaN stays NaN: the clamp would turn it into -448, so it is selected around.
-__device__ __forceinline__ uint32_t e4m3_byte(float v) {
-  const float c = fminf(fmaxf(v, -448.0f), 448.0f);
-  v = v != v ? v : c;
-  return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(v, v, 0, false) & 0xffu;
-}
-
-// E8M0 byte of a block whose largest magnitude is amax: 2^(floor(log2 amax)
-// - 8), the MX rule for E4M3 elements, kept in [1, 254].  amax is taken with
-// fmaxf, which skips NaN: a block's scale comes from its non-NaN elements.
-__device__ __forceinline__ uint32_t mxfp8_scale_byte(float amax) {
-  const int ef = (int)((__float_as_uint(amax) >> 23) & 0xffu);
-  return (uint32_t)min(max(ef - 8, 1), 254);
-}
-
 template <bool GATEUP>
 __global__ __launch_bounds__(kThreads) void gg_f8f4_kernel(GGArgs a) {
   __shared__ __align__(1024) char lds[kF8Lds];
@@ -1592,6 +1628,44 @@ __global__ __launch_bounds__(256) void quantize_mxfp8_kernel(const uint16_t* __r
   qs[b] = (uint8_t)sbyte;
 }
 
+// x [T][K] bf16 -> the same shape in bf16, each value rounded to the MXFP8
+// grid of its 32-element block (E4M3 code times the block's E8M0 scale, both
+// chosen as quantize_mxfp8_kernel does): the activations of the FP8 path with
+// NVFP4 weights, whose products then run on bf16 MFMA.  One thread per block.
+__global__ __launch_bounds__(256) void round_mxfp8_kernel(const uint16_t* __restrict__ x, long long nblocks,
+                                                          uint16_t* __restrict__ y) {
+  const long long b = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+  if (b >= nblocks) return;
+  const u32x4* src = reinterpret_cast<const u32x4*>(x + 32 * b);
+  float v[32];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const u32x4 w = src[j];
+    const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      v[8 * j + 2 * t] = __uint_as_float(ww[t] << 16);
+      v[8 * j + 2 * t + 1] = __uint_as_float(ww[t] & 0xffff0000u);
+    }
+  }
+  float amax = 0.f;
+#pragma unroll
+  for (int j = 0; j < 32; ++j) amax = fmaxf(amax, fabsf(v[j]));
+  const uint32_t sbyte = mxfp8_scale_byte(amax);
+  const float inv = __uint_as_float((254u - sbyte) << 23);
+  const float sc = __uint_as_float(sbyte << 23);
+  uint32_t out[16];
+#pragma unroll
+  for (int j = 0; j < 16; ++j) {
+    const uint32_t lo = f32_to_bf16(e4m3_to_f32(e4m3_byte(v[2 * j] * inv)) * sc);
+    const uint32_t hi = f32_to_bf16(e4m3_to_f32(e4m3_byte(v[2 * j + 1] * inv)) * sc);
+    out[j] = lo | (hi << 16);
+  }
+  u32x4* dst = reinterpret_cast<u32x4*>(y + 32 * b);
+#pragma unroll
+  for (int j = 0; j < 4; ++j) dst[j] = u32x4{out[4 * j], out[4 * j + 1], out[4 * j + 2], out[4 * j + 3]};
+}
+
 // K-steps of loads in flight (register budget of two waves per SIMD).
 constexpr int kDepthDirect = 2;  // gg_direct_b_kernel, MX-FP4 weights
 
@@ -1611,7 +1685,9 @@ template <bool GATEUP>
 hipError_t launch_gg(const Dims& dm, const GGArgs& a, hipStream_t s) {
   const size_t max_tiles = grouped_gemm_max_mtiles(dm) * (size_t)a.ntiles;
   const dim3 grid((unsigned)((max_tiles + kXcds - 1) / kXcds * kXcds)), block(kThreads);
-  if (dm.wfmt == kNVFP4)
+  if (GATEUP && dm.fp8 && dm.wfmt == kNVFP4)
+    gg_mx_group_kernel<kNVFP4, true, true><<<grid, block, 0, s>>>(a);  // h on the MXFP8 grid
+  else if (dm.wfmt == kNVFP4)
     gg_mx_row_kernel<kNVFP4, GATEUP><<<grid, block, 0, s>>>(a);
   else if (dm.wfmt == kMXFP4 && mx_grouped(a.K))
     gg_mx_group_kernel<kMXFP4, GATEUP><<<grid, block, 0, s>>>(a);
@@ -1657,7 +1733,17 @@ hipError_t launch_gg_down(const Dims& dm, const void* h, const Plan& p, const We
 }
 
 bool fp8_path_ok(const Dims& dm) {
-  return dm.act == kBF16 && dm.wfmt == kMXFP4 && mx_grouped(dm.d) && mx_grouped(dm.f);
+  return dm.act == kBF16 && is_fp4(dm.wfmt) && mx_grouped(dm.d) && mx_grouped(dm.f);
+}
+
+hipError_t launch_round_mxfp8(const void* x, long long rows, int K, void* y, hipStream_t s) {
+  LaunchTimer tm("round_mxfp8", s);
+  const long long nb = rows * (K / 32);
+  if (nb == 0) return hipSuccess;
+  const dim3 grid((unsigned)((nb + 255) / 256)), block(256);
+  round_mxfp8_kernel<<<grid, block, 0, s>>>(reinterpret_cast<const uint16_t*>(x), nb,
+                                            reinterpret_cast<uint16_t*>(y));
+  return hipGetLastError();
 }
 
 hipError_t launch_quantize_mxfp8(const void* x, long long rows, int K, uint8_t* q, uint8_t* qs,

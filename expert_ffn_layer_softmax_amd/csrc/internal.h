@@ -119,10 +119,14 @@ bool grouped_gemm_ok(const Dims& dm);
 size_t grouped_gemm_max_mtiles(const Dims& dm);
 hipError_t launch_gg_gate_up(const Dims& dm, const void* x, const Plan& p, const Weights& w,
                              void* h, hipStream_t s);
-// FP8 activations (MXFP8) x MX-FP4 weights on the scaled MFMA.
+// FP8 activations (MXFP8): with MX-FP4 weights on the scaled MFMA, with NVFP4
+// weights as bf16 values on bf16 MFMA.
 bool fp8_path_ok(const Dims& dm);
 hipError_t launch_quantize_mxfp8(const void* x, long long rows, int K, uint8_t* q, uint8_t* qs,
                                  hipStream_t s);
+// bf16 x rounded to the MXFP8 grid, kept as bf16 (FP8 activations with NVFP4
+// weights: the gate/up GEMM then rounds h the same way, from fp32).
+hipError_t launch_round_mxfp8(const void* x, long long rows, int K, void* y, hipStream_t s);
 hipError_t launch_gg_f8_gate_up(const Dims& dm, const uint8_t* xq, const uint8_t* xs, const Plan& p,
                                 const Weights& w, uint8_t* hq, uint8_t* hs, hipStream_t s);
 hipError_t launch_gg_f8_down(const Dims& dm, const uint8_t* hq, const uint8_t* hs, const Plan& p,

@@ -86,16 +86,21 @@ typedef enum {
 /* Compute options (moe_dims_t.flags).
  *  MOE_FLAG_FP8_ACTIVATIONS: run the expert products with FP8 activations,
  *    the pages' production precision ("FP8 compute" with 4-bit expert
- *    weights: SGLang-TorchTPU on TPU v7 page, "Results").  x and h are
- *    quantised to MXFP8 (OCP FP8 E4M3 values, one E8M0 scale per 32
- *    elements along the reduction dimension: scale 2^(floor(log2 amax) - 8),
- *    elements rounded to nearest even and saturated at +-448) and multiplied
- *    with MX-FP4 weights on the gfx950 scaled MFMA.  Requires act BF16,
- *    weights MXFP4, d and f multiples of 256 (else MOE_ERR_UNSUPPORTED); x, out
- *    and every other buffer keep their layouts.  Applies at every T (the
- *    grouped MFMA path is then used for decode too).  Results are defined
- *    with the quantised activations; they differ from the bf16 path by the
- *    FP8 rounding (about 2-4 % relative). */
+ *    weights: SGLang-TorchTPU on TPU v7 page, "Results", which pairs FP8
+ *    compute with NVFP4 expert weights).  x and h are quantised to MXFP8
+ *    (OCP FP8 E4M3 values, one E8M0 scale per 32 elements along the
+ *    reduction dimension: scale 2^(floor(log2 amax) - 8), elements rounded to
+ *    nearest even and saturated at +-448; h from its fp32 value).  With
+ *    MX-FP4 weights the products run on the gfx950 scaled MFMA (E8M0 block
+ *    scales on both operands).  With NVFP4 weights, whose E4M3 block scales
+ *    that instruction does not take, the quantised activations are carried
+ *    as their exact bf16 values and multiplied on bf16 MFMA with fp32 sums,
+ *    which computes the same products (exact for block scales >= 2^-124).
+ *    Requires act BF16, weights MXFP4 or NVFP4, d and f multiples of 256
+ *    (else MOE_ERR_UNSUPPORTED); x, out and every other buffer keep their
+ *    layouts.  Applies at every T (the grouped MFMA path is then used for
+ *    decode too).  Results are defined with the quantised activations; they
+ *    differ from the bf16 path by the FP8 rounding (about 2-4 % relative). */
 /*  MOE_FLAG_EXPERT_NORM: divide each selected expert's output row by its
  *    root mean square over d, sqrt(mean(y^2) + 1e-6), before the weighted
  *    sum.  The report that describes the combine (TensorSharp Muse Spark

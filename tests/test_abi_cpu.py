@@ -75,13 +75,18 @@ def test_workspace_size_validation(m):
     assert _ws(m, _dims(m, d=256, f=512, w=2, flags=3))[0] == OK
     assert _ws(m, _dims(m, flags=2))[1] == _ws(m, _dims(m))[1]
     assert _ws(m, _dims(m, d=256, f=512, w=1, flags=1))[0] == UNSUPPORTED   # bf16 weights
-    assert _ws(m, _dims(m, d=256, f=512, w=3, flags=1))[0] == UNSUPPORTED   # NVFP4 weights
+    assert _ws(m, _dims(m, d=256, f=512, w=3, flags=1))[0] == OK            # NVFP4 weights
+    assert _ws(m, _dims(m, d=256, f=320, w=3, flags=1))[0] == UNSUPPORTED   # f % 256
     assert _ws(m, _dims(m, d=320, f=512, w=2, flags=1))[0] == UNSUPPORTED   # d % 256
     # the FP8 workspace holds the MXFP8 activations instead of the bf16 h
     T, k, d, f = 64, 8, 256, 512
     w8 = _ws(m, _dims(m, T=T, d=d, E=16, k=k, f=f, w=2, flags=1))[1]
     w16 = _ws(m, _dims(m, T=T, d=d, E=16, k=k, f=f, w=2))[1]
     assert w8 - w16 >= T * d + T * d // 32 + T * k * f // 32 - T * k * f - 4 * 256
+    # with NVFP4 weights the FP8 workspace adds the rounded x (bf16) to the bf16 h
+    n8 = _ws(m, _dims(m, T=T, d=d, E=16, k=k, f=f, w=3, flags=1))[1]
+    n16 = _ws(m, _dims(m, T=T, d=d, E=16, k=k, f=f, w=3))[1]
+    assert n8 - n16 >= T * d * 2
     assert m.lib.moe_workspace_size(None, None) == INVALID
 
 

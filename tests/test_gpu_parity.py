@@ -267,27 +267,33 @@ def test_single_token_fused_path_equals_stagewise(wfmt, k, f, d):
 # accumulation and, rarely, an FP8 rounding decision that the accumulation
 # difference moves across a boundary, so the bf16 tolerance applies.
 FP8_CASES = [
-    # name, T, d, E, k, f
-    ("fp8_t1", 1, 256, 16, 4, 256),
-    ("fp8_t16", 16, 512, 32, 8, 256),
-    ("fp8_t100", 100, 256, 8, 4, 512),
-    ("fp8_hot", 700, 512, 5, 2, 512),       # several m-tiles per expert
-    ("fp8_tails", 150, 768, 6, 2, 256),     # 3 down n-tiles, ragged m-tiles
+    # name, T, d, E, k, f, weights (MX-FP4: scaled MFMA; NVFP4: bf16 MFMA on
+    # MXFP8-valued activations, the pages' own FP8 + NVFP4 pairing)
+    ("fp8_t1", 1, 256, 16, 4, 256, "mxfp4"),
+    ("fp8_t16", 16, 512, 32, 8, 256, "mxfp4"),
+    ("fp8_t100", 100, 256, 8, 4, 512, "mxfp4"),
+    ("fp8_hot", 700, 512, 5, 2, 512, "mxfp4"),       # several m-tiles per expert
+    ("fp8_tails", 150, 768, 6, 2, 256, "mxfp4"),     # 3 down n-tiles, ragged m-tiles
+    ("fp8nv_t1", 1, 256, 16, 4, 256, "nvfp4"),
+    ("fp8nv_t16", 16, 512, 32, 8, 256, "nvfp4"),
+    ("fp8nv_t100", 100, 256, 8, 4, 512, "nvfp4"),
+    ("fp8nv_hot", 700, 512, 5, 2, 512, "nvfp4"),
+    ("fp8nv_tails", 150, 768, 6, 2, 768, "nvfp4"),   # partial n-tiles on both GEMMs
 ]
 
 
 @pytest.mark.parametrize("case", FP8_CASES, ids=[c[0] for c in FP8_CASES])
 def test_layer_fp8_activations(case):
-    name, T, d, E, k, f = case
+    name, T, d, E, k, f, wfmt = case
     log(f"fp8 layer {name}")
-    wl = Workload(name, T=T, d=d, E=E, k=k, f=f, act="bf16", wfmt="mxfp4",
+    wl = Workload(name, T=T, d=d, E=E, k=k, f=f, act="bf16", wfmt=wfmt,
                   seed=zlib.crc32(name.encode()) % 100000,
                   x_std=1.0, wg_std=d ** -0.5, wu_std=d ** -0.5, wd_std=f ** -0.5)
     x, w, w_r, logits = make_inputs(wl)
     got, ref, _ = run_layer_and_oracle(wl, x, w, w_r, logits, fp8=True)
     check_out(name, got, ref["out"], 5e-3, token_tol=FP8_TOKEN_TOL)
     # the FP8 rounding is real: the bf16-activation result differs by about 2-4 %
-    plain = oracle.layer(to_host_act(x), logits.cpu().numpy(), k, expert_getter(w, "mxfp4"), E=E)
+    plain = oracle.layer(to_host_act(x), logits.cpu().numpy(), k, expert_getter(w, wfmt), E=E)
     sep = rel_l2(plain["out"], ref["out"])
     log(f"  bf16-activation reference differs by {sep:.3e}")
     assert sep > 5e-3
@@ -307,6 +313,7 @@ NORM_CASES = [
     ("norm_gg_bf16", 300, 512, 16, 4, 384, "bf16", "bf16", False),
     ("norm_gg_mx_k20", 90, 640, 32, 20, 256, "bf16", "mxfp4", False),   # 5 slots per wave
     ("norm_fp8", 100, 256, 8, 4, 512, "bf16", "mxfp4", True),
+    ("norm_fp8_nv", 100, 256, 8, 4, 512, "bf16", "nvfp4", True),
 ]
 
 
@@ -439,7 +446,7 @@ def test_mx_nan_scale_propagates(T):
 
 # ------------------------------------------------------------ HIP graphs
 @pytest.mark.parametrize("T,wfmt", [(1, "bf16"), (16, "bf16"), (100, "bf16"), (100, "mxfp4"),
-                                    (100, "nvfp4"), (100, "mxfp4_fp8")])
+                                    (100, "nvfp4"), (100, "mxfp4_fp8"), (100, "nvfp4_fp8")])
 def test_hip_graph_replay(T, wfmt):
     """A captured layer replays to the eager result, bit for bit, after eager
     calls with other routing have rewritten the same workspace and outputs."""
@@ -556,7 +563,8 @@ def _oracle_on_tokens(x, lg, k, w, wfmt, E, S, act_quant=None, expert_norm=False
         get.close()
 
 
-@pytest.mark.parametrize("name", ["prefill_bf16", "prefill_mxfp4", "prefill_nvfp4", "prefill_mxfp4_fp8"])
+@pytest.mark.parametrize("name", ["prefill_bf16", "prefill_mxfp4", "prefill_nvfp4", "prefill_mxfp4_fp8",
+                                  "prefill_nvfp4_fp8"])
 def test_prefill_full_stratified(name, full_bf16_weights):
     """T=4096 with skewed load, in the bench's launch configuration: routing
     checked in full; outputs on every token that owns the first or last row
