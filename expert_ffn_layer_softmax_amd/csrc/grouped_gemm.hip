@@ -397,6 +397,7 @@ __device__ __forceinline__ void dma16(const char* g, char* lds) {
 }
 constexpr int kAuxA = 0;  // activation rows: reused by every n-tile of the m-tile
 constexpr int kAuxB = 0;  // weight panel
+constexpr int kAuxNT = 2; // non-temporal: a weight panel no other block reads
 
 // Wait until at most N of this wave's vector-memory operations are
 // outstanding and its LDS reads have returned, then join the block.
@@ -520,15 +521,22 @@ __global__ __launch_bounds__(kThreads) void gg_dma_kernel(GGArgs a) {
   }
   char* const adst = lds + (kDmaA * 8) * wave * (BK * 2);
   char* const bdst = lds + kStageA + (kDmaB * 8) * wave * (BK * 2);
-  auto issue = [&](int kk, int stage) {
+  // Weight panels of an expert with one m-tile are read by this block alone:
+  // they are fetched non-temporally (measured on this chip: the LDS DMA
+  // streams at 6.8 TB/s non-temporal against 6.0 TB/s with the default
+  // policy).  Panels shared by several m-tiles keep the default policy, so
+  // the m-tiles find them in L2 (non-temporal there re-fetches them).
+  auto issue = [&](int kk, int stage, auto nt_c) {
+    constexpr int AUXB = decltype(nt_c)::value ? kAuxNT : kAuxB;
     const size_t go = (size_t)kk * (BK * 2);
     const int so = stage * kStageBytes;
 #pragma unroll
     for (int j = 0; j < kDmaA; ++j) dma16<kAuxA>(asrc[j] + go, adst + so + j * 8 * (BK * 2));
 #pragma unroll
-    for (int j = 0; j < kDmaB; ++j) dma16<kAuxB>(bsrc[j] + go, bdst + so + j * 8 * (BK * 2));
+    for (int j = 0; j < kDmaB; ++j) dma16<AUXB>(bsrc[j] + go, bdst + so + j * 8 * (BK * 2));
   };
-  auto issue_tail = [&](int stage) {
+  auto issue_tail = [&](int stage, auto nt_c) {
+    constexpr int AUXB = decltype(nt_c)::value ? kAuxNT : kAuxB;
     const size_t go = (size_t)nk * (BK * 2);
     const int so = stage * kStageBytes;
 #pragma unroll
@@ -536,7 +544,7 @@ __global__ __launch_bounds__(kThreads) void gg_dma_kernel(GGArgs a) {
       dma16<kAuxA>(asrc[j] + go - ((ahi >> j) & 1) * BK, adst + so + j * 8 * (BK * 2));
 #pragma unroll
     for (int j = 0; j < kDmaB; ++j)
-      dma16<kAuxB>(bsrc[j] + go - ((bhi >> j) & 1) * BK, bdst + so + j * 8 * (BK * 2));
+      dma16<AUXB>(bsrc[j] + go - ((bhi >> j) & 1) * BK, bdst + so + j * 8 * (BK * 2));
   };
 
   // ---- fragment offsets inside a stage: [sub-tile or matrix][substep]
@@ -561,36 +569,42 @@ __global__ __launch_bounds__(kThreads) void gg_dma_kernel(GGArgs a) {
   // valid 32-row sub-tiles of this wave's 64 rows (block-uniform per wave)
   const int vm = min(max((nrows + 31) / 32 - 2 * wm, 0), 2);
 
-  if (nk > 0) issue(0, 0);
-  if (nk > 1) issue(1, 1);
-  // The loop is instantiated per sub-tile count so the accumulators keep
-  // fixed registers.
-  auto main_loop = [&](auto vm_c) {
+  // The loop is instantiated per sub-tile count (so the accumulators keep
+  // fixed registers) and per weight cache policy.
+  auto main_loop = [&](auto vm_c, auto nt_c) {
     constexpr int VM = decltype(vm_c)::value;
+    if (nk > 0) issue(0, 0, nt_c);
+    if (nk > 1) issue(1, 1, nt_c);
     int stage = 0;
     for (int kk = 0; kk < nk; ++kk) {
       if (kk + 1 < nk)
         wait_and_barrier<kDmaPerStage>();
       else
         wait_and_barrier<0>();
-      if (kk + 2 < nk) issue(kk + 2, stage == 0 ? 2 : stage - 1);
+      if (kk + 2 < nk) issue(kk + 2, stage == 0 ? 2 : stage - 1, nt_c);
       dma_step<VM>(lds + stage * kStageBytes, aoff, boff, acc);
       stage = stage == kStages - 1 ? 0 : stage + 1;
     }
     if (ktail) {
       // stage `stage` was last read at step nk - 3, before every wave passed
       // the barrier of step nk - 2
-      issue_tail(stage);
+      issue_tail(stage, nt_c);
       wait_and_barrier<0>();
       dma_step<VM, true>(lds + stage * kStageBytes, aoff, boff, acc, half);
     }
   };
-  if (vm == 2)
-    main_loop(std::integral_constant<int, 2>{});
-  else if (vm == 1)
-    main_loop(std::integral_constant<int, 1>{});
+  auto by_vm = [&](auto nt_c) {
+    if (vm == 2)
+      main_loop(std::integral_constant<int, 2>{}, nt_c);
+    else if (vm == 1)
+      main_loop(std::integral_constant<int, 1>{}, nt_c);
+    else
+      main_loop(std::integral_constant<int, 0>{}, nt_c);
+  };
+  if (nmt == 1)
+    by_vm(std::true_type{});
   else
-    main_loop(std::integral_constant<int, 0>{});
+    by_vm(std::false_type{});
 
   // ---- epilogue (C layout of a 32x32 MFMA: lane holds column lane%32 and
   // rows 8*(i/4) + 4*(lane/32) + i%4 for i in 0..15)
