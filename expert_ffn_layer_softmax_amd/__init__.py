@@ -19,6 +19,7 @@ from ._lib import (  # noqa: F401
     lib,
     load,
     moe_combine,
+    moe_debug_check,
     moe_expert_ffn,
     moe_layer_forward,
     moe_layer_forward_noalloc,

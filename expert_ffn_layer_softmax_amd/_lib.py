@@ -51,6 +51,7 @@ _SIGS = {
     "moe_last_device_error": [],
     "moe_quantize_mxfp8": [_vp, ctypes.c_int64, _i32, _vp, _vp, _vp],
     "moe_layer_forward_noalloc": [_P(MoeDims), _vp, _vp, _vp, _P(MoeExpertWeights), _vp, _vp, _vp, _vp],
+    "moe_debug_check": [_P(ctypes.c_uint32)],
 }
 
 
@@ -364,6 +365,14 @@ def moe_layer_forward_noalloc(x, weights: dict, k, logits=None, w_router=None, t
                                          ctypes.byref(w), _ptr(topk_idx), _ptr(topk_w), _ptr(out),
                                          _stream(x)), "moe_layer_forward_noalloc")
     return dict(out=out, logits=logits, topk_idx=topk_idx, topk_w=topk_w)
+
+
+def moe_debug_check() -> int:
+    """Bounds-check violations recorded by a debug build since the last call
+    (bit mask, see include/moe.h); raises MoeError on a release build."""
+    v = ctypes.c_uint32(0)
+    _check(lib.moe_debug_check(ctypes.byref(v)), "moe_debug_check")
+    return v.value
 
 
 def moe_timing_start():

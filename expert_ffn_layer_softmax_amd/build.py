@@ -3,6 +3,10 @@
 Every source is compiled for gfx950 only.  Packed-fp32 VALU instructions are
 disabled on the device side (``-target-feature -packed-fp32-ops``).
 
+``--debug-checks`` builds ``libmoe_mi355x_dbg.so``: the same library with
+-DMOE_DEBUG_CHECKS, whose kernels bounds-check every index they read from
+memory (see moe_debug_check in include/moe.h).
+
 ``--sanitize`` builds ``libmoe_mi355x_san.so`` instead, whose host code (the
 C ABI's validation, workspace plan and launch logic) carries AddressSanitizer
 and UndefinedBehaviorSanitizer; device code is compiled as usual.  Load it
@@ -24,6 +28,7 @@ CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libmoe_mi355x.so")
 SAN_LIB = os.path.join(PKG, "libmoe_mi355x_san.so")
+DBG_LIB = os.path.join(PKG, "libmoe_mi355x_dbg.so")
 
 SOURCES = ["abi.cpp", "route.hip", "permute.hip", "gemv.hip", "combine.hip", "grouped_gemm.hip",
            "scratch.hip"]
@@ -88,11 +93,12 @@ def _compile(src: str, hipcc: str, extra, build_dir: str) -> str:
     return obj
 
 
-def build(verbose: bool = False, extra=(), sanitize: bool = False) -> str:
+def build(verbose: bool = False, extra=(), sanitize: bool = False, debug_checks: bool = False) -> str:
     """Compile every source and link the shared library; returns its path."""
-    build_dir = BUILD + ("_san" if sanitize else "")
-    lib = SAN_LIB if sanitize else LIB
-    extra = list(extra) + (SANITIZE if sanitize else [])
+    assert not (sanitize and debug_checks), "one variant at a time"
+    build_dir = BUILD + ("_san" if sanitize else "_dbg" if debug_checks else "")
+    lib = SAN_LIB if sanitize else DBG_LIB if debug_checks else LIB
+    extra = list(extra) + (SANITIZE if sanitize else []) + (["-DMOE_DEBUG_CHECKS"] if debug_checks else [])
     os.makedirs(build_dir, exist_ok=True)
     hipcc = _hipcc()
     srcs = [s for s in SOURCES if os.path.exists(os.path.join(CSRC, s))]
@@ -117,4 +123,4 @@ def build(verbose: bool = False, extra=(), sanitize: bool = False) -> str:
 
 
 if __name__ == "__main__":
-    build(verbose=True, sanitize="--sanitize" in sys.argv[1:])
+    build(verbose=True, sanitize="--sanitize" in sys.argv[1:], debug_checks="--debug-checks" in sys.argv[1:])

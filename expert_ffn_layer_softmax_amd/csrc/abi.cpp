@@ -319,7 +319,7 @@ moe_status_t moe_expert_ffn(const moe_dims_t* dims, const void* x, const int32_t
   Plan p = plan_at(workspace, L);
   p.offsets = const_cast<int*>(offsets);
   p.sorted_src = const_cast<int*>(sorted_src);
-  hipError_t e = launch_plan_from_offsets(offsets, dm.E, p, s);
+  hipError_t e = launch_plan_from_offsets(offsets, dm.E, (int)dm.Tk(), p, s);
   if (e == hipSuccess)
     e = run_expert_ffn(dm, x, p, w, static_cast<char*>(workspace), L, y_sorted, s);
   return device_status(e);
@@ -380,6 +380,23 @@ moe_status_t moe_quantize_mxfp8(const void* x, int64_t rows, int32_t K, uint8_t*
   if (!x || !q || !scales) return MOE_ERR_INVALID_ARGUMENT;
   if (!aligned16(x) || !aligned16(q)) return MOE_ERR_INVALID_ARGUMENT;
   return device_status(launch_quantize_mxfp8(x, rows, K, q, scales, (hipStream_t)stream));
+}
+
+moe_status_t moe_debug_check(uint32_t* violations) {
+  if (!violations) return MOE_ERR_INVALID_ARGUMENT;
+  *violations = 0;
+#ifdef MOE_DEBUG_CHECKS
+  unsigned f = 0;
+  hipError_t e = dbg_take_route(&f);
+  if (e == hipSuccess) e = dbg_take_permute(&f);
+  if (e == hipSuccess) e = dbg_take_gemv(&f);
+  if (e == hipSuccess) e = dbg_take_combine(&f);
+  if (e == hipSuccess) e = dbg_take_grouped_gemm(&f);
+  *violations = f;
+  return device_status(e);
+#else
+  return MOE_ERR_UNSUPPORTED;
+#endif
 }
 
 const char* moe_status_string(moe_status_t status) {

@@ -23,7 +23,7 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
   __shared__ float wts[kMaxK];
   const int t = blockIdx.y;
   if (threadIdx.x < k) {
-    rows[threadIdx.x] = dest_row[(size_t)t * k + threadIdx.x];
+    rows[threadIdx.x] = dbg_idx(dest_row[(size_t)t * k + threadIdx.x], (int)gridDim.y * k, kDbgDestRow);
     wts[threadIdx.x] = topk_w[(size_t)t * k + threadIdx.x];
   }
   __syncthreads();
@@ -78,7 +78,8 @@ __global__ __launch_bounds__(NT) void combine_norm_kernel(const float* __restric
   const int t = blockIdx.x;
   const int lane = lane_id();
   const int wave = threadIdx.x >> 6;
-  if (threadIdx.x < k) rows[threadIdx.x] = dest_row[(size_t)t * k + threadIdx.x];
+  if (threadIdx.x < k)
+    rows[threadIdx.x] = dbg_idx(dest_row[(size_t)t * k + threadIdx.x], (int)gridDim.x * k, kDbgDestRow);
   __syncthreads();
   const int n4 = d >> 2;
   const int P = kWaves > k ? kWaves / k : 1;  // waves per row
@@ -159,7 +160,7 @@ __global__ __launch_bounds__(NT) void combine_norm_reg_kernel(const float* __res
   float4 v[KMAX][C];
 #pragma unroll
   for (int j = 0; j < KMAX; ++j) {
-    const int row = j < k ? dest_row[(size_t)t * k + j] : 0;
+    const int row = j < k ? dbg_idx(dest_row[(size_t)t * k + j], (int)gridDim.x * k, kDbgDestRow) : 0;
     const float4* y = reinterpret_cast<const float4*>(y_sorted + (size_t)row * d);
 #pragma unroll
     for (int c = 0; c < C; ++c) {
@@ -258,5 +259,7 @@ hipError_t launch_combine(const Dims& dm, const float* y_sorted, const int* dest
     combine_kernel<kBF16><<<grid, block, 0, s>>>(y_sorted, dest_row, topk_w, out, dm.d, dm.k);
   return hipGetLastError();
 }
+
+MOE_DBG_TAKE_DEFINE(dbg_take_combine)
 
 }  // namespace moe

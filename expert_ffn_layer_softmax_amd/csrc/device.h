@@ -111,6 +111,51 @@ __device__ __forceinline__ int block_exclusive_scan(int v, int* tmp, int* total)
 }
 
 // ---------------------------------------------------------------------------
+// Debug builds (MOE_DEBUG_CHECKS): bounds checks on index arrays
+// ---------------------------------------------------------------------------
+// An index read from memory (dest_row, sorted_src, an expert id, a row range
+// of the plan) is checked before it addresses anything: out of [0, n) it sets
+// bit `code` of this file's flag word and is clamped into range, so the
+// access stays in bounds and the kernel runs to its end (wrong results, no
+// fault).  moe_debug_check() reads and clears the flag words of every file.
+// Release builds compile the checks away.
+enum : unsigned {
+  kDbgDestRow = 1u,     // dest_row outside [0, T*k)
+  kDbgSortedSrc = 2u,   // sorted_src outside [0, T*k)
+  kDbgExpert = 4u,      // expert id outside [0, E)
+  kDbgRows = 8u,        // a segment's rows outside [0, T*k]
+  kDbgOffsets = 16u,    // offsets not ascending from 0 to T*k
+  kDbgTopk = 32u        // topk_idx outside [0, E)
+};
+#ifdef MOE_DEBUG_CHECKS
+static __device__ unsigned g_dbg_flags;
+__device__ __forceinline__ int dbg_idx(int v, int n, unsigned code) {
+  if ((unsigned)v >= (unsigned)n) {
+    atomicOr(&g_dbg_flags, code);
+    v = v < 0 ? 0 : n - 1;
+  }
+  return v;
+}
+__device__ __forceinline__ void dbg_flag(bool bad, unsigned code) {
+  if (bad) atomicOr(&g_dbg_flags, code);
+}
+// Host side, one per file: OR this file's flag word into *flags, then clear it.
+#define MOE_DBG_TAKE_DEFINE(NAME)                                                 \
+  hipError_t NAME(unsigned* flags) {                                              \
+    unsigned v = 0, z = 0;                                                        \
+    hipError_t e = hipMemcpyFromSymbol(&v, HIP_SYMBOL(g_dbg_flags), sizeof v);     \
+    if (e == hipSuccess) e = hipMemcpyToSymbol(HIP_SYMBOL(g_dbg_flags), &z, sizeof z); \
+    *flags |= v;                                                                  \
+    return e;                                                                     \
+  }
+#else
+__device__ __forceinline__ int dbg_idx(int v, int, unsigned) { return v; }
+__device__ __forceinline__ void dbg_flag(bool, unsigned) {}
+#define MOE_DBG_TAKE_DEFINE(NAME) \
+  hipError_t NAME(unsigned*) { return hipSuccess; }
+#endif
+
+// ---------------------------------------------------------------------------
 // Loads
 // ---------------------------------------------------------------------------
 // Streaming (non-temporal) 16-byte load: weights are read once per call, so

@@ -276,6 +276,7 @@ struct GateUpArgs {
   const int* num_active;
   void* h;
   int d, f, k;
+  int T;  // tokens: sorted_src values lie in [0, T*k)
 };
 
 // h[r][n] = silu(<w_gate[e][n], x[t]>) * <w_up[e][n], x[t]> for every row r
@@ -323,7 +324,8 @@ __global__ __launch_bounds__(256) void gemv_gate_up_kernel(GateUpArgs a) {
   const size_t xrb = (size_t)a.d * act_bytes<WF>();
   const int nseg = MULTISEG ? (nchunks + SEG - 1) / SEG : 1;
   for (int tt = 0; tt < ntok; ++tt) {
-    const char* xr = reinterpret_cast<const char*>(a.x) + (size_t)(a.sorted_src[r0 + tt] / a.k) * xrb;
+    const char* xr = reinterpret_cast<const char*>(a.x) +
+                     (size_t)(dbg_idx(a.sorted_src[r0 + tt], a.T * a.k, kDbgSortedSrc) / a.k) * xrb;
     float ag[RPW], au[RPW];
 #pragma unroll
     for (int r = 0; r < RPW; ++r) ag[r] = au[r] = 0.f;
@@ -691,6 +693,7 @@ struct DownCombineArgs {
   const int* dest_row;
   void* out;
   int d, f, k;
+  int E;
 };
 
 // Single token: down projection fused with the weighted combine.  Block =
@@ -705,7 +708,7 @@ __global__ __launch_bounds__(NTH) void gemv_down_combine_t1_kernel(DownCombineAr
   const int j = threadIdx.x >> 6;
   const int n0 = blockIdx.x * RPW;
   const int nrows = min(RPW, a.d - n0);
-  const int e = a.topk_idx[j];
+  const int e = dbg_idx(a.topk_idx[j], a.E, kDbgExpert);
   const int nchunks = a.f / CE;
   const size_t rb = WT<WF>::row_bytes(a.f);
   const size_t sb = scale_row_bytes<WF>(a.f);
@@ -714,7 +717,7 @@ __global__ __launch_bounds__(NTH) void gemv_down_combine_t1_kernel(DownCombineAr
   W.load_all(reinterpret_cast<const char*>(a.wd) + woff * rb, rb,
              is_fp4(WF) ? a.sd + woff * sb : nullptr, sb, nrows, 0, nchunks, lane);
   const char* hr =
-      reinterpret_cast<const char*>(a.h) + (size_t)a.dest_row[j] * a.f * act_bytes<WF>();
+      reinterpret_cast<const char*>(a.h) + (size_t)dbg_idx(a.dest_row[j], a.k, kDbgDestRow) * a.f * act_bytes<WF>();
   XChunk<WF> hc[MAXC];
 #pragma unroll
   for (int i = 0; i < MAXC; ++i) {
@@ -767,13 +770,13 @@ __global__ __launch_bounds__(NTH) void gemv_down_combine_t1_ring_kernel(DownComb
   const int j = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int n0 = blockIdx.x * RPW;
   const int nrows = min(RPW, a.d - n0);
-  const int e = a.topk_idx[j];
+  const int e = dbg_idx(a.topk_idx[j], a.E, kDbgExpert);
   const int nchunks = a.f / WT<WF>::CE;
   const int rb = (int)WT<WF>::row_bytes(a.f);
   const int sb = (int)scale_row_bytes<WF>(a.f);
   // slot j's activations (its row of h), loaded first so that waiting for
   // them does not wait for the weights
-  const char* hr = reinterpret_cast<const char*>(a.h) + (size_t)a.dest_row[j] * a.f * act_bytes<WF>();
+  const char* hr = reinterpret_cast<const char*>(a.h) + (size_t)dbg_idx(a.dest_row[j], a.k, kDbgDestRow) * a.f * act_bytes<WF>();
   XChunk<WF> hc[MAXC];
 #pragma unroll
   for (int i = 0; i < MAXC; ++i) hc[i] = load_x<WF>(hr, min(i * kWave + lane, nchunks - 1));
@@ -894,7 +897,7 @@ hipError_t launch_gemv_gate_up(const Dims& dm, const void* x, const Plan& p, con
                                void* h, hipStream_t s) {
   LaunchTimer tm("gemv_gate_up", s);
   GateUpArgs a{x, w.wg, w.wu, w.sg, w.su, w.tg, w.tu, p.sorted_src, p.slot_info, p.num_active,
-               h, dm.d, dm.f, dm.k};
+               h, dm.d, dm.f, dm.k, dm.T};
   const long long max_active = dm.Tk() < dm.E ? dm.Tk() : dm.E;
   const int nchunks = dm.d / chunk_elems(dm.wfmt);
   const int maxc = pick_maxc(nchunks, dm.wfmt);
@@ -957,7 +960,7 @@ hipError_t launch_gemv_gate_up_t1_routed(const Dims& dm, const float* logits, co
                                          float* topk_w, hipStream_t s) {
   LaunchTimer tm("gemv_gate_up", s);
   GateUpArgs a{x, w.wg, w.wu, w.sg, w.su, w.tg, w.tu, p.sorted_src, p.slot_info, p.num_active,
-               h, dm.d, dm.f, dm.k};
+               h, dm.d, dm.f, dm.k, dm.T};
   const T1RouteArgs r{logits, dm.E, topk_idx, topk_w, p};
   const int nchunks = dm.d / chunk_elems(dm.wfmt);
   const int maxc = pick_maxc(nchunks, dm.wfmt);
@@ -1019,7 +1022,7 @@ hipError_t launch_gemv_down_combine_t1(const Dims& dm, const void* h, const Plan
                                        const int* topk_idx, const float* topk_w,
                                        const Weights& w, void* out, hipStream_t s) {
   LaunchTimer tm("gemv_down_combine_t1", s);
-  DownCombineArgs a{h, w.wd, w.sd, w.td, topk_idx, topk_w, p.dest_row, out, dm.d, dm.f, dm.k};
+  DownCombineArgs a{h, w.wd, w.sd, w.td, topk_idx, topk_w, p.dest_row, out, dm.d, dm.f, dm.k, dm.E};
   const int maxc = pick_maxc(dm.f / chunk_elems(dm.wfmt), dm.wfmt);
   const dim3 block(64 * dm.k);
   if (is_fp4(dm.wfmt) && dm.k <= 8 && maxc <= 2 && dm.f % 128 == 0) {
@@ -1048,5 +1051,7 @@ hipError_t launch_gemv_down_combine_t1(const Dims& dm, const void* h, const Plan
   }
   return hipGetLastError();
 }
+
+MOE_DBG_TAKE_DEFINE(dbg_take_gemv)
 
 }  // namespace moe

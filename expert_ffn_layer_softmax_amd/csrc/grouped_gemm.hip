@@ -121,6 +121,7 @@ struct GGArgs {
   const int* num_mtiles;
   void* out;              // gate/up: h bf16 [T*k][N]; down: y_sorted fp32 [T*k][N]
   int K, N, k, ntiles;
+  int T;                  // tokens: sorted_src values lie in [0, T*k)
 };
 
 // LDS tiles hold rows of 128 B (64 bf16 of K).  16-byte unit u of row r
@@ -243,7 +244,7 @@ __global__ __launch_bounds__(kThreads) void gg_direct_b_kernel(GGArgs a) {
     const int r = (tid >> 3) + i * (kThreads / 8);
     const int src = row0 + min(r, nrows - 1);
     ap[i] = reinterpret_cast<const char*>(a.a_src) +
-            (GATEUP ? (size_t)(a.sorted_src[src] / a.k) : (size_t)src) * a_rb + unit * 16;
+            (GATEUP ? (size_t)(dbg_idx(a.sorted_src[src], a.T * a.k, kDbgSortedSrc) / a.k) : (size_t)src) * a_rb + unit * 16;
   }
 
   // K % 64 == 32: step nk is a tail of 32 K.  Its A units 4..7 and the
@@ -498,7 +499,7 @@ __global__ __launch_bounds__(kThreads) void gg_dma_kernel(GGArgs a) {
     const int f = (r & 7) ^ ((r >> 3) & 1);
     const int src = row0 + min(r, nrows - 1);
     asrc[j] = reinterpret_cast<const char*>(a.a_src) +
-              (GATEUP ? (size_t)(a.sorted_src[src] / a.k) : (size_t)src) * rb + ((slot16 ^ f) << 4);
+              (GATEUP ? (size_t)(dbg_idx(a.sorted_src[src], a.T * a.k, kDbgSortedSrc) / a.k) : (size_t)src) * rb + ((slot16 ^ f) << 4);
     ahi |= ((slot16 ^ f) >= 4 ? 1 : 0) << j;
   }
   const char* bsrc[kDmaB];
@@ -836,7 +837,7 @@ __global__ __launch_bounds__(kThreads) void gg_mx_group_kernel(GGArgs a) {
     const int f = (r & 7) ^ ((r >> 3) & 1);
     const int src = row0 + min(r, nrows - 1);
     asrc[j] = reinterpret_cast<const char*>(a.a_src) +
-              (GATEUP ? (size_t)(a.sorted_src[src] / a.k) : (size_t)src) * rb + ((slot16 ^ f) << 4);
+              (GATEUP ? (size_t)(dbg_idx(a.sorted_src[src], a.T * a.k, kDbgSortedSrc) / a.k) : (size_t)src) * rb + ((slot16 ^ f) << 4);
   }
   char* const adst = lds_a + (kDmaA * 8) * wave * (BK * 2);
 
@@ -1141,7 +1142,7 @@ __global__ __launch_bounds__(kThreads) void gg_mx_row_kernel(GGArgs a) {
     const int f = (r & 7) ^ ((r >> 3) & 1);
     const int src = row0 + min(r, nrows - 1);
     asrc[j] = reinterpret_cast<const char*>(a.a_src) +
-              (GATEUP ? (size_t)(a.sorted_src[src] / a.k) : (size_t)src) * rb + ((slot16 ^ f) << 4);
+              (GATEUP ? (size_t)(dbg_idx(a.sorted_src[src], a.T * a.k, kDbgSortedSrc) / a.k) : (size_t)src) * rb + ((slot16 ^ f) << 4);
   }
   char* const adst = lds_a + (kDmaA * 8) * wave * (BK * 2);
 
@@ -1439,7 +1440,7 @@ __global__ __launch_bounds__(kThreads) void gg_f8f4_kernel(GGArgs a) {
   // activation row r of the tile (0..127) -> source row index
   auto arow_src = [&](int r) -> size_t {
     const int src = row0 + min(r, nrows - 1);
-    return GATEUP ? (size_t)(a.sorted_src[src] / a.k) : (size_t)src;
+    return GATEUP ? (size_t)(dbg_idx(a.sorted_src[src], a.T * a.k, kDbgSortedSrc) / a.k) : (size_t)src;
   };
 
   // ---- activation DMA: wave w fills rows 16w .. 16w+15; lane -> row
@@ -1732,7 +1733,7 @@ hipError_t launch_gg_gate_up(const Dims& dm, const void* x, const Plan& p, const
   LaunchTimer tm("gg_gate_up", s);
   const int tc = tile_cols(dm, true);
   GGArgs a{x, p.sorted_src, w.wg, w.wu, w.sg, w.su, w.tg, w.tu, nullptr, nullptr, p.mtiles, p.num_mtiles, h,
-           dm.d, dm.f, dm.k, (dm.f + tc - 1) / tc};
+           dm.d, dm.f, dm.k, (dm.f + tc - 1) / tc, dm.T};
   return launch_gg<true>(dm, a, s);
 }
 
@@ -1742,7 +1743,7 @@ hipError_t launch_gg_down(const Dims& dm, const void* h, const Plan& p, const We
   const int tc = tile_cols(dm, false);
   GGArgs a{h, nullptr, w.wd, nullptr, w.sd, nullptr, w.td, nullptr, nullptr, nullptr, p.mtiles, p.num_mtiles,
            y_sorted,
-           dm.f, dm.d, dm.k, (dm.d + tc - 1) / tc};
+           dm.f, dm.d, dm.k, (dm.d + tc - 1) / tc, dm.T};
   return launch_gg<false>(dm, a, s);
 }
 
@@ -1774,7 +1775,7 @@ hipError_t launch_gg_f8_gate_up(const Dims& dm, const uint8_t* xq, const uint8_t
                                 const Weights& w, uint8_t* hq, uint8_t* hs, hipStream_t s) {
   LaunchTimer tm("gg_gate_up", s);
   GGArgs a{xq, p.sorted_src, w.wg, w.wu, w.sg, w.su, nullptr, nullptr, xs, hs, p.mtiles, p.num_mtiles,
-           hq, dm.d, dm.f, dm.k, dm.f / (BN / 2)};
+           hq, dm.d, dm.f, dm.k, dm.f / (BN / 2), dm.T};
   const size_t max_tiles = grouped_gemm_max_mtiles(dm) * (size_t)a.ntiles;
   const dim3 grid((unsigned)((max_tiles + kXcds - 1) / kXcds * kXcds)), block(kThreads);
   gg_f8f4_kernel<true><<<grid, block, 0, s>>>(a);
@@ -1785,11 +1786,13 @@ hipError_t launch_gg_f8_down(const Dims& dm, const uint8_t* hq, const uint8_t* h
                              const Weights& w, float* y_sorted, hipStream_t s) {
   LaunchTimer tm("gg_down", s);
   GGArgs a{hq, nullptr, w.wd, nullptr, w.sd, nullptr, nullptr, nullptr, hs, nullptr, p.mtiles,
-           p.num_mtiles, y_sorted, dm.f, dm.d, dm.k, dm.d / BN};
+           p.num_mtiles, y_sorted, dm.f, dm.d, dm.k, dm.d / BN, dm.T};
   const size_t max_tiles = grouped_gemm_max_mtiles(dm) * (size_t)a.ntiles;
   const dim3 grid((unsigned)((max_tiles + kXcds - 1) / kXcds * kXcds)), block(kThreads);
   gg_f8f4_kernel<false><<<grid, block, 0, s>>>(a);
   return hipGetLastError();
 }
+
+MOE_DBG_TAKE_DEFINE(dbg_take_grouped_gemm)
 
 }  // namespace moe

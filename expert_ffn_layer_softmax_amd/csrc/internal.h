@@ -73,6 +73,14 @@ struct Plan {
 constexpr size_t kScratchBytes = size_t(64) << 20;
 hipError_t scratch_for_current_device(void** ptr);
 
+// Debug builds: each kernel file's bounds-check flag word, OR-ed into *flags
+// and cleared (synchronous).  No-ops in release builds.
+hipError_t dbg_take_route(unsigned* flags);
+hipError_t dbg_take_permute(unsigned* flags);
+hipError_t dbg_take_gemv(unsigned* flags);
+hipError_t dbg_take_combine(unsigned* flags);
+hipError_t dbg_take_grouped_gemm(unsigned* flags);
+
 // Per-kernel event timing (abi.cpp).  Bracket every launch with it.
 struct LaunchTimer {
   LaunchTimer(const char* name, hipStream_t s);
@@ -96,7 +104,7 @@ hipError_t launch_route_plan_t1(const float* logits, int E, int k, int* topk_idx
                                 const Plan& p, hipStream_t s);
 hipError_t launch_permute(const int* topk_idx, int T, int E, int k, const Plan& p,
                           bool with_lists, hipStream_t s);
-hipError_t launch_plan_from_offsets(const int* offsets, int E, const Plan& p, hipStream_t s);
+hipError_t launch_plan_from_offsets(const int* offsets, int E, int Tk, const Plan& p, hipStream_t s);
 hipError_t launch_gemv_gate_up(const Dims& dm, const void* x, const Plan& p, const Weights& w,
                                void* h, hipStream_t s);
 hipError_t launch_gemv_down(const Dims& dm, const void* h, const Plan& p, const Weights& w,

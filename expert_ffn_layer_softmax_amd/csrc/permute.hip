@@ -129,6 +129,7 @@ __device__ void permute_block(KeyFn key, int N, int E, const Plan& p, bool with_
       if (g + u * kWave >= q1) break;  // wave-uniform: the chunk's last batch is done
       const uint32_t q = g + u * kWave + lane;
       const bool valid = q < q1;
+      dbg_flag(valid && (unsigned)ks[u] >= (unsigned)E, kDbgTopk);
       const int e = valid ? min(max(ks[u], 0), E - 1) : 0;
       uint64_t peers = __ballot(valid);
       for (int b = 0; b < nbits; ++b) {
@@ -158,12 +159,22 @@ __global__ __launch_bounds__(kPermThreads) void permute_kernel(const int* __rest
 }
 
 __global__ __launch_bounds__(kPermThreads) void plan_kernel(const int* __restrict__ offsets, int E,
-                                                            Plan p) {
+                                                            int Tk, Plan p) {
   __shared__ int tmp[32];
   const int e = threadIdx.x;
-  const int c = e < E ? offsets[e + 1] - offsets[e] : 0;
-  const int first = e < E ? offsets[e] : 0;
-  write_lists(c, first, E, p, tmp);
+  int first = e < E ? offsets[e] : 0;
+  int next = e < E ? offsets[e + 1] : 0;
+#ifdef MOE_DEBUG_CHECKS
+  // caller's offsets: ascending from 0 to T*k; otherwise clamped so that the
+  // plan stays inside [0, T*k]
+  if (e < E) {
+    dbg_flag(next < first || first < 0 || next > Tk || (e == 0 && first != 0) || (e == E - 1 && next != Tk),
+             kDbgOffsets);
+    first = min(max(first, 0), Tk);
+    next = min(max(next, first), Tk);
+  }
+#endif
+  write_lists(next - first, first, E, p, tmp);
 }
 
 // Decode-sized layers (T <= 16, T*k <= 1024): wave t routes token t, then the
@@ -227,9 +238,9 @@ hipError_t launch_permute(const int* topk_idx, int T, int E, int k, const Plan& 
   return hipGetLastError();
 }
 
-hipError_t launch_plan_from_offsets(const int* offsets, int E, const Plan& p, hipStream_t s) {
+hipError_t launch_plan_from_offsets(const int* offsets, int E, int Tk, const Plan& p, hipStream_t s) {
   LaunchTimer tm("plan", s);
-  plan_kernel<<<1, kPermThreads, 0, s>>>(offsets, E, p);
+  plan_kernel<<<1, kPermThreads, 0, s>>>(offsets, E, Tk, p);
   return hipGetLastError();
 }
 
@@ -249,5 +260,7 @@ hipError_t launch_route_permute_small(const float* logits, int T, int E, int k, 
     route_permute_small_kernel<16><<<g, b, 0, s>>>(logits, T, E, k, topk_idx, topk_w, p);
   return hipGetLastError();
 }
+
+MOE_DBG_TAKE_DEFINE(dbg_take_permute)
 
 }  // namespace moe

@@ -91,4 +91,6 @@ hipError_t launch_route_topk(const float* logits, int T, int E, int k, int* topk
   return hipGetLastError();
 }
 
+MOE_DBG_TAKE_DEFINE(dbg_take_route)
+
 }  // namespace moe

@@ -251,6 +251,21 @@ moe_status_t moe_layer_forward_noalloc(const moe_dims_t* dims, const void* x, co
 moe_status_t moe_quantize_mxfp8(const void* x, int64_t rows, int32_t K, uint8_t* q,
                                 uint8_t* scales, moe_stream_t stream);
 
+/* Bounds checks of a debug build (compiled with -DMOE_DEBUG_CHECKS:
+ * `python -m expert_ffn_layer_softmax_amd.build --debug-checks` makes
+ * libmoe_mi355x_dbg.so).  In such a build every kernel checks each index it
+ * reads from memory before using it as an address -- dest_row and sorted_src
+ * values against [0, T*k), expert ids against [0, E), topk_idx against
+ * [0, E) in moe_permute, and moe_expert_ffn's offsets for ascending from 0
+ * to T*k -- and an index out of range is clamped into range (the access
+ * stays in bounds; the results are then wrong) and recorded.  This call
+ * returns the OR of the recorded bits since the previous call, and clears
+ * them: 1 dest_row, 2 sorted_src, 4 expert id, 8 segment rows, 16 offsets,
+ * 32 topk_idx.  Call it after the work to check has finished (it reads the
+ * flags synchronously, on the null stream).  Release builds check nothing
+ * and return MOE_ERR_UNSUPPORTED with *violations = 0. */
+moe_status_t moe_debug_check(uint32_t* violations);
+
 /* Static, NUL-terminated description of a status code. */
 const char* moe_status_string(moe_status_t status);
 

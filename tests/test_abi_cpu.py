@@ -209,3 +209,12 @@ def test_layer_forward_noalloc_validation(m):
     assert L.moe_layer_forward_noalloc(*args(big, _w(m))) == WS_SMALL
     prefill = _dims(m, T=4096, d=6144, E=256, k=8, f=2816)
     assert L.moe_layer_forward_noalloc(*args(prefill, _w(m))) == WS_SMALL
+
+
+def test_debug_check_entry_point(m):
+    """moe_debug_check validates its pointer; a release build has no checks."""
+    L = m.lib
+    assert L.moe_debug_check(None) == INVALID
+    v = ctypes.c_uint32(7)
+    assert L.moe_debug_check(ctypes.byref(v)) == UNSUPPORTED
+    assert v.value == 0

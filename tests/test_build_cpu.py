@@ -58,6 +58,8 @@ def test_build_from_a_fresh_checkout(fresh_tree):
     os.remove(lib)
     _run([sys.executable, "-c", "import __graft_entry__ as g; g.build()"], fresh_tree)
     assert os.path.exists(lib)
+    # build() also makes the bounds-checking debug variant
+    assert os.path.exists(os.path.join(fresh_tree, PKG, "libmoe_mi355x_dbg.so"))
     names = _declared(fresh_tree)
     assert "moe_layer_forward" in names
     probe = ("import ctypes, sys; L = ctypes.CDLL(sys.argv[1]); "
