@@ -84,15 +84,10 @@ __device__ __forceinline__ uint32_t mxfp8_scale_byte(float amax) {
   return (uint32_t)min(max(ef - 8, 1), 254);
 }
 
-// v rounded to the MXFP8 grid of its 32-element block, as fp32: the block is
-// the 32 lanes of one half of the wave (one row, 32 consecutive columns of an
-// MFMA result), so every lane of the wave must call.  The value is
-// E4M3(code) * 2^(s - 127), which bf16 holds exactly for block scales
-// s >= 3 (smaller ones only below 2^-124).
-__device__ __forceinline__ float mxfp8_round_lanes32(float v) {
-  float amax = fabsf(v);
-#pragma unroll
-  for (int o = 1; o < 32; o <<= 1) amax = fmaxf(amax, __shfl_xor(amax, o, kWave));
+// v rounded to the MXFP8 grid of a 32-element block whose largest magnitude
+// is amax, as fp32: E4M3(code) * 2^(s - 127), which bf16 holds exactly for
+// block scales s >= 3 (smaller ones only below 2^-124).
+__device__ __forceinline__ float mxfp8_round(float v, float amax) {
   const uint32_t sbyte = mxfp8_scale_byte(amax);
   const float inv = __uint_as_float((254u - sbyte) << 23);  // 2^(127 - s)
   return e4m3_to_f32(e4m3_byte(v * inv)) * __uint_as_float(sbyte << 23);
@@ -770,10 +765,7 @@ __device__ __forceinline__ void mx4_step(const char* st, const char* cb, const c
   }
 }
 
-// QH (gate/up only): h is rounded to the MXFP8 grid before it is stored (as
-// bf16), for FP8 activations with NVFP4 weights; the wave's 32 output columns
-// are one MX block along f.
-template <int WF, bool GATEUP, bool QH = false>
+template <int WF, bool GATEUP>
 __global__ __launch_bounds__(kThreads) void gg_mx_group_kernel(GGArgs a) {
   using GS = GroupScales<WF>;
   __shared__ __align__(1024) char lds[GS::kLds];
@@ -992,25 +984,6 @@ __global__ __launch_bounds__(kThreads) void gg_mx_group_kernel(GGArgs a) {
       acc[1][mi] *= t1;
     }
   }
-  if constexpr (GATEUP && QH) {
-    // every lane rounds (the block maximum is a cross-lane reduction); rows
-    // past the tile and columns past N are then not stored.  N % 32 == 0, so
-    // a block lies wholly inside or outside the matrix.
-    const int col = nbase + 32 * wn + cl;
-#pragma unroll
-    for (int mi = 0; mi < 2; ++mi) {
-      if (mi < vm) {
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int row = 64 * wm + 32 * mi + 8 * (i >> 2) + 4 * half + (i & 3);
-          const float h = mxfp8_round_lanes32(silu_mul(acc[0][mi][i], acc[1][mi][i]));
-          if (row < nrows && col < a.N)
-            reinterpret_cast<uint16_t*>(a.out)[(size_t)(row0 + row) * a.N + col] = f32_to_bf16(h);
-        }
-      }
-    }
-    return;
-  }
 #pragma unroll
   for (int mi = 0; mi < 2; ++mi) {
     if (mi < vm) {
@@ -1083,7 +1056,11 @@ __device__ __forceinline__ void mx4_row_step(const char* st, const char* cb, con
 // pair: prefill 5.88 -> 5.34 ms.  For MX-FP4 (one convert per pair) the extra
 // activation reads cost more than the halved conversions save (gate/up 2.65
 // -> 2.84 ms), so it keeps the 2 x 4 grid.
-template <int WF, bool GATEUP>
+// QH (gate/up only): h is rounded to the MXFP8 grid before it is stored (as
+// bf16), for FP8 activations with NVFP4 weights.  A wave holds 16 output
+// columns, so each 32-column MX block spans waves 2j and 2j + 1: their
+// per-row partial maxima meet in LDS after the main loop.
+template <int WF, bool GATEUP, bool QH = false>
 __global__ __launch_bounds__(kThreads) void gg_mx_row_kernel(GGArgs a) {
   using GS = GroupScales<WF>;
   __shared__ __align__(1024) char lds[GS::kLds];
@@ -1294,6 +1271,46 @@ __global__ __launch_bounds__(kThreads) void gg_mx_row_kernel(GGArgs a) {
     const float t = (GATEUP && cl >= 16) ? a.t1[e] : a.t0[e];
 #pragma unroll
     for (int mi = 0; mi < 4; ++mi) acc[mi] *= t;
+  }
+  if constexpr (GATEUP && QH) {
+    // h in place of the W_gate sums (lanes cl < 16; the others hold W_up's),
+    // then each row's maximum over the wave's 16 columns: one value per row
+    // per wave into LDS, which every wave has finished reading
+    __syncthreads();
+    float* part = reinterpret_cast<float*>(lds);  // [8 waves][128 rows]
+    // sub-tiles past the tile's rows hold nothing to store (vm is the same
+    // in both waves of a pair)
+#pragma unroll
+    for (int mi = 0; mi < 4; ++mi) {
+      if (mi >= vm) continue;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const float v = acc[mi][i];
+        const float u = __shfl_xor(v, 16, kWave);  // every lane takes part
+        const float h = silu_mul(v, u);
+        acc[mi][i] = h;
+        float am = cl < 16 ? fabsf(h) : 0.f;  // fmaxf below skips NaN
+#pragma unroll
+        for (int o = 1; o < 16; o <<= 1) am = fmaxf(am, __shfl_xor(am, o, kWave));
+        const int row = 32 * mi + 8 * (i >> 2) + 4 * half + (i & 3);
+        if (cl == 0) part[wave * BM + row] = am;
+      }
+    }
+    __syncthreads();
+    const int col = nbase + 16 * wave + cl;
+#pragma unroll
+    for (int mi = 0; mi < 4; ++mi) {
+      if (mi >= vm) continue;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int row = 32 * mi + 8 * (i >> 2) + 4 * half + (i & 3);
+        const float amax = fmaxf(part[wave * BM + row], part[(wave ^ 1) * BM + row]);
+        const float hq = mxfp8_round(acc[mi][i], amax);
+        if (cl < 16 && row < nrows && col < a.N)
+          reinterpret_cast<uint16_t*>(a.out)[(size_t)(row0 + row) * a.N + col] = f32_to_bf16(hq);
+      }
+    }
+    return;
   }
 #pragma unroll
   for (int mi = 0; mi < 4; ++mi) {
@@ -1701,7 +1718,7 @@ hipError_t launch_gg(const Dims& dm, const GGArgs& a, hipStream_t s) {
   const size_t max_tiles = grouped_gemm_max_mtiles(dm) * (size_t)a.ntiles;
   const dim3 grid((unsigned)((max_tiles + kXcds - 1) / kXcds * kXcds)), block(kThreads);
   if (GATEUP && dm.fp8 && dm.wfmt == kNVFP4)
-    gg_mx_group_kernel<kNVFP4, true, true><<<grid, block, 0, s>>>(a);  // h on the MXFP8 grid
+    gg_mx_row_kernel<kNVFP4, true, true><<<grid, block, 0, s>>>(a);  // h on the MXFP8 grid
   else if (dm.wfmt == kNVFP4)
     gg_mx_row_kernel<kNVFP4, GATEUP><<<grid, block, 0, s>>>(a);
   else if (dm.wfmt == kMXFP4 && mx_grouped(a.K))
