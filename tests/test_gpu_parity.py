@@ -139,6 +139,11 @@ SMALL = [
     ("gg_mx_gtail", 150, 512, 6, 2, 320, "bf16", "mxfp4"),     # gate/up N=320: partial n-tile
     ("gg_mx_ktail", 120, 352, 8, 2, 352, "bf16", "mxfp4"),     # K % 64 == 32 on both GEMMs
     ("gg_mx_ktail_t48", 48, 96, 4, 2, 160, "bf16", "mxfp4"),   # 1.5 and 2.5 K-steps
+    # MX-FP4 tiles of 129..256 rows (K % 256 == 0)
+    ("gg_mx_big", 640, 512, 8, 2, 512, "bf16", "mxfp4"),       # ~160 rows/expert, both GEMMs
+    ("gg_mx_big_hot", 900, 256, 3, 2, 768, "bf16", "mxfp4"),   # ~600 rows/expert: 256 + 256 + rest
+    ("gg_mx_big_gtail", 520, 512, 4, 2, 320, "bf16", "mxfp4"), # gate/up N=320: partial n-tile
+    ("gg_mx_big_dtail", 520, 640, 4, 2, 512, "bf16", "mxfp4"), # down N=640: partial n-tile
     # NVFP4: 16-element E4M3 blocks and fp32 matrix scales
     ("nv_t1", 1, 256, 16, 4, 96, "bf16", "nvfp4"),
     ("nv_t5", 5, 512, 32, 8, 160, "bf16", "nvfp4"),
@@ -416,6 +421,33 @@ def test_routing_and_shape_extremes(case):
     check_routing(res, lg, k, E)
     if mode == "hot":
         assert set(np.unique(res["topk_idx"].cpu().numpy()).tolist()) == set(hot.cpu().tolist())
+    ref = oracle.layer(to_host_act(x), lg, k, expert_getter(w, wfmt), E=E)
+    check_out(name, to_host_act(res["out"]), ref["out"], 5e-3 if wfmt == "bf16" else MXFP4_TOL)
+
+
+@pytest.mark.parametrize("wfmt", ["mxfp4", "bf16"])
+def test_tile_height_edges(wfmt):
+    """Experts with exactly 1, 128, 129, 256, 257 and 383 rows (k = 1, each
+    token sent to a chosen expert in shuffled order): the boundaries between
+    one and two 128-row m-tiles and between the MX-FP4 tiles of up to 128
+    and of 129..256 rows."""
+    from expert_ffn_layer_softmax_amd import moe_layer_forward
+    counts = [128, 129, 256, 257, 1, 383]
+    E, k, d, f = len(counts), 1, 512, 512
+    T = sum(counts)
+    name = f"tile_edges_{wfmt}"
+    log(f"tile edges {wfmt}: counts {counts}")
+    wl = Workload(name, T=T, d=d, E=E, k=k, f=f, act="bf16", wfmt=wfmt, seed=zlib.crc32(name.encode()) % 100000,
+                  x_std=1.0, wg_std=d ** -0.5, wu_std=d ** -0.5, wd_std=f ** -0.5)
+    x, w, _, logits = make_inputs(wl)
+    target = np.repeat(np.arange(E), counts)
+    np.random.default_rng(5).shuffle(target)
+    logits[torch.arange(T, device=logits.device), torch.from_numpy(target).to(logits.device)] += 100.0
+    res = moe_layer_forward(x, w, k, logits=logits)
+    torch.cuda.synchronize()
+    lg = logits.cpu().numpy()
+    check_routing(res, lg, k, E)
+    assert np.bincount(res["topk_idx"].cpu().numpy().ravel(), minlength=E).tolist() == counts
     ref = oracle.layer(to_host_act(x), lg, k, expert_getter(w, wfmt), E=E)
     check_out(name, to_host_act(res["out"]), ref["out"], 5e-3 if wfmt == "bf16" else MXFP4_TOL)
 
