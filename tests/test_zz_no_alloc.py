@@ -88,3 +88,43 @@ def test_noalloc_with_router_and_rejection():
     ref2 = moe_layer_forward(x[:5].contiguous(), w, wl.k, w_router=w_r)
     torch.cuda.synchronize()
     _same(got2["out"], ref2["out"], "out after a rejected call")
+
+
+@pytest.mark.parametrize("T,wfmt", [(1, "mxfp4"), (16, "bf16"), (100, "bf16"), (100, "mxfp4")])
+def test_noalloc_under_graph_capture(T, wfmt):
+    """The callers this entry point is for include code under HIP graph
+    capture.  Captured once, the call replays to the eager result bit for
+    bit, each replay after an eager call with other routing has rewritten
+    the shared scratch and the outputs."""
+    from expert_ffn_layer_softmax_amd import moe_layer_forward_noalloc
+    log(f"noalloc graph T={T} {wfmt}")
+    k = 8
+    wl = Workload(f"noalloc_graph_{wfmt}", T=T, d=512, E=32, k=k, f=256, act="bf16", wfmt=wfmt, seed=97 + T,
+                  x_std=1.0, wg_std=512 ** -0.5, wu_std=512 ** -0.5, wd_std=256 ** -0.5)
+    x, w, _, logits = make_inputs(wl)
+    other = torch.randn(T, wl.E, generator=torch.Generator().manual_seed(1000 + T)).cuda()
+    eager = moe_layer_forward_noalloc(x, w, k, logits=logits)
+    torch.cuda.synchronize()
+    ref_out, ref_idx, ref_w = eager["out"].clone(), eager["topk_idx"].clone(), eager["topk_w"].clone()
+    out = torch.empty_like(ref_out)
+    idx = torch.empty_like(ref_idx)
+    tw = torch.empty_like(ref_w)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        moe_layer_forward_noalloc(x, w, k, logits=logits, topk_idx=idx, topk_w=tw, out=out)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        moe_layer_forward_noalloc(x, w, k, logits=logits, topk_idx=idx, topk_w=tw, out=out)
+    torch.cuda.synchronize()
+    for rep in range(3):
+        moe_layer_forward_noalloc(x, w, k, logits=other, topk_idx=idx, topk_w=tw, out=out)
+        torch.cuda.synchronize()
+        assert not torch.equal(idx, ref_idx), "the eager call should route differently"
+        g.replay()
+        torch.cuda.synchronize()
+        _same(idx, ref_idx, f"replay {rep}: topk_idx")
+        _same(tw, ref_w, f"replay {rep}: topk_w")
+        _same(out, ref_out, f"replay {rep}: out")
