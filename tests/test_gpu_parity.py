@@ -452,6 +452,48 @@ def test_tile_height_edges(wfmt):
     check_out(name, to_host_act(res["out"]), ref["out"], 5e-3 if wfmt == "bf16" else MXFP4_TOL)
 
 
+def _random_fp4_weights(wfmt, E, d, f, seed):
+    """Expert weights whose bytes cover the format's domain: codes uniform
+    over all 16 nibbles; NVFP4 block scales uniform over every E4M3 byte but
+    the two NaNs (so zero, subnormal, negative and the largest scales occur),
+    matrix scales in [0.25, 4); MX-FP4 scales uniform over E8M0 bytes
+    110..144 (2^-17 .. 2^17: a wide range with no fp32 overflow in the
+    layer)."""
+    g = torch.Generator().manual_seed(seed)
+    shapes = dict(gate=(E, f, d), up=(E, f, d), down=(E, d, f))
+    w = {}
+    for n, (a, b, K) in shapes.items():
+        w["w_" + n] = torch.randint(0, 256, (a, b, K // 2), generator=g, dtype=torch.uint8)
+        if wfmt == "nvfp4":
+            r = torch.randint(0, 254, (a, b, K // 16), generator=g, dtype=torch.int32)
+            w["s_" + n] = (r + (r >= 0x7F).to(torch.int32)).to(torch.uint8).view(torch.float8_e4m3fn)
+            w["t_" + n] = 0.25 + 3.75 * torch.rand(a, generator=g)
+        else:
+            w["s_" + n] = torch.randint(110, 145, (a, b, K // 32), generator=g, dtype=torch.uint8)
+    return {key: v.cuda() for key, v in w.items()}
+
+
+@pytest.mark.parametrize("wfmt,T", [("nvfp4", 1), ("nvfp4", 16), ("nvfp4", 200),
+                                    ("mxfp4", 1), ("mxfp4", 16), ("mxfp4", 200)])
+def test_fp4_scale_byte_domain(wfmt, T):
+    """4-bit weights over the whole code and scale domain (not only what the
+    quantiser of the synthetic weights produces), on the single-token kernels,
+    the GEMV path and the grouped MFMA path (T = 200, K % 256 == 0)."""
+    name = f"scale_domain_{wfmt}_T{T}"
+    log(name)
+    d, f, E, k = 512, 512, 8, 2
+    wl = Workload(name, T=T, d=d, E=E, k=k, f=f, act="bf16", wfmt=wfmt, seed=zlib.crc32(name.encode()) % 100000,
+                  x_std=1.0)
+    w = _random_fp4_weights(wfmt, E, d, f, wl.seed)
+    if wfmt == "nvfp4":
+        s8 = torch.cat([w["s_" + n].view(torch.uint8).flatten() for n in ("gate", "up", "down")]).cpu()
+        present = set(torch.unique(s8).tolist())
+        assert 0x7F not in present and 0xFF not in present and len(present) == 254
+    x, w, _, logits = make_inputs(wl, weights=w)
+    got, ref, _ = run_layer_and_oracle(wl, x, w, None, logits)
+    check_out(name, got, ref["out"], MXFP4_TOL)
+
+
 @pytest.mark.parametrize("T", [1, 64])
 def test_mx_nan_scale_propagates(T):
     """An E8M0 scale byte of 255 is NaN (OCP MX): the output columns that use
