@@ -400,6 +400,8 @@ EXTREMES = [
     ("k_is_E_64", 100, 128, 64, 64, 64, "bf16", "rand"),                # largest k: dense mixture
     ("min_gemm_shape", 64, 64, 4, 2, 64, "bf16", "rand"),               # d = f = 64 on the MFMA path
     ("many_tokens_small", 20000, 64, 16, 2, 64, "bf16", "rand"),
+    ("many_experts_gg_bf16", 256, 256, 1024, 8, 256, "bf16", "rand"),   # ~2 rows per expert: 1024 tiny m-tiles
+    ("many_experts_gg_mx", 256, 256, 1024, 8, 256, "mxfp4", "rand"),
 ]
 
 
