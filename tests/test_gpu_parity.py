@@ -496,6 +496,37 @@ def test_fp4_scale_byte_domain(wfmt, T):
     check_out(name, got, ref["out"], MXFP4_TOL)
 
 
+@pytest.mark.parametrize("wfmt,T,fp8", [("bf16", 16, False), ("bf16", 200, False), ("mxfp4", 16, False),
+                                        ("mxfp4", 200, False), ("nvfp4", 200, False), ("mxfp4", 200, True)])
+def test_nan_token_is_isolated(wfmt, T, fp8):
+    """Tokens are independent: a NaN in one token's activations makes that
+    token's whole output NaN and leaves every other token as the oracle
+    computes it, on the GEMV and the grouped MFMA paths (where other rows of
+    the NaN token's tiles, and padding rows copied from it, share its
+    blocks)."""
+    from expert_ffn_layer_softmax_amd import moe_layer_forward
+    name = f"nan_token_{wfmt}_T{T}{'_fp8' if fp8 else ''}"
+    log(name)
+    d, f, E, k = 512, 512, 8, 4
+    wl = Workload(name, T=T, d=d, E=E, k=k, f=f, act="bf16", wfmt=wfmt, seed=zlib.crc32(name.encode()) % 100000,
+                  x_std=1.0, wg_std=d ** -0.5, wu_std=d ** -0.5, wd_std=f ** -0.5)
+    x, w, _, logits = make_inputs(wl)
+    bad = T // 3
+    x[bad, 17] = float("nan")
+    res = moe_layer_forward(x, w, k, logits=logits, fp8=fp8)
+    torch.cuda.synchronize()
+    out = to_host_act(res["out"])
+    assert np.isnan(out[bad]).all(), "the NaN token's output is not all NaN"
+    keep = np.array([t for t in range(T) if t != bad])
+    assert not np.isnan(out[keep]).any(), "NaN reached another token"
+    lg = logits.cpu().numpy()
+    check_routing(res, lg, k, E)
+    ref = oracle.layer(to_host_act(x)[keep], lg[keep], k, expert_getter(w, wfmt), E=E,
+                       act_quant=oracle.quantize_mxfp8 if fp8 else None)
+    check_out(name, out[keep], ref["out"], MXFP4_TOL if wfmt != "bf16" else 5e-3,
+              token_tol=FP8_TOKEN_TOL if fp8 else None)
+
+
 @pytest.mark.parametrize("T", [1, 64])
 def test_mx_nan_scale_propagates(T):
     """An E8M0 scale byte of 255 is NaN (OCP MX): the output columns that use
