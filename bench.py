@@ -72,6 +72,10 @@ def _parse():
                    help="time one GPU's share of the layer split over 8 GPUs: ep8 = 1/8 of the "
                         "experts with the T*k/8 rows dispatched to them (k=1 locally), tp8 = every "
                         "expert with f/8; tokens/s counts the whole layer's tokens")
+    p.add_argument("--streams", type=int, default=1,
+                   help="independent requests per step: each a layer call (its own logit set, "
+                        "workspace and outputs) on its own HIP stream at the default priority, "
+                        "so their kernels may overlap; tokens/s counts every request's tokens")
     p.add_argument("--graph", action="store_true",
                    help="replay each step from a captured HIP graph (one graph per logit-set "
                         "offset, rotated) instead of launching it")
@@ -236,10 +240,11 @@ def measure(wl, ws_list, args, with_cpu: bool):
     dref, wref = ctypes.byref(dims), [ctypes.byref(t) for t in wts]
     wsn = ws.numel()
 
-    def launch(i, stream):
+    def launch(i, stream, bufs=None):
+        ap, fx = (aptr, fixed) if bufs is None else bufs
         for layer in range(nl):
-            st = fwd(dref, aptr[layer], None, lptr[(i + layer) % nsets], wref[layer], fixed[0],
-                     fixed[1], aptr[layer + 1], fixed[2], wsn, stream)
+            st = fwd(dref, ap[layer], None, lptr[(i + layer) % nsets], wref[layer], fx[0],
+                     fx[1], ap[layer + 1], fx[2], wsn, stream)
             if st != 0:
                 raise L.MoeError(st, "moe_layer_forward")
 
@@ -248,6 +253,25 @@ def measure(wl, ws_list, args, with_cpu: bool):
     def step(i):
         launch(i, stream0)
 
+    # --streams S: requests 1..S-1 get their own outputs, workspace and stream
+    # (request 0 is the one above, on the current stream)
+    S = max(1, args.streams)
+    others = []
+    for _ in range(S - 1):
+        a_s = [x] + [torch.empty_like(t) for t in acts[1:]]
+        f_s = [torch.empty_like(topk_idx), torch.empty_like(topk_w), torch.empty_like(ws)]
+        strm = torch.cuda.Stream()
+        others.append((strm, ([ctypes.c_void_p(t.data_ptr()) for t in a_s],
+                              [ctypes.c_void_p(t.data_ptr()) for t in f_s]), a_s + f_s))
+    if others:
+        for strm, _, _ in others:
+            strm.wait_stream(torch.cuda.current_stream())
+
+        def step(i):  # noqa: F811
+            launch(S * i, stream0)
+            for j, (strm, bufs, _) in enumerate(others):
+                launch(S * i + j + 1, ctypes.c_void_p(strm.cuda_stream), bufs)
+
     # unique experts per layer call (for algorithmic bytes), from the device's routing
     uniq = []
     for i in range(nsets):
@@ -255,6 +279,8 @@ def measure(wl, ws_list, args, with_cpu: bool):
         uniq.append(int(torch.unique(topk_idx).numel()))
 
     graphs = None
+    if args.graph and others:
+        raise SystemExit("--graph takes one stream")
     if args.graph:
         # one graph per logit-set offset; replays rotate through them
         ng = min(nsets, 8)
@@ -290,7 +316,7 @@ def measure(wl, ws_list, args, with_cpu: bool):
         loops.append(time.perf_counter() - t0)
     el = sorted(loops)[len(loops) // 2]
     ms = el * 1e3 / args.steps
-    tokens_per_s = getattr(args, "job_tokens", wl.T) * args.steps / el
+    tokens_per_s = getattr(args, "job_tokens", wl.T) * S * args.steps / el
 
     # per-kernel HIP-event durations on the launch stream (separate pass of
     # launched steps; graph replays carry no events)
@@ -325,7 +351,8 @@ def measure(wl, ws_list, args, with_cpu: bool):
         achieved = k_bytes / (kernel_us * 1e-6) / 1e9
     layer_bytes = (mean_uniq * eb["total"] + 2 * wl.T * wl.d * act_b + wl.T * wl.E * 4 + wl.T * k * 8)
     layer_flops = 6.0 * wl.T * k * wl.d * wl.f
-    step_bytes, step_flops = nl * layer_bytes, nl * layer_flops
+    # S independent requests per step, each streaming its own experts
+    step_bytes, step_flops = S * nl * layer_bytes, S * nl * layer_flops
     t_floor = max(step_bytes / (HBM_PEAK_GBS * 1e9), step_flops / (mfma_peak * 1e12))
     digest = _source_digest(srcs)
     # counters are kept per path: the FP8 GEMMs are other kernels than the
@@ -343,6 +370,8 @@ def measure(wl, ws_list, args, with_cpu: bool):
         cfg["layers"] = nl
     if graphs:
         cfg["hip_graph"] = True
+    if S > 1:
+        cfg["streams"] = S
     if args.fp8:
         cfg["activations"] = "mxfp8"
     if args.expert_norm:
